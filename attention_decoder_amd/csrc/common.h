@@ -1,0 +1,87 @@
+// Shared device-side types and helpers of the gfx950 LFM3 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define LFM3_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;  // bf16 bit pattern
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+typedef __attribute__((ext_vector_type(16))) float f32x16_v;
+
+namespace lfm3 {
+
+constexpr int kMaxBatch = 64;
+constexpr int kHeadDim = 128;
+constexpr int kHalfDim = 64;
+constexpr int kQPerKv = 4;
+constexpr int kPageTokens = 16;
+constexpr int kMaxTaps = 8;
+
+// Which slot and position each row of a pass belongs to. A prefill pass is one slot at
+// consecutive positions (mode 0); a decode step is one row per slot (mode 1).
+struct Rows {
+  int32_t n;
+  int32_t mode;
+  int32_t slot0;
+  int32_t pos0;
+  int32_t slot[kMaxBatch];
+  int32_t pos[kMaxBatch];
+};
+
+LFM3_DEV int row_slot(const Rows& r, int i) { return r.mode == 0 ? r.slot0 : r.slot[i]; }
+LFM3_DEV int row_pos(const Rows& r, int i) { return r.mode == 0 ? r.pos0 + i : r.pos[i]; }
+
+LFM3_DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bf16, round to nearest even (NaN kept quiet).
+LFM3_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+LFM3_DEV uint32_t pack_bf2(float lo, float hi) { return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16); }
+
+LFM3_DEV float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+LFM3_DEV float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum for blockDim.x a multiple of 64 (<= 1024); `red` holds >= 16 floats of LDS.
+LFM3_DEV float block_sum(float v, float* red) {
+  v = warp_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// Orderable key for a float: larger float -> larger key; NaN ranks as -inf.
+LFM3_DEV uint32_t order_key(float f) {
+  if (f != f) f = -__builtin_huge_valf();
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// A quantized linear [N, K] as stored in the blob (device pointers into it).
+struct QLinear {
+  const uint8_t* q;       // [N, K * bits / 8]
+  const bf16_t* scales;   // [N, K / group]
+  const bf16_t* biases;   // [N, K / group]
+  int32_t n, k, bits, group;
+};
+
+}  // namespace lfm3

@@ -1,0 +1,314 @@
+// Small per-row kernels of the LFM3 forward pass on gfx950: embedding gather, residual + sandwich
+// RMSNorm, per-head q/k norm + RoPE + KV store, the gated short conv with its kept state, and
+// bookkeeping (page table, argmax finalisation, fills, the dequant check).
+#include "kernels.h"
+
+namespace lfm3 {
+
+// Code k of a row stored as a little-endian low-bit-first bitstream of `bits`-bit codes.
+LFM3_DEV uint32_t code_at(const uint8_t* row, int k, int bits) {
+  const int bit = k * bits;
+  const int byte = bit >> 3, sh = bit & 7;
+  uint32_t v = row[byte];
+  if (sh + bits > 8) v |= (uint32_t)row[byte + 1] << 8;
+  return (v >> sh) & ((1u << bits) - 1u);
+}
+
+// The affine dequantisation w = q * scale + bias (MLX affine format); exact in fp32 for bf16
+// scale/bias and codes below 2^8.
+LFM3_DEV float deq_value(uint32_t q, float s, float b) { return fmaf((float)q, s, b); }
+
+// ---------------------------------------------------------------------------------------------
+// embedding ("LFM3-1.7B port" table: vocab 128000, tied; TensorFold #1491: quantized like the
+// linears, 8-bit in the VL 4-bit export)
+// ---------------------------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) k_embed(QLinear e, const int32_t* __restrict__ tokens, float* __restrict__ h) {
+  const int r = blockIdx.x;
+  const int tok = tokens[r];
+  float* out = h + (size_t)r * e.k;
+  if (tok < 0 || tok >= e.n) {
+    for (int k = threadIdx.x; k < e.k; k += blockDim.x) out[k] = 0.f;
+    return;
+  }
+  const size_t row_bytes = (size_t)e.k * e.bits / 8;
+  const uint8_t* row = e.q + (size_t)tok * row_bytes;
+  const int ng = e.k / e.group;
+  for (int k = threadIdx.x; k < e.k; k += blockDim.x) {
+    const int g = k / e.group;
+    const float s = bf2f(e.scales[(size_t)tok * ng + g]);
+    const float b = bf2f(e.biases[(size_t)tok * ng + g]);
+    out[k] = deq_value(code_at(row, k, e.bits), s, b);
+  }
+}
+
+hipError_t launch_embed(hipStream_t s, const QLinear& emb, const int32_t* tokens, int rows, float* h) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, emb, tokens, h);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) k_bf16_to_f32(const bf16_t* __restrict__ in, size_t n, float* __restrict__ out) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) out[i] = bf2f(in[i]);
+}
+
+hipError_t launch_bf16_to_f32(hipStream_t s, const bf16_t* in, int rows, int cols, float* out) {
+  const size_t n = (size_t)rows * cols;
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(k_bf16_to_f32, dim3((unsigned)blocks), dim3(256), 0, s, in, n, out);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) k_dequant_rows(QLinear w, int row0, float* f32, bf16_t* bf) {
+  const int r = blockIdx.x;
+  const int n = row0 + r;
+  const size_t row_bytes = (size_t)w.k * w.bits / 8;
+  const uint8_t* row = w.q + (size_t)n * row_bytes;
+  const int ng = w.k / w.group;
+  for (int k = threadIdx.x; k < w.k; k += blockDim.x) {
+    const int g = k / w.group;
+    const float v = deq_value(code_at(row, k, w.bits), bf2f(w.scales[(size_t)n * ng + g]),
+                              bf2f(w.biases[(size_t)n * ng + g]));
+    if (f32) f32[(size_t)r * w.k + k] = v;
+    if (bf) bf[(size_t)r * w.k + k] = f2bf(v);
+  }
+}
+
+hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int rows, float* f32, bf16_t* bf) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dequant_rows, dim3(rows), dim3(256), 0, s, w, row0, f32, bf);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// residual + sandwich RMSNorm ("LFM3-1.7B port" table row 5: operator_norm -> mixer ->
+// post_operator_norm -> + residual -> ffn_norm -> SwiGLU -> post_ffn_norm -> + residual;
+// RMSNorm eps 1e-5). One block per row, 256 threads, hidden <= 4096.
+// ---------------------------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  const int H = a.hidden;
+  const size_t base = (size_t)r * H;
+  constexpr int kPer = 16;
+  float hv[kPer];
+  const int per = H / blockDim.x;
+  if (a.m) {
+    float mv[kPer];
+    float ss = 0.f;
+    for (int i = 0; i < per; ++i) {
+      const int k = threadIdx.x + i * blockDim.x;
+      mv[i] = a.m[base + k];
+      ss += mv[i] * mv[i];
+    }
+    ss = block_sum(ss, red);
+    const float rm = rsqrtf(ss / (float)H + a.eps);
+    for (int i = 0; i < per; ++i) {
+      const int k = threadIdx.x + i * blockDim.x;
+      hv[i] = a.h_in[base + k] + mv[i] * rm * bf2f(a.w_post[k]);
+    }
+  } else {
+    for (int i = 0; i < per; ++i) hv[i] = a.h_in[base + threadIdx.x + i * blockDim.x];
+  }
+  float ss = 0.f;
+  for (int i = 0; i < per; ++i) ss += hv[i] * hv[i];
+  ss = block_sum(ss, red);
+  const float rh = rsqrtf(ss / (float)H + a.eps);
+  for (int i = 0; i < per; ++i) {
+    const int k = threadIdx.x + i * blockDim.x;
+    if (a.m) a.h_out[base + k] = hv[i];
+    if (a.capture) a.capture[base + k] = hv[i];
+    const bf16_t xb = f2bf(hv[i] * rh * bf2f(a.w_pre[k]));
+    a.x_out[base + k] = xb;
+    if (a.x_copy) a.x_copy[base + k] = xb;
+  }
+}
+
+hipError_t launch_resid_norm(hipStream_t s, const NormArgs& a) {
+  if (a.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_resid_norm, dim3(a.rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// q/k per-head RMSNorm, RoPE and the KV store.
+// "LFM3-1.7B port": per-head q/k RMSNorm unchanged from LFM2.5; "partial_rotary_factor" section:
+// rotate_half pairs (i, i+64), angle p * inv_freq_i, inv_freq 0 on the tail of the full layers.
+// One block per row, 4 waves; lane l holds dims l and l + 64 of a head.
+// ---------------------------------------------------------------------------------------------
+
+LFM3_DEV bf16_t* kv_row(const KvRef& kv, bf16_t* base, int slot, int pos, int kvh, int n_kv) {
+  if (kv.ring == 0) {
+    const int page = kv.page_table[(size_t)slot * kv.max_pages + pos / kPageTokens];
+    return base + (((size_t)page * n_kv + kvh) * kPageTokens + (pos % kPageTokens)) * kHeadDim;
+  }
+  return base + (((size_t)slot * n_kv + kvh) * kv.ring + (pos % kv.ring)) * kHeadDim;
+}
+
+__global__ void __launch_bounds__(256) k_qk_rope(QkRopeArgs a) {
+  const int r = blockIdx.x;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int pos = row_pos(a.rows, r), slot = row_slot(a.rows, r);
+  const float* src = a.qkvg + (size_t)r * a.ld;
+  const float c = a.cos_t[(size_t)pos * kHalfDim + l];
+  const float sn = a.sin_t[(size_t)pos * kHalfDim + l];
+  const int nq = a.n_q_heads, nkv = a.n_kv_heads;
+  // q heads and k heads: norm + rope
+  for (int h = w; h < nq + nkv; h += 4) {
+    const bool is_q = h < nq;
+    const float* hp = src + (size_t)h * kHeadDim;  // k heads follow q heads contiguously
+    const float x0 = hp[l], x1 = hp[l + kHalfDim];
+    const float ss = warp_sum(x0 * x0 + x1 * x1);
+    const float rr = rsqrtf(ss / (float)kHeadDim + a.eps);
+    const bf16_t* nw = is_q ? a.q_norm : a.k_norm;
+    const float n0 = x0 * rr * bf2f(nw[l]);
+    const float n1 = x1 * rr * bf2f(nw[l + kHalfDim]);
+    const float o0 = n0 * c - n1 * sn;
+    const float o1 = n1 * c + n0 * sn;
+    bf16_t* dst;
+    if (is_q) {
+      dst = a.q_out + ((size_t)r * nq + h) * kHeadDim;
+    } else {
+      dst = kv_row(a.kv, a.kv.k, slot, pos, h - nq, nkv);
+    }
+    dst[l] = f2bf(o0);
+    dst[l + kHalfDim] = f2bf(o1);
+  }
+  // v heads: stored bf16 as produced
+  for (int h = w; h < nkv; h += 4) {
+    const float* vp = src + (size_t)(nq + nkv + h) * kHeadDim;
+    bf16_t* dst = kv_row(a.kv, a.kv.v, slot, pos, h, nkv);
+    dst[l] = f2bf(vp[l]);
+    dst[l + kHalfDim] = f2bf(vp[l + kHalfDim]);
+  }
+}
+
+hipError_t launch_qk_rope(hipStream_t s, const QkRopeArgs& a) {
+  if (a.rows.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_qk_rope, dim3(a.rows.n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// gated short conv ("LFM3-1.7B port" table row 1: kernel 7, state = last 6 columns of B*x;
+// "--pad-tail": the new state is columns [n, n + 6) of [state | Bx] after n real rows).
+// Prefill (rows.mode 0): block (channel block, row block); the row-block-0 block alone reads and
+// then rewrites the slot's state, so no other block races with it. Decode (mode 1): one block per
+// row, each row a distinct slot.
+// ---------------------------------------------------------------------------------------------
+
+constexpr int kConvRowBlock = 64;
+
+__global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= a.hidden) return;
+  const int H = a.hidden, T = a.taps, S = T - 1;
+  float ker[kMaxTaps];
+  for (int j = 0; j < T; ++j) ker[j] = bf2f(a.kernel[(size_t)c * T + j]);
+  auto zrow = [&](int r) -> float {
+    const float* p = a.bcx + (size_t)r * a.ld;
+    return bf2f(f2bf(p[c] * p[2 * H + c]));
+  };
+  auto crow = [&](int r) -> float { return a.bcx[(size_t)r * a.ld + H + c]; };
+  float win[kMaxTaps];
+  if (a.rows.mode == 1) {
+    const int r = blockIdx.y;
+    bf16_t* st = a.state + (size_t)a.rows.slot[r] * a.slot_stride;
+    for (int j = 0; j < S; ++j) win[j] = bf2f(st[(size_t)j * H + c]);
+    const float z = zrow(r);
+    float y = ker[S] * z;
+    for (int j = 0; j < S; ++j) y = fmaf(ker[j], win[j], y);
+    a.out[(size_t)r * H + c] = f2bf(crow(r) * y);
+    for (int j = 0; j + 1 < S; ++j) st[(size_t)j * H + c] = f2bf(win[j + 1]);
+    st[(size_t)(S - 1) * H + c] = f2bf(z);
+    return;
+  }
+  const int M = a.rows.n;
+  const int r0 = blockIdx.y * kConvRowBlock;
+  const int r1 = min(M, r0 + kConvRowBlock);
+  bf16_t* st = a.state + (size_t)a.rows.slot0 * a.slot_stride;
+  for (int j = 0; j < S; ++j) {
+    const int t = r0 - S + j;
+    win[j] = t >= 0 ? zrow(t) : bf2f(st[(size_t)(S + t) * H + c]);
+  }
+  for (int r = r0; r < r1; ++r) {
+    const float z = zrow(r);
+    float y = ker[S] * z;
+    for (int j = 0; j < S; ++j) y = fmaf(ker[j], win[j], y);
+    a.out[(size_t)r * H + c] = f2bf(crow(r) * y);
+    for (int j = 0; j + 1 < S; ++j) win[j] = win[j + 1];
+    win[S - 1] = z;
+  }
+  if (blockIdx.y == 0) {
+    // new state: the last S entries of [state | z_0 .. z_{M-1}]; ascending j reads state[M + j]
+    // (M >= 1) before it is overwritten.
+    for (int j = 0; j < S; ++j) {
+      const int t = M - S + j;
+      const float v = t >= 0 ? zrow(t) : bf2f(st[(size_t)(S + t) * H + c]);
+      st[(size_t)j * H + c] = f2bf(v);
+    }
+  }
+}
+
+hipError_t launch_conv(hipStream_t s, const ConvArgs& a) {
+  if (a.rows.n <= 0) return hipSuccess;
+  const int cb = (a.hidden + 255) / 256;
+  const int rb = a.rows.mode == 1 ? a.rows.n : (a.rows.n + kConvRowBlock - 1) / kConvRowBlock;
+  hipLaunchKernelGGL(k_conv, dim3(cb, rb), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// bookkeeping
+// ---------------------------------------------------------------------------------------------
+
+struct PageList { int32_t v[32]; };
+
+__global__ void k_set_pages(int32_t* pt, int index0, int count, PageList pl) {
+  const int i = threadIdx.x;
+  if (i < count) pt[index0 + i] = pl.v[i];
+}
+
+hipError_t launch_set_pages(hipStream_t s, int32_t* page_table, int index0, int count, const int32_t* pages) {
+  for (int off = 0; off < count; off += 32) {
+    PageList pl;
+    const int n = count - off < 32 ? count - off : 32;
+    for (int i = 0; i < n; ++i) pl.v[i] = pages[off + i];
+    hipLaunchKernelGGL(k_set_pages, dim3(1), dim3(32), 0, s, page_table, index0 + off, n, pl);
+  }
+  return hipGetLastError();
+}
+
+__global__ void k_zero(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero(hipStream_t s, void* p, size_t bytes) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+// keys: (order_key(value) << 32) | (0xffffffff - index); the max key is the largest value with
+// the lowest index. Resets the keys for the next step.
+__global__ void k_argmax_finalize(uint64_t* keys, int32_t* ids, int rows) {
+  const int r = threadIdx.x;
+  if (r < rows) {
+    const uint64_t k = keys[r];
+    if (ids) ids[r] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
+    keys[r] = 0;
+  }
+}
+
+hipError_t launch_argmax_finalize(hipStream_t s, uint64_t* keys, int32_t* ids, int rows) {
+  hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(kMaxBatch), 0, s, keys, ids, rows);
+  return hipGetLastError();
+}
+
+}  // namespace lfm3

@@ -1,0 +1,692 @@
+// Host runtime and C ABI of the LFM3 forward pass: config and blob admission, workspace layout,
+// slot bookkeeping (lengths, KV pages), and the layer walk for prefill passes and decode steps.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/lfm3.h"
+#include "kernels.h"
+
+using namespace lfm3;
+
+namespace {
+
+thread_local std::string g_err;
+
+// ------------------------------------------------------------------------------------------------
+// blob format (the writer is the seeded input generator; this reader is independent)
+//   64-byte header: "LFM3BLB1", u32 version 1, u32 n_tensors, u64 table_offset, u64 data_offset,
+//   u64 total_bytes; then n_tensors 128-byte entries: name[80], u32 dtype, u32 ndim, u32 shape[4],
+//   u64 offset, u64 nbytes. dtype 0 = packed codes (bytes), 1 = bf16.
+// ------------------------------------------------------------------------------------------------
+struct Entry {
+  uint32_t dtype, ndim, shape[4];
+  uint64_t offset, nbytes;
+};
+
+constexpr uint32_t DT_CODES = 0, DT_BF16 = 1;
+
+struct Expect {
+  std::string name;
+  uint32_t dtype;
+  std::vector<uint32_t> shape;
+};
+
+int n_of_type(const lfm3_config& c, int t) {
+  int n = 0;
+  for (int i = 0; i < c.n_layers; ++i) n += c.layer_type[i] == t;
+  return n;
+}
+
+int qkvg_rows(const lfm3_config& c) { return c.n_q_heads * c.head_dim + 2 * c.n_kv_heads * c.head_dim + c.n_q_heads; }
+
+void add_linear(std::vector<Expect>& v, const std::string& name, uint32_t n, uint32_t k, int bits, int group) {
+  v.push_back({name + ".q", DT_CODES, {n, (uint32_t)((uint64_t)k * bits / 8)}});
+  v.push_back({name + ".scales", DT_BF16, {n, k / (uint32_t)group}});
+  v.push_back({name + ".biases", DT_BF16, {n, k / (uint32_t)group}});
+}
+
+std::vector<Expect> expected_tensors(const lfm3_config& c) {
+  std::vector<Expect> v;
+  const uint32_t H = c.hidden, F = c.ffn, D = c.head_dim;
+  if (c.has_embedding) add_linear(v, "embedding", c.vocab, H, c.embed_bits, c.embed_group);
+  for (int i = 0; i < c.n_layers; ++i) {
+    const std::string p = "layers." + std::to_string(i) + ".";
+    for (const char* nm : {"operator_norm", "post_operator_norm", "ffn_norm", "post_ffn_norm"})
+      v.push_back({p + nm, DT_BF16, {H}});
+    if (c.layer_type[i] == LFM3_LAYER_CONV) {
+      v.push_back({p + "conv.kernel", DT_BF16, {H, (uint32_t)c.conv_taps}});
+      add_linear(v, p + "conv.in_proj", 3 * H, H, c.bits, c.group);
+      add_linear(v, p + "conv.out_proj", H, H, c.bits, c.group);
+    } else {
+      v.push_back({p + "attn.q_norm", DT_BF16, {D}});
+      v.push_back({p + "attn.k_norm", DT_BF16, {D}});
+      add_linear(v, p + "attn.qkvg_proj", qkvg_rows(c), H, c.bits, c.group);
+      add_linear(v, p + "attn.o_proj", H, c.n_q_heads * D, c.bits, c.group);
+    }
+    add_linear(v, p + "ffn.w13", 2 * F, H, c.bits, c.group);
+    add_linear(v, p + "ffn.w2", H, F, c.bits, c.group);
+  }
+  v.push_back({"embedding_norm", DT_BF16, {H}});
+  return v;
+}
+
+uint64_t elem_bytes(const Expect& e) {
+  uint64_t n = e.dtype == DT_BF16 ? 2 : 1;
+  for (uint32_t s : e.shape) n *= s;
+  return n;
+}
+
+bool parse_header(const uint8_t* p, size_t bytes, std::unordered_map<std::string, Entry>& out, uint64_t& total, std::string& err) {
+  if (bytes < 64) { err = "blob smaller than its 64-byte header"; return false; }
+  if (memcmp(p, "LFM3BLB1", 8) != 0) { err = "blob magic is not LFM3BLB1"; return false; }
+  uint32_t ver, n;
+  uint64_t tab, dat;
+  memcpy(&ver, p + 8, 4); memcpy(&n, p + 12, 4); memcpy(&tab, p + 16, 8); memcpy(&dat, p + 24, 8); memcpy(&total, p + 32, 8);
+  if (ver != 1) { err = "blob version " + std::to_string(ver) + " is not 1"; return false; }
+  if (tab + (uint64_t)n * 128 > bytes || tab + (uint64_t)n * 128 > dat) { err = "blob tensor table runs past the data offset"; return false; }
+  for (uint32_t i = 0; i < n; ++i) {
+    const uint8_t* e = p + tab + (uint64_t)i * 128;
+    char name[81];
+    memcpy(name, e, 80);
+    name[80] = 0;
+    Entry en;
+    memcpy(&en.dtype, e + 80, 4); memcpy(&en.ndim, e + 84, 4); memcpy(en.shape, e + 88, 16);
+    memcpy(&en.offset, e + 104, 8); memcpy(&en.nbytes, e + 112, 8);
+    if (out.count(name)) { err = std::string("blob names tensor ") + name + " twice"; return false; }
+    out[name] = en;
+  }
+  return true;
+}
+
+bool check_config(const lfm3_config& c, std::string& err) {
+  auto bad = [&](const char* f, ...) {
+    char buf[256];
+    va_list ap;
+    va_start(ap, f);
+    vsnprintf(buf, sizeof buf, f, ap);
+    va_end(ap);
+    err = buf;
+    return false;
+  };
+  if (c.n_layers < 1 || c.n_layers > LFM3_MAX_LAYERS) return bad("n_layers %d outside [1, %d]", c.n_layers, LFM3_MAX_LAYERS);
+  if (c.hidden < 512 || c.hidden > 4096 || c.hidden % 512) return bad("hidden %d: this build runs multiples of 512 up to 4096", c.hidden);
+  if (c.ffn < 512 || c.ffn % 512) return bad("ffn %d: this build runs multiples of 512", c.ffn);
+  if (c.head_dim != kHeadDim) return bad("head_dim %d: this build runs 128", c.head_dim);
+  if (c.n_kv_heads < 1 || c.n_q_heads != kQPerKv * c.n_kv_heads) return bad("heads %d/%d: this build runs 4 query heads per KV head", c.n_q_heads, c.n_kv_heads);
+  if (c.n_q_heads * c.head_dim != c.hidden) return bad("n_q_heads * head_dim %d != hidden %d", c.n_q_heads * c.head_dim, c.hidden);
+  if (c.vocab < 1) return bad("vocab %d", c.vocab);
+  if (c.conv_taps < 2 || c.conv_taps > kMaxTaps) return bad("conv_taps %d outside [2, %d]", c.conv_taps, kMaxTaps);
+  if (c.window < 1) return bad("window %d", c.window);
+  if (c.rope_pairs_full < 0 || c.rope_pairs_full > kHalfDim || c.rope_pairs_sliding < 0 || c.rope_pairs_sliding > kHalfDim)
+    return bad("rope pairs %d/%d outside [0, 64]", c.rope_pairs_full, c.rope_pairs_sliding);
+  if (!(c.rope_theta_full > 1.0) || !(c.rope_theta_sliding > 1.0)) return bad("rope theta must be > 1 (full %g, sliding %g)", c.rope_theta_full, c.rope_theta_sliding);
+  if (!(c.norm_eps > 0.f)) return bad("norm_eps must be > 0");
+  auto bits_ok = [](int b) { return b == 4 || b == 6 || b == 8; };
+  if (!bits_ok(c.bits)) return bad("unsupported affine bits %d (4, 6 or 8)", c.bits);
+  if (c.group != 32 && c.group != 64) return bad("unsupported affine group %d (32 or 64)", c.group);
+  if (c.has_embedding != 0 && c.has_embedding != 1) return bad("has_embedding must be 0 or 1");
+  if (c.has_embedding) {
+    if (!bits_ok(c.embed_bits)) return bad("unsupported embedding bits %d", c.embed_bits);
+    if (c.embed_group != 32 && c.embed_group != 64) return bad("unsupported embedding group %d", c.embed_group);
+  }
+  for (int i = 0; i < c.n_layers; ++i)
+    if (c.layer_type[i] > LFM3_LAYER_SLIDING) return bad("layer %d has unknown type %d", i, c.layer_type[i]);
+  if (c.max_slots < 1) return bad("max_slots %d", c.max_slots);
+  if (c.max_ctx < 1) return bad("max_ctx %d", c.max_ctx);
+  if (c.page_tokens != kPageTokens) return bad("page_tokens %d: this build runs 16", c.page_tokens);
+  if (c.max_chunk < 1) return bad("max_chunk %d", c.max_chunk);
+  if (c.n_pages < 0) return bad("n_pages %d", c.n_pages);
+  if (n_of_type(c, LFM3_LAYER_FULL) > 0 && c.n_pages < 1) return bad("full-attention layers need n_pages >= 1");
+  return true;
+}
+
+// ------------------------------------------------------------------------------------------------
+// workspace layout
+// ------------------------------------------------------------------------------------------------
+struct Layout {
+  size_t cos_f, sin_f, cos_s, sin_s;
+  size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
+  size_t h, x, big, sbuf, mix, qrot, m, xf, part, keys;
+  size_t total;
+  int max_rows, max_pages, ring_rows, max_splits, big_ld;
+  size_t ring_layer, pool_layer, conv_slot;
+};
+
+Layout make_layout(const lfm3_config& c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  const size_t H = c.hidden, F = c.ffn;
+  const int n_conv = n_of_type(c, LFM3_LAYER_CONV), n_full = n_of_type(c, LFM3_LAYER_FULL),
+            n_swa = n_of_type(c, LFM3_LAYER_SLIDING);
+  L.max_rows = std::max(c.max_chunk, c.max_slots);
+  L.max_pages = (c.max_ctx + kPageTokens - 1) / kPageTokens;
+  L.ring_rows = c.window + c.max_chunk;
+  L.max_splits = (c.max_ctx + attn_decode_split_keys() - 1) / attn_decode_split_keys() + 1;
+  L.big_ld = std::max<int>(3 * c.hidden, qkvg_rows(c));
+  L.big_ld = (L.big_ld + 7) / 8 * 8;
+  const size_t tab = (size_t)c.max_ctx * kHalfDim * 4;
+  L.cos_f = take(tab); L.sin_f = take(tab); L.cos_s = take(tab); L.sin_s = take(tab);
+  L.conv_slot = (size_t)n_conv * (c.conv_taps - 1) * H;
+  L.conv_state = take((size_t)c.max_slots * L.conv_slot * 2);
+  L.ring_layer = (size_t)c.max_slots * c.n_kv_heads * L.ring_rows * kHeadDim;
+  L.ring_k = take((size_t)n_swa * L.ring_layer * 2);
+  L.ring_v = take((size_t)n_swa * L.ring_layer * 2);
+  L.pool_layer = (size_t)c.n_pages * c.n_kv_heads * kPageTokens * kHeadDim;
+  L.pool_k = take((size_t)n_full * L.pool_layer * 2);
+  L.pool_v = take((size_t)n_full * L.pool_layer * 2);
+  L.page_table = take((size_t)c.max_slots * L.max_pages * 4);
+  const size_t R = L.max_rows;
+  L.h = take(R * H * 4);
+  L.x = take(R * H * 2);
+  L.big = take(R * L.big_ld * 4);
+  L.sbuf = take(R * F * 2);
+  L.mix = take(R * H * 2);
+  L.qrot = take(R * c.n_q_heads * kHeadDim * 2);
+  L.m = take(R * H * 4);
+  L.xf = take(R * H * 2);
+  L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * (kHeadDim + 2) * 4);
+  L.keys = take((size_t)std::max(kMaxBatch, (int)R) * 8);
+  L.total = off;
+  return L;
+}
+
+struct LayerW {
+  int type;
+  int sub;  // index among layers of the same type
+  const bf16_t *op_norm, *post_op, *ffn_norm, *post_ffn, *conv_kernel, *q_norm, *k_norm;
+  QLinear mix_in, mix_out, w13, w2;
+};
+
+}  // namespace
+
+struct lfm3_ctx {
+  lfm3_config cfg;
+  Layout L;
+  hipStream_t stream;
+  const uint8_t* blob;
+  uint8_t* ws;
+  std::vector<LayerW> layers;
+  QLinear emb{};
+  const bf16_t* emb_norm = nullptr;
+  std::vector<int> len;
+  std::vector<std::vector<int32_t>> pages;
+  std::vector<int32_t> free_pages;
+  float* capture = nullptr;
+  int capture_rows = 0;
+  std::string err;
+  std::unordered_map<std::string, QLinear> lin_by_name;
+
+  template <class T> T* at(size_t off) { return (T*)(ws + off); }
+  lfm3_status fail(lfm3_status s, const std::string& m) {
+    err = m;
+    return s;
+  }
+};
+
+namespace {
+
+// Admission of a blob: `head` holds at least the header and table (head_len bytes); blob_bytes is
+// the whole blob's size, against which every tensor's byte range is checked.
+bool validate_blob_impl(const lfm3_config& c, const uint8_t* head, size_t head_len, size_t blob_bytes, std::string& err,
+                        std::unordered_map<std::string, Entry>* out_entries) {
+  std::unordered_map<std::string, Entry> ent;
+  uint64_t total = 0;
+  if (!parse_header(head, head_len, ent, total, err)) return false;
+  if (total != blob_bytes) { err = "blob header total " + std::to_string(total) + " != blob size " + std::to_string(blob_bytes); return false; }
+  const auto exp = expected_tensors(c);
+  if (ent.size() != exp.size()) {
+    err = "blob holds " + std::to_string(ent.size()) + " tensors, config implies " + std::to_string(exp.size());
+    return false;
+  }
+  for (const auto& e : exp) {
+    auto it = ent.find(e.name);
+    if (it == ent.end()) { err = "blob lacks tensor " + e.name; return false; }
+    const Entry& en = it->second;
+    if (en.dtype != e.dtype) { err = "tensor " + e.name + " has dtype " + std::to_string(en.dtype); return false; }
+    if (en.ndim != e.shape.size()) { err = "tensor " + e.name + " has " + std::to_string(en.ndim) + " dims"; return false; }
+    for (size_t d = 0; d < e.shape.size(); ++d)
+      if (en.shape[d] != e.shape[d]) {
+        err = "tensor " + e.name + " dim " + std::to_string(d) + " is " + std::to_string(en.shape[d]) + ", expected " + std::to_string(e.shape[d]);
+        return false;
+      }
+    if (en.nbytes != elem_bytes(e)) { err = "tensor " + e.name + " byte count " + std::to_string(en.nbytes) + " != " + std::to_string(elem_bytes(e)); return false; }
+    if (en.offset % 16 != 0) { err = "tensor " + e.name + " offset not 16-byte aligned"; return false; }
+    if (en.offset + en.nbytes > blob_bytes) { err = "tensor " + e.name + " runs past the blob end"; return false; }
+  }
+  if (out_entries) *out_entries = std::move(ent);
+  return true;
+}
+
+size_t blob_size_for(const lfm3_config& c) {
+  const auto exp = expected_tensors(c);
+  size_t off = 64 + exp.size() * 128;
+  off = (off + 4095) / 4096 * 4096;
+  for (const auto& e : exp) off = (off + elem_bytes(e) + 255) / 256 * 256;
+  return off;
+}
+
+#define LFM3_TRY(expr)                                                                      \
+  do {                                                                                      \
+    hipError_t _e = (expr);                                                                 \
+    if (_e != hipSuccess) return ctx->fail(LFM3_ERR_DEVICE, std::string("HIP: ") + hipGetErrorString(_e) + " in " #expr); \
+  } while (0)
+
+KvRef kv_for(lfm3_ctx* ctx, const LayerW& lw) {
+  KvRef kv{};
+  const Layout& L = ctx->L;
+  if (lw.type == LFM3_LAYER_FULL) {
+    kv.k = ctx->at<bf16_t>(L.pool_k) + (size_t)lw.sub * L.pool_layer;
+    kv.v = ctx->at<bf16_t>(L.pool_v) + (size_t)lw.sub * L.pool_layer;
+    kv.page_table = ctx->at<int32_t>(L.page_table);
+    kv.max_pages = L.max_pages;
+    kv.ring = 0;
+  } else {
+    kv.k = ctx->at<bf16_t>(L.ring_k) + (size_t)lw.sub * L.ring_layer;
+    kv.v = ctx->at<bf16_t>(L.ring_v) + (size_t)lw.sub * L.ring_layer;
+    kv.ring = L.ring_rows;
+  }
+  return kv;
+}
+
+// One pass of the layer stack over `rows` rows whose hidden input is already in h.
+// decode = one row per slot (GEMV path), else a prefill chunk of one slot (GEMM path).
+lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture_row0, bf16_t* hidden_out) {
+  const lfm3_config& c = ctx->cfg;
+  const Layout& L = ctx->L;
+  hipStream_t s = ctx->stream;
+  const int M = rows.n;
+  const int H = c.hidden;
+  float* h = ctx->at<float>(L.h);
+  bf16_t* x = ctx->at<bf16_t>(L.x);
+  float* big = ctx->at<float>(L.big);
+  bf16_t* sb = ctx->at<bf16_t>(L.sbuf);
+  bf16_t* mix = ctx->at<bf16_t>(L.mix);
+  bf16_t* qrot = ctx->at<bf16_t>(L.qrot);
+  float* m = ctx->at<float>(L.m);
+  bf16_t* xf = ctx->at<bf16_t>(L.xf);
+
+  // fp32 output (STORE) or bf16 SwiGLU output
+  auto linear = [&](const QLinear& w, const bf16_t* in, int ldin, float* outf, bf16_t* outb, int ldout, int epi) -> hipError_t {
+    if (decode) {
+      GemvArgs g{};
+      g.w = w; g.x = in; g.ldx = ldin; g.batch = M; g.y = outb; g.yf = outf; g.ldy = ldout;
+      g.epi = epi == GEMM_SWIGLU ? GEMV_SWIGLU : GEMV_STORE;
+      return launch_gemv(s, g);
+    }
+    GemmArgs g{};
+    g.w = w; g.x = in; g.ldx = ldin; g.m = M; g.epi = epi; g.y = outb; g.yf = outf; g.ldy = ldout;
+    return launch_gemm(s, g);
+  };
+  auto cap = [&](int layer) -> float* {
+    if (!ctx->capture || layer < 0) return nullptr;
+    return ctx->capture + ((size_t)layer * ctx->capture_rows + capture_row0) * H;
+  };
+
+  for (int i = 0; i < c.n_layers; ++i) {
+    const LayerW& lw = ctx->layers[i];
+    // h += post_ffn_norm(m) of the previous layer (if any); x = operator_norm(h)
+    NormArgs na{};
+    na.h_in = h; na.h_out = h; na.x_out = x; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
+    na.w_pre = lw.op_norm;
+    if (i > 0) { na.m = m; na.w_post = ctx->layers[i - 1].post_ffn; na.capture = cap(i - 1); }
+    LFM3_TRY(launch_resid_norm(s, na));
+
+    if (lw.type == LFM3_LAYER_CONV) {
+      LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE));
+      ConvArgs ca{};
+      ca.bcx = big; ca.ld = L.big_ld; ca.kernel = lw.conv_kernel;
+      ca.state = ctx->at<bf16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
+      ca.slot_stride = (int64_t)L.conv_slot;
+      ca.out = mix; ca.rows = rows; ca.hidden = H; ca.taps = c.conv_taps;
+      LFM3_TRY(launch_conv(s, ca));
+    } else {
+      LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE));
+      const bool full = lw.type == LFM3_LAYER_FULL;
+      QkRopeArgs qa{};
+      qa.qkvg = big; qa.ld = L.big_ld; qa.q_norm = lw.q_norm; qa.k_norm = lw.k_norm;
+      qa.cos_t = ctx->at<float>(full ? L.cos_f : L.cos_s);
+      qa.sin_t = ctx->at<float>(full ? L.sin_f : L.sin_s);
+      qa.q_out = qrot; qa.kv = kv_for(ctx, lw); qa.rows = rows;
+      qa.n_q_heads = c.n_q_heads; qa.n_kv_heads = c.n_kv_heads; qa.eps = c.norm_eps;
+      LFM3_TRY(launch_qk_rope(s, qa));
+      AttnArgs aa{};
+      aa.q = qrot;
+      aa.gate = big + (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
+      aa.ldg = L.big_ld; aa.kv = qa.kv; aa.rows = rows;
+      aa.window = full ? 0 : c.window;
+      aa.n_q_heads = c.n_q_heads; aa.n_kv_heads = c.n_kv_heads; aa.out = mix;
+      aa.part = ctx->at<float>(L.part);
+      if (decode) {
+        int ms = 1;
+        for (int r = 0; r < M; ++r) {
+          const int lo = full ? 0 : std::max(0, rows.pos[r] - (c.window - 1));
+          ms = std::max(ms, (rows.pos[r] - lo) / attn_decode_split_keys() + 1);
+        }
+        aa.max_splits = ms;
+        LFM3_TRY(launch_attn_decode(s, aa));
+      } else {
+        LFM3_TRY(launch_attn_prefill(s, aa));
+      }
+    }
+    LFM3_TRY(linear(lw.mix_out, mix, H, m, nullptr, H, GEMM_STORE));
+    // h += post_operator_norm(m); x = ffn_norm(h)
+    NormArgs nb{};
+    nb.h_in = h; nb.h_out = h; nb.x_out = x; nb.rows = M; nb.hidden = H; nb.eps = c.norm_eps;
+    nb.m = m; nb.w_post = lw.post_op; nb.w_pre = lw.ffn_norm;
+    LFM3_TRY(launch_resid_norm(s, nb));
+    LFM3_TRY(linear(lw.w13, x, H, nullptr, sb, c.ffn, GEMM_SWIGLU));
+    LFM3_TRY(linear(lw.w2, sb, c.ffn, m, nullptr, H, GEMM_STORE));
+  }
+  NormArgs nf{};
+  nf.h_in = h; nf.h_out = h; nf.x_out = xf; nf.rows = M; nf.hidden = H; nf.eps = c.norm_eps;
+  nf.m = m; nf.w_post = ctx->layers[c.n_layers - 1].post_ffn; nf.w_pre = ctx->emb_norm;
+  nf.capture = cap(c.n_layers - 1);
+  nf.x_copy = hidden_out;
+  LFM3_TRY(launch_resid_norm(s, nf));
+  return LFM3_OK;
+}
+
+lfm3_status head(lfm3_ctx* ctx, const bf16_t* xrows, int n, float* logits, int32_t* ids) {
+  if (!logits && !ids) return LFM3_OK;
+  GemvArgs g{};
+  g.w = ctx->emb; g.x = xrows; g.ldx = ctx->cfg.hidden; g.batch = n; g.epi = GEMV_LOGITS;
+  g.logits = logits; g.ld_logits = ctx->cfg.vocab; g.keys = ctx->at<uint64_t>(ctx->L.keys);
+  LFM3_TRY(launch_gemv(ctx->stream, g));
+  LFM3_TRY(launch_argmax_finalize(ctx->stream, g.keys, ids, n));
+  return LFM3_OK;
+}
+
+// Reserve pages so `slot` can hold `new_len` positions; only host state changes here, the
+// page-table writes are returned in `writes` (index, page) to be enqueued by the caller.
+bool reserve_pages(lfm3_ctx* ctx, int slot, int new_len, std::vector<std::pair<int, int>>& writes, int& budget) {
+  if (n_of_type(ctx->cfg, LFM3_LAYER_FULL) == 0) return true;
+  const int need = (new_len + kPageTokens - 1) / kPageTokens;
+  const int have = (int)ctx->pages[slot].size();
+  if (need - have > budget) return false;
+  budget -= std::max(0, need - have);
+  (void)writes;
+  return true;
+}
+
+lfm3_status commit_pages(lfm3_ctx* ctx, int slot, int new_len) {
+  if (n_of_type(ctx->cfg, LFM3_LAYER_FULL) == 0) return LFM3_OK;
+  const int need = (new_len + kPageTokens - 1) / kPageTokens;
+  auto& pg = ctx->pages[slot];
+  const int first = (int)pg.size();
+  while ((int)pg.size() < need) {
+    pg.push_back(ctx->free_pages.back());
+    ctx->free_pages.pop_back();
+  }
+  if ((int)pg.size() > first) {
+    LFM3_TRY(launch_set_pages(ctx->stream, ctx->at<int32_t>(ctx->L.page_table), slot * ctx->L.max_pages + first,
+                              (int)pg.size() - first, pg.data() + first));
+  }
+  return LFM3_OK;
+}
+
+}  // namespace
+
+// ================================================================================================
+// C ABI
+// ================================================================================================
+extern "C" {
+
+lfm3_status lfm3_query_sizes(const lfm3_config* cfg, size_t* blob_bytes, size_t* workspace_bytes) {
+  if (!cfg) { g_err = "cfg is NULL"; return LFM3_ERR_ARG; }
+  std::string err;
+  if (!check_config(*cfg, err)) { g_err = err; return LFM3_ERR_CONFIG; }
+  if (blob_bytes) *blob_bytes = blob_size_for(*cfg);
+  if (workspace_bytes) *workspace_bytes = make_layout(*cfg).total;
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_validate_blob(const lfm3_config* cfg, const void* blob_host, size_t blob_bytes, char* err, size_t err_len) {
+  std::string e;
+  lfm3_status st = LFM3_OK;
+  if (!cfg || !blob_host) { e = "cfg or blob is NULL"; st = LFM3_ERR_ARG; }
+  else if (!check_config(*cfg, e)) st = LFM3_ERR_CONFIG;
+  else if (!validate_blob_impl(*cfg, (const uint8_t*)blob_host, blob_bytes, blob_bytes, e, nullptr)) st = LFM3_ERR_BLOB;
+  if (st != LFM3_OK) {
+    g_err = e;
+    if (err && err_len) { strncpy(err, e.c_str(), err_len - 1); err[err_len - 1] = 0; }
+  }
+  return st;
+}
+
+lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blob_bytes, void* workspace_dev,
+                        size_t workspace_bytes, void* hip_stream, lfm3_ctx** out) {
+  if (!cfg || !blob_dev || !workspace_dev || !out) { g_err = "NULL argument to lfm3_create"; return LFM3_ERR_ARG; }
+  *out = nullptr;
+  std::string err;
+  if (!check_config(*cfg, err)) { g_err = err; return LFM3_ERR_CONFIG; }
+  const Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.total) {
+    g_err = "workspace " + std::to_string(workspace_bytes) + " B < required " + std::to_string(L.total) + " B";
+    return LFM3_ERR_CAPACITY;
+  }
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) { g_err = "no HIP device"; return LFM3_ERR_DEVICE; }
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) { g_err = std::string("device is ") + prop.gcnArchName + ", this build runs gfx950"; return LFM3_ERR_DEVICE; }
+  // read the header back for admission
+  uint64_t hdr[5];
+  if (blob_bytes < 64 || hipMemcpy(hdr, blob_dev, 40, hipMemcpyDeviceToHost) != hipSuccess) { g_err = "cannot read the blob header"; return LFM3_ERR_BLOB; }
+  uint64_t data_off = hdr[3];
+  if (data_off > blob_bytes || data_off < 64) { g_err = "blob data offset out of range"; return LFM3_ERR_BLOB; }
+  std::vector<uint8_t> head(data_off);
+  if (hipMemcpy(head.data(), blob_dev, data_off, hipMemcpyDeviceToHost) != hipSuccess) { g_err = "cannot read the blob table"; return LFM3_ERR_BLOB; }
+  std::unordered_map<std::string, Entry> ent;
+  if (!validate_blob_impl(*cfg, head.data(), head.size(), blob_bytes, err, &ent)) { g_err = err; return LFM3_ERR_BLOB; }
+  auto* ctx = new lfm3_ctx();
+  ctx->cfg = *cfg;
+  ctx->L = L;
+  ctx->stream = (hipStream_t)hip_stream;
+  ctx->blob = (const uint8_t*)blob_dev;
+  ctx->ws = (uint8_t*)workspace_dev;
+  const lfm3_config& c = *cfg;
+  auto bf = [&](const std::string& n) { return (const bf16_t*)(ctx->blob + ent.at(n).offset); };
+  auto lin = [&](const std::string& n, int N, int K, int bits, int group) {
+    QLinear q;
+    q.q = ctx->blob + ent.at(n + ".q").offset;
+    q.scales = bf(n + ".scales");
+    q.biases = bf(n + ".biases");
+    q.n = N; q.k = K; q.bits = bits; q.group = group;
+    ctx->lin_by_name[n] = q;
+    return q;
+  };
+  int sub[3] = {0, 0, 0};
+  for (int i = 0; i < c.n_layers; ++i) {
+    const std::string p = "layers." + std::to_string(i) + ".";
+    LayerW lw{};
+    lw.type = c.layer_type[i];
+    lw.sub = sub[lw.type]++;
+    lw.op_norm = bf(p + "operator_norm");
+    lw.post_op = bf(p + "post_operator_norm");
+    lw.ffn_norm = bf(p + "ffn_norm");
+    lw.post_ffn = bf(p + "post_ffn_norm");
+    if (lw.type == LFM3_LAYER_CONV) {
+      lw.conv_kernel = bf(p + "conv.kernel");
+      lw.mix_in = lin(p + "conv.in_proj", 3 * c.hidden, c.hidden, c.bits, c.group);
+      lw.mix_out = lin(p + "conv.out_proj", c.hidden, c.hidden, c.bits, c.group);
+    } else {
+      lw.q_norm = bf(p + "attn.q_norm");
+      lw.k_norm = bf(p + "attn.k_norm");
+      lw.mix_in = lin(p + "attn.qkvg_proj", qkvg_rows(c), c.hidden, c.bits, c.group);
+      lw.mix_out = lin(p + "attn.o_proj", c.hidden, c.n_q_heads * c.head_dim, c.bits, c.group);
+    }
+    lw.w13 = lin(p + "ffn.w13", 2 * c.ffn, c.hidden, c.bits, c.group);
+    lw.w2 = lin(p + "ffn.w2", c.hidden, c.ffn, c.bits, c.group);
+    ctx->layers.push_back(lw);
+  }
+  if (c.has_embedding) ctx->emb = lin("embedding", c.vocab, c.hidden, c.embed_bits, c.embed_group);
+  ctx->emb_norm = bf("embedding_norm");
+  ctx->len.assign(c.max_slots, 0);
+  ctx->pages.assign(c.max_slots, {});
+  for (int p = c.n_pages - 1; p >= 0; --p) ctx->free_pages.push_back(p);
+
+  // RoPE tables: angle p * theta^(-2i/head_dim) in float64, stored fp32; pairs past n_pairs get
+  // angle 0 (cos 1, sin 0).
+  {
+    const size_t n = (size_t)c.max_ctx * kHalfDim;
+    std::vector<float> cf(n), sf(n), cs(n), ss(n);
+    for (int i = 0; i < kHalfDim; ++i) {
+      const double invf = i < c.rope_pairs_full ? std::pow(c.rope_theta_full, -2.0 * i / c.head_dim) : 0.0;
+      const double invs = i < c.rope_pairs_sliding ? std::pow(c.rope_theta_sliding, -2.0 * i / c.head_dim) : 0.0;
+      for (int p = 0; p < c.max_ctx; ++p) {
+        const double af = (double)p * invf, as = (double)p * invs;
+        cf[(size_t)p * kHalfDim + i] = (float)std::cos(af);
+        sf[(size_t)p * kHalfDim + i] = (float)std::sin(af);
+        cs[(size_t)p * kHalfDim + i] = (float)std::cos(as);
+        ss[(size_t)p * kHalfDim + i] = (float)std::sin(as);
+      }
+    }
+    bool ok = hipMemcpy(ctx->at<float>(L.cos_f), cf.data(), n * 4, hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemcpy(ctx->at<float>(L.sin_f), sf.data(), n * 4, hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemcpy(ctx->at<float>(L.cos_s), cs.data(), n * 4, hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemcpy(ctx->at<float>(L.sin_s), ss.data(), n * 4, hipMemcpyHostToDevice) == hipSuccess;
+    if (!ok) { delete ctx; g_err = "RoPE table upload failed"; return LFM3_ERR_DEVICE; }
+  }
+  // zero the conv states, page table and argmax keys
+  if (launch_zero(ctx->stream, ctx->at<void>(L.conv_state), (size_t)c.max_slots * L.conv_slot * 2) != hipSuccess ||
+      launch_zero(ctx->stream, ctx->at<void>(L.page_table), (size_t)c.max_slots * L.max_pages * 4) != hipSuccess ||
+      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)std::max(kMaxBatch, L.max_rows) * 8) != hipSuccess) {
+    delete ctx;
+    g_err = "workspace clear failed";
+    return LFM3_ERR_DEVICE;
+  }
+  *out = ctx;
+  return LFM3_OK;
+}
+
+void lfm3_destroy(lfm3_ctx* ctx) { delete ctx; }
+
+lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev, const uint16_t* hidden_dev, int32_t n_rows,
+                         float* logits_last_dev, int32_t* argmax_last_dev, uint16_t* hidden_out_dev) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  const lfm3_config& c = ctx->cfg;
+  if (slot < 0 || slot >= c.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
+  if (n_rows < 1) return ctx->fail(LFM3_ERR_ARG, "n_rows must be >= 1");
+  if ((tokens_dev == nullptr) == (hidden_dev == nullptr)) return ctx->fail(LFM3_ERR_ARG, "pass exactly one of tokens and hidden");
+  if (tokens_dev && !c.has_embedding) return ctx->fail(LFM3_ERR_ARG, "token input needs has_embedding = 1");
+  if ((logits_last_dev || argmax_last_dev) && !c.has_embedding) return ctx->fail(LFM3_ERR_ARG, "logits need the tied head (has_embedding = 1)");
+  if ((int64_t)ctx->len[slot] + n_rows > c.max_ctx)
+    return ctx->fail(LFM3_ERR_CAPACITY, "slot length " + std::to_string(ctx->len[slot]) + " + rows " + std::to_string(n_rows) + " > max_ctx");
+  if (ctx->capture && n_rows > ctx->capture_rows) return ctx->fail(LFM3_ERR_CAPACITY, "capture buffer holds fewer rows than this call");
+  std::vector<std::pair<int, int>> writes;
+  int budget = (int)ctx->free_pages.size();
+  if (!reserve_pages(ctx, slot, ctx->len[slot] + n_rows, writes, budget)) return ctx->fail(LFM3_ERR_CAPACITY, "KV page pool exhausted");
+  lfm3_status st = commit_pages(ctx, slot, ctx->len[slot] + n_rows);
+  if (st != LFM3_OK) return st;
+  const int H = c.hidden;
+  float* h = ctx->at<float>(ctx->L.h);
+  for (int r0 = 0; r0 < n_rows; r0 += c.max_chunk) {
+    const int M = std::min(c.max_chunk, n_rows - r0);
+    Rows rows{};
+    rows.n = M; rows.mode = 0; rows.slot0 = slot; rows.pos0 = ctx->len[slot];
+    if (tokens_dev) {
+      LFM3_TRY(launch_embed(ctx->stream, ctx->emb, tokens_dev + r0, M, h));
+    } else {
+      LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev + (size_t)r0 * H, M, H, h));
+    }
+    st = run_layers(ctx, rows, false, r0, hidden_out_dev ? (bf16_t*)hidden_out_dev + (size_t)r0 * H : nullptr);
+    if (st != LFM3_OK) return st;
+    ctx->len[slot] += M;
+    if (r0 + M == n_rows) {
+      st = head(ctx, ctx->at<bf16_t>(ctx->L.xf) + (size_t)(M - 1) * H, 1, logits_last_dev, argmax_last_dev);
+      if (st != LFM3_OK) return st;
+    }
+  }
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_host, const int32_t* tokens_dev,
+                              const uint16_t* hidden_dev, float* logits_dev, int32_t* argmax_dev, uint16_t* hidden_out_dev) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  const lfm3_config& c = ctx->cfg;
+  if (n < 1 || n > std::min(c.max_slots, (int)kMaxBatch)) return ctx->fail(LFM3_ERR_ARG, "batch n outside [1, min(max_slots, 64)]");
+  if (!slots_host) return ctx->fail(LFM3_ERR_ARG, "slots_host is NULL");
+  if ((tokens_dev == nullptr) == (hidden_dev == nullptr)) return ctx->fail(LFM3_ERR_ARG, "pass exactly one of tokens and hidden");
+  if (tokens_dev && !c.has_embedding) return ctx->fail(LFM3_ERR_ARG, "token input needs has_embedding = 1");
+  if ((logits_dev || argmax_dev) && !c.has_embedding) return ctx->fail(LFM3_ERR_ARG, "logits need the tied head (has_embedding = 1)");
+  if (ctx->capture && n > ctx->capture_rows) return ctx->fail(LFM3_ERR_CAPACITY, "capture buffer holds fewer rows than this call");
+  std::vector<char> seen(c.max_slots, 0);
+  int budget = (int)ctx->free_pages.size();
+  std::vector<std::pair<int, int>> writes;
+  for (int b = 0; b < n; ++b) {
+    const int sl = slots_host[b];
+    if (sl < 0 || sl >= c.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(sl) + " outside [0, max_slots)");
+    if (seen[sl]) return ctx->fail(LFM3_ERR_ARG, "slot " + std::to_string(sl) + " appears twice in one step");
+    seen[sl] = 1;
+    if (ctx->len[sl] + 1 > c.max_ctx) return ctx->fail(LFM3_ERR_CAPACITY, "slot " + std::to_string(sl) + " is at max_ctx");
+    if (!reserve_pages(ctx, sl, ctx->len[sl] + 1, writes, budget)) return ctx->fail(LFM3_ERR_CAPACITY, "KV page pool exhausted");
+  }
+  Rows rows{};
+  rows.n = n; rows.mode = 1;
+  for (int b = 0; b < n; ++b) {
+    rows.slot[b] = slots_host[b];
+    rows.pos[b] = ctx->len[slots_host[b]];
+    lfm3_status st = commit_pages(ctx, slots_host[b], ctx->len[slots_host[b]] + 1);
+    if (st != LFM3_OK) return st;
+  }
+  float* h = ctx->at<float>(ctx->L.h);
+  if (tokens_dev) {
+    LFM3_TRY(launch_embed(ctx->stream, ctx->emb, tokens_dev, n, h));
+  } else {
+    LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev, n, c.hidden, h));
+  }
+  lfm3_status st = run_layers(ctx, rows, true, 0, (bf16_t*)hidden_out_dev);
+  if (st != LFM3_OK) return st;
+  for (int b = 0; b < n; ++b) ctx->len[slots_host[b]] += 1;
+  return head(ctx, ctx->at<bf16_t>(ctx->L.xf), n, logits_dev, argmax_dev);
+}
+
+lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  if (slot < 0 || slot >= ctx->cfg.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
+  const Layout& L = ctx->L;
+  if (L.conv_slot) LFM3_TRY(launch_zero(ctx->stream, ctx->at<bf16_t>(L.conv_state) + (size_t)slot * L.conv_slot, L.conv_slot * 2));
+  for (auto it = ctx->pages[slot].rbegin(); it != ctx->pages[slot].rend(); ++it) ctx->free_pages.push_back(*it);
+  ctx->pages[slot].clear();
+  ctx->len[slot] = 0;
+  return LFM3_OK;
+}
+
+int32_t lfm3_slot_length(const lfm3_ctx* ctx, int32_t slot) {
+  if (!ctx || slot < 0 || slot >= ctx->cfg.max_slots) return -1;
+  return ctx->len[slot];
+}
+
+int32_t lfm3_free_pages(const lfm3_ctx* ctx) { return ctx ? (int32_t)ctx->free_pages.size() : -1; }
+
+const char* lfm3_last_error(const lfm3_ctx* ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+lfm3_status lfm3_capture_layers(lfm3_ctx* ctx, float* dev_buf, int32_t max_rows) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  if (dev_buf && max_rows < 1) return ctx->fail(LFM3_ERR_ARG, "max_rows must be >= 1");
+  ctx->capture = dev_buf;
+  ctx->capture_rows = dev_buf ? max_rows : 0;
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_dequant_rows(lfm3_ctx* ctx, const char* name, int32_t row0, int32_t n_rows, float* out_f32_dev, uint16_t* out_bf16_dev) {
+  if (!ctx || !name) { g_err = "NULL argument"; return LFM3_ERR_ARG; }
+  auto it = ctx->lin_by_name.find(name);
+  if (it == ctx->lin_by_name.end()) return ctx->fail(LFM3_ERR_ARG, std::string("no quantized linear named ") + name);
+  const QLinear& w = it->second;
+  if (row0 < 0 || n_rows < 1 || row0 + n_rows > w.n) return ctx->fail(LFM3_ERR_ARG, "rows outside the tensor");
+  LFM3_TRY(launch_dequant_rows(ctx->stream, w, row0, n_rows, out_f32_dev, (bf16_t*)out_bf16_dev));
+  return LFM3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,253 @@
+"""ctypes binding of liblfm3.so (include/lfm3.h): argument marshalling only.
+
+Every step of the forward pass runs in the HIP library; PyTorch provides device memory and the
+stream. There is no fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblfm3.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "lfm3.h")
+
+STATUS = {0: "LFM3_OK", 1: "LFM3_ERR_ARG", 2: "LFM3_ERR_CONFIG", 3: "LFM3_ERR_BLOB", 4: "LFM3_ERR_SLOT",
+          5: "LFM3_ERR_CAPACITY", 6: "LFM3_ERR_DEVICE"}
+MAX_LAYERS = 64
+MAX_BATCH = 64
+
+
+class LFM3Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "hidden", "ffn", "n_q_heads", "n_kv_heads", "head_dim", "vocab", "conv_taps", "window",
+        "rope_pairs_full", "rope_pairs_sliding", "bits", "group", "embed_bits", "embed_group", "has_embedding",
+        "max_slots", "max_ctx", "page_tokens", "max_chunk", "n_pages")] + [
+        ("norm_eps", ctypes.c_float), ("rope_theta_full", ctypes.c_double), ("rope_theta_sliding", ctypes.c_double),
+        ("layer_type", ctypes.c_uint8 * MAX_LAYERS)]
+
+
+def config_from_dict(d: dict) -> Config:
+    c = Config()
+    for name, _ in Config._fields_:
+        if name == "layer_type":
+            lt = (ctypes.c_uint8 * MAX_LAYERS)(*([int(v) for v in d["layer_type"]] + [0] * (MAX_LAYERS - len(d["layer_type"]))))
+            c.layer_type = lt
+        else:
+            setattr(c, name, d[name])
+    return c
+
+
+_lib = None
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblfm3.so (raises if it is not built: there is no other implementation)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"{path} is not built; run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    sig = {
+        "lfm3_query_sizes": (_i32, [P(Config), P(_sz), P(_sz)]),
+        "lfm3_validate_blob": (_i32, [P(Config), _vp, _sz, ctypes.c_char_p, _sz]),
+        "lfm3_create": (_i32, [P(Config), _vp, _sz, _vp, _sz, _vp, P(_vp)]),
+        "lfm3_destroy": (None, [_vp]),
+        "lfm3_prefill": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp]),
+        "lfm3_decode_batch": (_i32, [_vp, _i32, P(_i32), _vp, _vp, _vp, _vp, _vp]),
+        "lfm3_reset_slot": (_i32, [_vp, _i32]),
+        "lfm3_slot_length": (_i32, [_vp, _i32]),
+        "lfm3_free_pages": (_i32, [_vp]),
+        "lfm3_last_error": (ctypes.c_char_p, [_vp]),
+        "lfm3_capture_layers": (_i32, [_vp, _vp, _i32]),
+        "lfm3_dequant_rows": (_i32, [_vp, ctypes.c_char_p, _i32, _i32, _vp, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_symbols(path: str = HEADER) -> list[str]:
+    """Names of the functions include/lfm3.h declares."""
+    text = open(path).read()
+    return sorted(set(re.findall(r"\b(lfm3_[a-z_]+)\s*\(", text)))
+
+
+def _check(st: int, ctx=None):
+    if st != 0:
+        msg = load_library().lfm3_last_error(ctx).decode(errors="replace")
+        raise LFM3Error(st, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ---- the C calls under their own names -----------------------------------------------------------
+
+def lfm3_query_sizes(cfg: Config):
+    b, w = _sz(), _sz()
+    _check(load_library().lfm3_query_sizes(ctypes.byref(cfg), ctypes.byref(b), ctypes.byref(w)))
+    return b.value, w.value
+
+
+def lfm3_validate_blob(cfg: Config, blob: bytes) -> tuple[int, str]:
+    buf = ctypes.create_string_buffer(512)
+    st = load_library().lfm3_validate_blob(ctypes.byref(cfg), ctypes.c_char_p(blob), len(blob), buf, 512)
+    return st, buf.value.decode(errors="replace")
+
+
+def lfm3_create(cfg: Config, blob_dev, blob_bytes: int, ws_dev, ws_bytes: int, stream_handle: int):
+    ctx = ctypes.c_void_p()
+    _check(load_library().lfm3_create(ctypes.byref(cfg), _ptr(blob_dev), blob_bytes, _ptr(ws_dev), ws_bytes,
+                                      ctypes.c_void_p(stream_handle), ctypes.byref(ctx)))
+    return ctx
+
+
+def lfm3_prefill(ctx, slot, tokens, hidden, n_rows, logits_last, argmax_last, hidden_out):
+    _check(load_library().lfm3_prefill(ctx, slot, _ptr(tokens), _ptr(hidden), n_rows, _ptr(logits_last),
+                                       _ptr(argmax_last), _ptr(hidden_out)), ctx)
+
+
+def lfm3_decode_batch(ctx, slots, tokens, hidden, logits, argmax, hidden_out):
+    arr = (ctypes.c_int32 * len(slots))(*[int(s) for s in slots])
+    _check(load_library().lfm3_decode_batch(ctx, len(slots), arr, _ptr(tokens), _ptr(hidden), _ptr(logits),
+                                            _ptr(argmax), _ptr(hidden_out)), ctx)
+
+
+def lfm3_reset_slot(ctx, slot):
+    _check(load_library().lfm3_reset_slot(ctx, slot), ctx)
+
+
+def lfm3_slot_length(ctx, slot) -> int:
+    return load_library().lfm3_slot_length(ctx, slot)
+
+
+def lfm3_free_pages(ctx) -> int:
+    return load_library().lfm3_free_pages(ctx)
+
+
+def lfm3_capture_layers(ctx, buf, max_rows):
+    _check(load_library().lfm3_capture_layers(ctx, _ptr(buf), max_rows), ctx)
+
+
+def lfm3_dequant_rows(ctx, name: str, row0: int, n_rows: int, out_f32, out_bf16):
+    _check(load_library().lfm3_dequant_rows(ctx, name.encode(), row0, n_rows, _ptr(out_f32), _ptr(out_bf16)), ctx)
+
+
+def lfm3_destroy(ctx):
+    load_library().lfm3_destroy(ctx)
+
+
+# ---- a small owner of the device regions -----------------------------------------------------------
+
+class Engine:
+    """Holds the device blob and workspace (torch tensors) and a context on one stream."""
+
+    def __init__(self, cfg: dict, blob: bytes, device: str = "cuda:0", stream=None):
+        import numpy as np
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.c = config_from_dict(cfg)
+        blob_bytes, ws_bytes = lfm3_query_sizes(self.c)
+        if blob_bytes != len(blob):
+            raise LFM3Error(3, f"blob is {len(blob)} B, config implies {blob_bytes} B")
+        self.stream = stream or torch.cuda.current_stream(self.device)
+        self.blob = torch.from_numpy(np.frombuffer(blob, dtype=np.uint8).copy()).to(self.device)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        self.ws_bytes = ws_bytes
+        torch.cuda.synchronize(self.device)
+        self.ctx = lfm3_create(self.c, self.blob, len(blob), self.ws, ws_bytes, self.stream.cuda_stream)
+
+    def close(self):
+        if self.ctx:
+            self.torch.cuda.synchronize(self.device)
+            lfm3_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _empty(self, shape, dtype):
+        return self.torch.empty(shape, dtype=dtype, device=self.device)
+
+    def prefill(self, slot, tokens=None, hidden=None, logits=True, argmax=True, hidden_out=False):
+        t = self.torch
+        n = int(tokens.shape[0] if tokens is not None else hidden.shape[0])
+        out = {}
+        has_head = bool(self.cfg["has_embedding"])
+        out["logits"] = self._empty((self.cfg["vocab"],), t.float32) if (logits and has_head) else None
+        out["argmax"] = self._empty((1,), t.int32) if (argmax and has_head) else None
+        out["hidden"] = self._empty((n, self.cfg["hidden"]), t.int16) if hidden_out else None
+        lfm3_prefill(self.ctx, slot, tokens, hidden, n, out["logits"], out["argmax"], out["hidden"])
+        return out
+
+    def decode(self, slots, tokens=None, hidden=None, logits=True, argmax=True, hidden_out=False, out=None):
+        t = self.torch
+        n = len(slots)
+        has_head = bool(self.cfg["has_embedding"])
+        if out is None:
+            out = {}
+            out["logits"] = self._empty((n, self.cfg["vocab"]), t.float32) if (logits and has_head) else None
+            out["argmax"] = self._empty((n,), t.int32) if (argmax and has_head) else None
+            out["hidden"] = self._empty((n, self.cfg["hidden"]), t.int16) if hidden_out else None
+        lfm3_decode_batch(self.ctx, slots, tokens, hidden, out.get("logits"), out.get("argmax"), out.get("hidden"))
+        return out
+
+    def reset(self, slot):
+        lfm3_reset_slot(self.ctx, slot)
+
+    def length(self, slot):
+        return lfm3_slot_length(self.ctx, slot)
+
+    def free_pages(self):
+        return lfm3_free_pages(self.ctx)
+
+    def capture(self, buf, max_rows):
+        lfm3_capture_layers(self.ctx, buf, max_rows)
+
+    def dequant_rows(self, name, row0, n, f32=True, bf16=True):
+        t = self.torch
+        k = None
+        # K from the blob-side shape is not needed: the library knows it; ask via a probe size
+        from .synth import tensor_plan
+        for nm, kind, shape, bits, group in tensor_plan(self.cfg):
+            if nm == name:
+                k = shape[1]
+        if k is None:
+            raise LFM3Error(1, f"no quantized linear named {name}")
+        of = self._empty((n, k), t.float32) if f32 else None
+        ob = self._empty((n, k), t.int16) if bf16 else None
+        lfm3_dequant_rows(self.ctx, name, row0, n, of, ob)
+        return of, ob
+
+
+def bf16_to_f32(t):
+    """int16 tensor of bf16 bit patterns -> float32 tensor (same device)."""
+    import torch
+    return (t.to(torch.int32) << 16).view(torch.float32)
+
+
+def f32_to_bf16_bits(t):
+    """float32 tensor -> int16 bf16 bit patterns (round to nearest even)."""
+    import torch
+    return t.to(torch.bfloat16).view(torch.int16)

@@ -1,0 +1,153 @@
+/*
+ * lfm3.h -- C ABI of the MI355X (gfx950) LFM3-1.7B hybrid-decoder forward pass.
+ *
+ * The library runs the decoder described on the "LFM3-1.7B port" knowledge note (comparison table:
+ * 24 layers at width 2048, 13 gated short-conv layers with a 7-tap kernel and a 6-column kept
+ * state, 11 GQA attention layers with 16 q / 4 kv heads of 128, six full layers with partial RoPE
+ * at theta 1e6 and five sliding layers over 256 tokens with RoPE at theta 1e4, a per-head sigmoid
+ * output gate, sandwich RMSNorms with eps 1e-5, a SwiGLU FFN of 7680 and a tied 128000-row head),
+ * with MLX-style affine-quantized linears (TensorFold issue #1491, "Checkpoint handling": 4/6/8-bit
+ * codes in groups of 64 or 32, bf16 scale and bias per group). It runs as chunked prompt prefill
+ * and as batched one-token decode over per-slot streams (TensorFold PR #1508: per-slot conv
+ * states, sliding rings and full-attention KV in pool pages; --parallel lanes).
+ *
+ * Conventions for every call below:
+ *  - Memory: the caller allocates every device region (weight blob, workspace, inputs, outputs)
+ *    and keeps it alive until lfm3_destroy. The library never allocates device memory.
+ *    Pointers named *_dev are device pointers; *_host are host pointers, read during the call only.
+ *  - Asynchrony: work is enqueued on the HIP stream given to lfm3_create; results are valid after
+ *    that stream is synchronised. Greedy ids stay on the device, so a decode loop needs no host sync.
+ *  - Errors: every argument, capacity and slot check runs on the host before anything is enqueued;
+ *    on error nothing is enqueued, the state is unchanged, and lfm3_last_error() names the cause.
+ *  - Threading: one context per stream; a context is not thread-safe.
+ *  - Layouts: row-major. bf16 is passed as uint16_t bit patterns. Hidden rows are [rows, hidden].
+ */
+#ifndef LFM3_H
+#define LFM3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LFM3_OK = 0,
+  LFM3_ERR_ARG = 1,      /* null pointer, bad row count, token id out of [0, vocab), duplicate slot */
+  LFM3_ERR_CONFIG = 2,   /* geometry or scheme this build does not run (named in the message)      */
+  LFM3_ERR_BLOB = 3,     /* weight blob header: magic, names, shapes, dtypes, byte ranges, size      */
+  LFM3_ERR_SLOT = 4,     /* slot index outside [0, max_slots)                                       */
+  LFM3_ERR_CAPACITY = 5, /* rows past max_ctx, page pool exhausted, workspace too small              */
+  LFM3_ERR_DEVICE = 6    /* not a gfx950 device, or a HIP call failed                               */
+} lfm3_status;
+
+enum { LFM3_LAYER_CONV = 0, LFM3_LAYER_FULL = 1, LFM3_LAYER_SLIDING = 2 };
+enum { LFM3_MAX_LAYERS = 64, LFM3_MAX_BATCH = 64 };
+
+/*
+ * Model and runtime configuration. Every field is explicit; nothing has a default (the
+ * "LFM3-1.7B port" note keeps one RoPE dict per layer type; reading a single legacy theta is a
+ * known trap on a sibling model's card).
+ *   geometry:  n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, vocab, conv_taps, window,
+ *              layer_type[i] in {LFM3_LAYER_CONV, _FULL, _SLIDING}
+ *   RoPE:      rope_theta_full / rope_pairs_full (1e6, 32 of 64 pairs rotate: partial, zero tail);
+ *              rope_theta_sliding / rope_pairs_sliding (1e4, all 64 pairs)
+ *   norms:     norm_eps (1e-5)
+ *   weights:   bits in {4, 6, 8}, group in {32, 64} for every linear; embed_bits / embed_group for
+ *              the tied embedding and head; has_embedding = 0 runs without embedding and head
+ *              (rows enter as hidden states, the output is the final normed hidden state)
+ *   runtime:   max_slots streams, max_ctx positions per slot, page_tokens positions per KV page
+ *              (16), max_chunk rows per prefill pass, n_pages pages in the full-attention pool
+ * This build runs head_dim 128, n_q_heads = 4 * n_kv_heads, conv_taps <= 8, page_tokens 16,
+ * hidden and ffn multiples of 512; anything else is refused with LFM3_ERR_CONFIG.
+ */
+typedef struct lfm3_config {
+  int32_t n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, vocab, conv_taps, window;
+  int32_t rope_pairs_full, rope_pairs_sliding;
+  int32_t bits, group, embed_bits, embed_group, has_embedding;
+  int32_t max_slots, max_ctx, page_tokens, max_chunk, n_pages;
+  float norm_eps;
+  double rope_theta_full, rope_theta_sliding;
+  uint8_t layer_type[LFM3_MAX_LAYERS];
+} lfm3_config;
+
+typedef struct lfm3_ctx lfm3_ctx;
+
+/* Sizes the caller must allocate: the exact weight-blob size this config implies and the device
+ * workspace (KV pool, sliding rings, conv states, RoPE tables, activation scratch). Host only. */
+lfm3_status lfm3_query_sizes(const lfm3_config* cfg, size_t* blob_bytes, size_t* workspace_bytes);
+
+/* Admission of a weight blob held in host memory: magic, version, every tensor's name, dtype,
+ * shape and byte range against what cfg implies, and the total size (TensorFold #1491: the loader
+ * checks names, shapes, dtypes and byte ranges before any kernel runs). Host only; err may be NULL. */
+lfm3_status lfm3_validate_blob(const lfm3_config* cfg, const void* blob_host, size_t blob_bytes,
+                               char* err, size_t err_len);
+
+/* Create a context. blob_dev holds the blob (validated by reading its header back); workspace_dev
+ * holds at least workspace_bytes from lfm3_query_sizes. hip_stream is a hipStream_t (NULL = the
+ * default stream). Zeroes every slot and uploads the RoPE tables (built in float64, stored fp32). */
+lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blob_bytes,
+                        void* workspace_dev, size_t workspace_bytes, void* hip_stream,
+                        lfm3_ctx** out);
+
+void lfm3_destroy(lfm3_ctx* ctx);
+
+/*
+ * Prompt prefill: append n_rows rows to `slot`, starting at its current length, in passes of at
+ * most max_chunk rows that carry the conv states, sliding rings and pages across passes ("LFM3-1.7B
+ * port", "Chunked prefill"). Exactly one input: tokens_dev int32 [n_rows] (needs has_embedding) or
+ * hidden_dev bf16 [n_rows, hidden]. Optional outputs (NULL to skip): logits_last_dev fp32 [vocab]
+ * and argmax_last_dev int32 [1] for the last row (needs has_embedding); hidden_out_dev bf16
+ * [n_rows, hidden], the final normed hidden state of every row.
+ */
+lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
+                         const uint16_t* hidden_dev, int32_t n_rows, float* logits_last_dev,
+                         int32_t* argmax_last_dev, uint16_t* hidden_out_dev);
+
+/*
+ * One decode step for n distinct slots (1 <= n <= min(max_slots, LFM3_MAX_BATCH)): row b appends
+ * one position to slots_host[b]. Input: tokens_dev int32 [n] or hidden_dev bf16 [n, hidden].
+ * Outputs (NULL to skip): logits_dev fp32 [n, vocab], argmax_dev int32 [n] (greedy id: ties go to
+ * the lower id, NaN ranks as -inf), hidden_out_dev bf16 [n, hidden].
+ */
+lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_host,
+                              const int32_t* tokens_dev, const uint16_t* hidden_dev,
+                              float* logits_dev, int32_t* argmax_dev, uint16_t* hidden_out_dev);
+
+/* Empty a slot: length 0, conv state zero, its pages back to the pool. */
+lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot);
+
+/* Current length of a slot (positions held), or -1 for a bad slot. */
+int32_t lfm3_slot_length(const lfm3_ctx* ctx, int32_t slot);
+
+/* Free pages in the full-attention pool (a census after resets), or -1 for a NULL ctx. */
+int32_t lfm3_free_pages(const lfm3_ctx* ctx);
+
+/* Message of the last failed call on ctx; with ctx NULL, of the last failed lfm3_create or
+ * host-only call on this thread. Never NULL. */
+const char* lfm3_last_error(const lfm3_ctx* ctx);
+
+/*
+ * Debug capture of the residual stream: while set, every later prefill / decode call writes the
+ * residual after each layer to dev_buf fp32 [n_layers, max_rows, hidden] (row r of the call at
+ * [layer, r, :]; a call may not have more rows than max_rows). dev_buf NULL turns it off. Used by
+ * the per-layer rel-L2 parity tests.
+ */
+lfm3_status lfm3_capture_layers(lfm3_ctx* ctx, float* dev_buf, int32_t max_rows);
+
+/*
+ * Run the library's own dequantisation of one stored linear (name as in the blob, without the
+ * .q/.scales/.biases suffix) for rows [row0, row0 + n_rows): out_f32_dev [n_rows, K] receives
+ * q * scale + bias as computed on the device in fp32 (the decode GEMV's value) and out_bf16_dev
+ * [n_rows, K] its round-to-nearest-even bf16 (the value the prefill GEMM stages in LDS). Either
+ * output may be NULL. For the bit-exact dequant parity test.
+ */
+lfm3_status lfm3_dequant_rows(lfm3_ctx* ctx, const char* name, int32_t row0, int32_t n_rows,
+                              float* out_f32_dev, uint16_t* out_bf16_dev);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LFM3_H */

@@ -253,13 +253,16 @@ class Oracle:
         return st
 
     def _r(self, x):
+        """bf16 diagnostic mode: round where a value is stored in bf16 -- every matmul input (the
+        normed rows, the mixer outputs z and C*y, the gated attention output, the SwiGLU product),
+        the cached k and v, and the conv state. Linear outputs and the residual stream stay wide."""
         return bf16_round(x) if self.bf16 else x
 
     # layers ---------------------------------------------------------------------------------
     def _conv_mixer(self, i, st, u):
         c = self.cfg
         H = c["hidden"]
-        bcx = self._r(u @ self._lin(f"layers.{i}.conv.in_proj").T)
+        bcx = u @ self._lin(f"layers.{i}.conv.in_proj").T
         b, cg, x = bcx[:, :H], bcx[:, H:2 * H], bcx[:, 2 * H:]
         z = self._r(b * x)
         ker = self.blob.bf16(f"layers.{i}.conv.kernel")
@@ -270,13 +273,13 @@ class Oracle:
         if "no_conv_state" not in self.controls:   # control: the state is not written back
             st.conv[i] = self._r(state)
         o = self._r(cg * ys)
-        return self._r(o @ self._lin(f"layers.{i}.conv.out_proj").T)
+        return o @ self._lin(f"layers.{i}.conv.out_proj").T
 
     def _attn_mixer(self, i, st, u, pos, lt):
         c = self.cfg
         hq, hkv, d = c["n_q_heads"], c["n_kv_heads"], c["head_dim"]
         m = u.shape[0]
-        qkvg = self._r(u @ self._lin(f"layers.{i}.attn.qkvg_proj").T)
+        qkvg = u @ self._lin(f"layers.{i}.attn.qkvg_proj").T
         q = qkvg[:, : hq * d].reshape(m, hq, d)
         k = qkvg[:, hq * d: hq * d + hkv * d].reshape(m, hkv, d)
         v = qkvg[:, hq * d + hkv * d: hq * d + 2 * hkv * d].reshape(m, hkv, d)
@@ -294,7 +297,7 @@ class Oracle:
         q = self._r(rope_apply(q, ang))
         k = self._r(rope_apply(k, ang))
         st.k[i] = np.concatenate([st.k[i], k], axis=0)
-        st.v[i] = np.concatenate([st.v[i], v], axis=0)
+        st.v[i] = np.concatenate([st.v[i], self._r(v)], axis=0)
         win = c["window"] if (lt == LT_SLIDING and "no_window" not in self.controls) else None
         o = np.empty((m, hq, d))
         for r0 in range(0, m, 256):
@@ -303,15 +306,15 @@ class Oracle:
         if "no_gate" not in self.controls:
             o = o * sigmoid(g)[:, :, None]
         o = self._r(o.reshape(m, hq * d))
-        return self._r(o @ self._lin(f"layers.{i}.attn.o_proj").T)
+        return o @ self._lin(f"layers.{i}.attn.o_proj").T
 
     def _ffn(self, i, h):
         c = self.cfg
         F = c["ffn"]
         u = self._r(rmsnorm(h, self.blob.bf16(f"layers.{i}.ffn_norm"), c["norm_eps"]))
-        ab = self._r(u @ self._lin(f"layers.{i}.ffn.w13").T)
+        ab = u @ self._lin(f"layers.{i}.ffn.w13").T
         s = self._r(silu(ab[:, :F]) * ab[:, F:])
-        return self._r(s @ self._lin(f"layers.{i}.ffn.w2").T)
+        return s @ self._lin(f"layers.{i}.ffn.w2").T
 
     # forward --------------------------------------------------------------------------------
     def forward(self, st: SlotState, tokens=None, hidden=None, logits: str = "last",
@@ -328,7 +331,6 @@ class Oracle:
             h = self.embedding()[tokens]
         else:
             h = np.asarray(hidden, dtype=np.float64)
-        h = self._r(h)
         m = h.shape[0]
         pos = np.arange(st.length, st.length + m)
         layers = []
@@ -338,9 +340,9 @@ class Oracle:
                 mo = self._conv_mixer(i, st, u)
             else:
                 mo = self._attn_mixer(i, st, u, pos, lt)
-            h = self._r(h + rmsnorm(mo, self.blob.bf16(f"layers.{i}.post_operator_norm"), eps))
+            h = h + rmsnorm(mo, self.blob.bf16(f"layers.{i}.post_operator_norm"), eps)
             f = self._ffn(i, h)
-            h = self._r(h + rmsnorm(f, self.blob.bf16(f"layers.{i}.post_ffn_norm"), eps))
+            h = h + rmsnorm(f, self.blob.bf16(f"layers.{i}.post_ffn_norm"), eps)
             if capture:
                 layers.append(h.copy())
         st.length += m
