@@ -5,9 +5,10 @@
 
 #define LFM3_DEV __device__ __forceinline__
 
-typedef uint16_t bf16_t;  // bf16 bit pattern
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef uint16_t bf16_t;  // bf16 bit pattern (the stored scales and biases, norm and conv weights)
+typedef uint16_t f16_t;   // IEEE fp16 bit pattern (matmul operands, KV cache, conv state)
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_v;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_v;
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 
@@ -44,7 +45,17 @@ LFM3_DEV bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
-LFM3_DEV uint32_t pack_bf2(float lo, float hi) { return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16); }
+LFM3_DEV float h2f(f16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+// float -> fp16, round to nearest even (the hardware conversion).
+LFM3_DEV f16_t f2h(float f) { return __builtin_bit_cast(f16_t, (_Float16)f); }
+LFM3_DEV uint32_t pack_h2(float lo, float hi) { return (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16); }
+// float -> fp16 (RNE) that the compiler cannot fuse with the multiply producing `f` (it would
+// otherwise pick a single-rounding mixed FMA in some template instances and not in others).
+LFM3_DEV f16_t f2h_sep(float f) {
+  uint32_t r;
+  asm("v_cvt_f16_f32 %0, %1" : "=v"(r) : "v"(f));
+  return (f16_t)(r & 0xffffu);
+}
 
 LFM3_DEV float warp_sum(float v) {
 #pragma unroll

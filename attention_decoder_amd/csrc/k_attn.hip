@@ -5,12 +5,12 @@
 // sliding layer, p - j < window ("LFM3-1.7B port", "window_size, with no mask input": absolute query
 // position minus key position below 256). Query head h reads KV head h / 4 ("TensorFold PR #1508":
 // four query heads a KV head). The output of each head is multiplied by sigmoid(g_h) in fp32 and
-// stored bf16 ("LFM3-1.7B port" table row 4 and the fp32-gate paragraph).
+// stored fp16 ("LFM3-1.7B port" table row 4 and the fp32-gate paragraph). q, K, V are fp16.
 #include "kernels.h"
 
 namespace lfm3 {
 
-LFM3_DEV const bf16_t* kv_src(const KvRef& kv, const bf16_t* base, int slot, int pos, int kvh, int n_kv) {
+LFM3_DEV const f16_t* kv_src(const KvRef& kv, const f16_t* base, int slot, int pos, int kvh, int n_kv) {
   if (kv.ring == 0) {
     const int page = kv.page_table[(size_t)slot * kv.max_pages + pos / kPageTokens];
     return base + (((size_t)page * n_kv + kvh) * kPageTokens + (pos % kPageTokens)) * kHeadDim;
@@ -22,7 +22,7 @@ LFM3_DEV float sigmoidf_(float g) { return 1.f / (1.f + __expf(-g)); }
 
 // ---------------------------------------------------------------------------------------------
 // prefill: one block per (32 query rows, kv head); wave w is query head 4 * kvh + w.
-// S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys as rows, queries as columns), so each lane owns one
+// S^T = K Q^T on v_mfma_f32_32x32x16_f16 (keys as rows, queries as columns), so each lane owns one
 // query: its softmax statistics need one exchange with lane ^ 32. Key slot r of the S^T tile reads
 // key pi(r) (bits 2 and 3 of r swapped) so that a lane's accumulators for P V are 8 consecutive keys
 // and feed the B operand of O^T += V^T P^T without moving data.
@@ -33,8 +33,8 @@ constexpr int KS = kHeadDim + 8;   // K tile row stride (elements)
 constexpr int VS = KT + 8;         // V^T tile row stride (elements)
 
 __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[KT * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[kHeadDim * VS];
+  __shared__ __attribute__((aligned(16))) f16_t Ks[KT * KS];
+  __shared__ __attribute__((aligned(16))) f16_t Vt[kHeadDim * VS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int kvh = blockIdx.y;
   const int h = kvh * kQPerKv + wave;
@@ -50,13 +50,13 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
   const int qr = r0 + (lane & 31);
   const int qpos = a.rows.pos0 + qr;
   const bool qvalid = qr < M;
-  bf16x8_v qv[8];
+  f16x8_v qv[8];
   {
-    const bf16_t* qp = a.q + ((size_t)(qvalid ? qr : 0) * nq + h) * kHeadDim;
+    const f16_t* qp = a.q + ((size_t)(qvalid ? qr : 0) * nq + h) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      if (qvalid) qv[s] = *(const bf16x8_v*)(qp + 16 * s + 8 * (lane >> 5));
-      else for (int e = 0; e < 8; ++e) qv[s][e] = (__bf16)0.f;
+      if (qvalid) qv[s] = *(const f16x8_v*)(qp + 16 * s + 8 * (lane >> 5));
+      else for (int e = 0; e < 8; ++e) qv[s][e] = (_Float16)0.f;
     }
   }
   int k_lo = 0;
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
         vv4 = *(const uint4*)(kv_src(a.kv, a.kv.v, slot, j, kvh, nkv) + 8 * c8);
       }
       *(uint4*)(Ks + key * KS + 8 * c8) = kv4;
-      const bf16_t* ve = (const bf16_t*)&vv4;
+      const f16_t* ve = (const f16_t*)&vv4;
 #pragma unroll
       for (int e = 0; e < 8; ++e) Vt[(8 * c8 + e) * VS + key] = ve[e];
     }
@@ -99,8 +99,8 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
     for (int v = 0; v < 16; ++v) st[v] = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8_v kvv = *(const bf16x8_v*)(Ks + kslot * KS + 16 * s + 8 * (lane >> 5));
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kvv, qv[s], st, 0, 0, 0);
+      const f16x8_v kvv = *(const f16x8_v*)(Ks + kslot * KS + 16 * s + 8 * (lane >> 5));
+      st = __builtin_amdgcn_mfma_f32_32x32x16_f16(kvv, qv[s], st, 0, 0, 0);
     }
     // acc v of this lane is key kb + 16(v/8) + 8(lane/32) + v%8 (after the slot permutation)
     float sv[16];
@@ -117,12 +117,12 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
     const float m_new = fmaxf(m_run, mloc);
     const float alpha = m_new == -__builtin_huge_valf() ? 1.f : exp2f(m_run - m_new);
     float lsum = 0.f;
-    bf16x8_v pv[2];
+    f16x8_v pv[2];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float p = m_new == -__builtin_huge_valf() ? 0.f : exp2f(sv[v] - m_new);
       lsum += p;
-      pv[v >> 3][v & 7] = (__bf16)p;
+      pv[v >> 3][v & 7] = (_Float16)p;
     }
     lsum += __shfl_xor(lsum, 32, 64);
     l_run = l_run * alpha + lsum;
@@ -136,8 +136,8 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const bf16x8_v vt = *(const bf16x8_v*)(Vt + (32 * d + (lane & 31)) * VS + 16 * t + 8 * (lane >> 5));
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pv[t], o[d], 0, 0, 0);
+        const f16x8_v vt = *(const f16x8_v*)(Vt + (32 * d + (lane & 31)) * VS + 16 * t + 8 * (lane >> 5));
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt, pv[t], o[d], 0, 0, 0);
       }
     }
   }
@@ -145,14 +145,14 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
   if (!qvalid) return;
   const float gate = sigmoidf_(a.gate[(size_t)qr * a.ldg + h]);
   const float inv = l_run > 0.f ? gate / l_run : 0.f;
-  bf16_t* dst = a.out + (size_t)qr * nq * kHeadDim + (size_t)h * kHeadDim;
+  f16_t* dst = a.out + (size_t)qr * nq * kHeadDim + (size_t)h * kHeadDim;
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
       const int dim = 32 * d + 8 * v4 + 4 * (lane >> 5);
-      const uint32_t w0 = pack_bf2(o[d][4 * v4] * inv, o[d][4 * v4 + 1] * inv);
-      const uint32_t w1 = pack_bf2(o[d][4 * v4 + 2] * inv, o[d][4 * v4 + 3] * inv);
+      const uint32_t w0 = pack_h2(o[d][4 * v4] * inv, o[d][4 * v4 + 1] * inv);
+      const uint32_t w1 = pack_h2(o[d][4 * v4 + 2] * inv, o[d][4 * v4 + 3] * inv);
       *(uint2*)(dst + dim) = make_uint2(w0, w1);
     }
 }
@@ -190,7 +190,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnArgs a) {
   const int j1 = min(pos, j0 + SPLIT - 1);
   for (int i = tid; i < kQPerKv * kHeadDim; i += 256) {
     const int hh = i / kHeadDim, d = i % kHeadDim;
-    qs[hh][d] = bf2f(a.q[((size_t)r * nq + kvh * kQPerKv + hh) * kHeadDim + d]);
+    qs[hh][d] = h2f(a.q[((size_t)r * nq + kvh * kQPerKv + hh) * kHeadDim + d]);
   }
   __syncthreads();
   const int j = j0 + tid;
@@ -200,10 +200,10 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnArgs a) {
 #pragma unroll 4
     for (int c = 0; c < kHeadDim / 8; ++c) {
       const uint4 v = kr[c];
-      const bf16_t* e = (const bf16_t*)&v;
+      const f16_t* e = (const f16_t*)&v;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float kf = bf2f(e[t]);
+        const float kf = h2f(e[t]);
 #pragma unroll
         for (int hh = 0; hh < kQPerKv; ++hh) sc[hh] = fmaf(qs[hh][8 * c + t], kf, sc[hh]);
       }
@@ -234,8 +234,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnArgs a) {
     for (int jj = j0; jj <= j1; ++jj) {
       const uint32_t vv = *(const uint32_t*)(kv_src(a.kv, a.kv.v, slot, jj, kvh, nkv) + 2 * lane);
       const float p = ps[wave][jj - j0];
-      o0 = fmaf(p, bf2f((bf16_t)(vv & 0xffffu)), o0);
-      o1 = fmaf(p, bf2f((bf16_t)(vv >> 16)), o1);
+      o0 = fmaf(p, h2f((f16_t)(vv & 0xffffu)), o0);
+      o1 = fmaf(p, h2f((f16_t)(vv >> 16)), o1);
     }
     float* dst = part + (size_t)wave * head_stride;
     if (lane == 0) { dst[0] = stat[wave][0]; dst[1] = stat[wave][1]; }
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(128) k_attn_merge(AttnArgs a) {
     o = fmaf(w, p[2 + d], o);
   }
   const float gate = sigmoidf_(a.gate[(size_t)r * a.ldg + h]);
-  a.out[(size_t)r * a.n_q_heads * kHeadDim + (size_t)h * kHeadDim + d] = f2bf(l > 0.f ? o / l * gate : 0.f);
+  a.out[(size_t)r * a.n_q_heads * kHeadDim + (size_t)h * kHeadDim + d] = f2h(l > 0.f ? o / l * gate : 0.f);
 }
 
 hipError_t launch_attn_decode(hipStream_t s, const AttnArgs& a) {

@@ -1,8 +1,8 @@
-// Dequant-to-LDS bf16 MFMA GEMM for prompt prefill on gfx950.
+// Dequant-to-LDS fp16 MFMA GEMM for prompt prefill on gfx950.
 //
-// Y[m, n] = sum_k X[m, k] * bf16(q[n, k] * s + bias) with MLX affine weights (TensorFold issue
-// #1491, "Checkpoint handling"). The dequantised weight is rounded once to bf16 as it is staged in
-// LDS; X is the bf16 activation; products accumulate in fp32 on v_mfma_f32_32x32x16_bf16.
+// Y[m, n] = sum_k X[m, k] * f16(q[n, k] * s + bias) with MLX affine weights (TensorFold issue
+// #1491, "Checkpoint handling"). The dequantised weight is rounded once to fp16 as it is staged in
+// LDS; X is the fp16 activation; products accumulate in fp32 on v_mfma_f32_32x32x16_f16.
 //
 // Tile 128 (M) x 128 (N) x 64 (K), 256 threads as 2 x 2 waves of 64 x 64 (2 x 2 MFMA tiles).
 // One LDS buffer per operand with a register prefetch of the next K tile. SwiGLU tiles interleave
@@ -44,8 +44,8 @@ template <int BITS> LFM3_DEV uint32_t code_j(const uint32_t (&w)[8], int j) {
 
 template <int BITS, int EPI>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDSK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * LDSK];
+  __shared__ __attribute__((aligned(16))) f16_t As[BM * LDSK];
+  __shared__ __attribute__((aligned(16))) f16_t Bs[BN * LDSK];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
       for (int j = 0; j < 16; ++j) {
         const float v0 = fmaf((float)code_j<BITS>(wraw, 2 * j), wsc, wbi);
         const float v1 = fmaf((float)code_j<BITS>(wraw, 2 * j + 1), wsc, wbi);
-        pk[j] = pack_bf2(v0, v1);
+        pk[j] = pack_h2(v0, v1);
       }
     } else {
 #pragma unroll
@@ -129,21 +129,21 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_v av[2], bv[2];
+      f16x8_v av[2], bv[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = 64 * wm + 32 * i + (lane & 31);
-        av[i] = *(const bf16x8_v*)(As + r * LDSK + 16 * ks + 8 * (lane >> 5));
+        av[i] = *(const f16x8_v*)(As + r * LDSK + 16 * ks + 8 * (lane >> 5));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = 64 * wn + 32 * j + (lane & 31);
-        bv[j] = *(const bf16x8_v*)(Bs + r * LDSK + 16 * ks + 8 * (lane >> 5));
+        bv[j] = *(const f16x8_v*)(Bs + r * LDSK + 16 * ks + 8 * (lane >> 5));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
     if (kt + 1 < nk) {
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
       if (EPI == GEMM_SWIGLU) {
         const int col = blockIdx.y * 64 + 32 * wn + (lane & 31);
         const float g = acc[i][0][v], u = acc[i][1][v];
-        a.y[(size_t)row * a.ldy + col] = f2bf(g / (1.f + __expf(-g)) * u);
+        a.y[(size_t)row * a.ldy + col] = f2h_sep(g / (1.f + __expf(-g)) * u);
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {

@@ -3,9 +3,9 @@
 // y[b, n] = sum_k x[b, k] * (q[n, k] * s[n, g] + bias[n, g]) with MLX affine weights (TensorFold
 // issue #1491, "Checkpoint handling"). The weights are never rounded: per lane chunk of one group,
 //   sum_k x_k (q_k s + bias) = s * sum_k x_k q_k + bias * sum_k x_k,
-// where q_k enters a bf16 dot2 exactly. For 4- and 6-bit codes the bf16 operand is 128 + q
-// (exponent 2^7 with q in the mantissa, built by one and-or per pair) and s * 128 * sum x is
-// subtracted; 8-bit codes are converted through fp32 (exact below 256). Accumulation is fp32.
+// where q_k enters an fp16 dot2 exactly as 1024 + q (exponent 2^10 with q in the 10-bit mantissa,
+// built by one and-or per pair for every code width) and s * 1024 * sum x is subtracted.
+// x is fp16; accumulation is fp32.
 //
 // Layout: a wave owns a group of 4 rows (SwiGLU: 2 gate rows + the 2 matching up rows); lane l
 // streams chunks l, l+64, ... of each row (16 B of codes: 32 4-bit or 16 8-bit codes; 12 B of
@@ -16,18 +16,25 @@
 namespace lfm3 {
 
 template <int BITS> struct QT;
-template <> struct QT<4> { static constexpr int CH = 32, NDW = 4, NP = 16; static constexpr float OFF = 128.f; };
-template <> struct QT<6> { static constexpr int CH = 16, NDW = 3, NP = 8; static constexpr float OFF = 128.f; };
-template <> struct QT<8> { static constexpr int CH = 16, NDW = 4, NP = 8; static constexpr float OFF = 0.f; };
+template <> struct QT<4> { static constexpr int CH = 32, NDW = 4, NP = 16; };
+template <> struct QT<6> { static constexpr int CH = 16, NDW = 3, NP = 8; };
+template <> struct QT<8> { static constexpr int CH = 16, NDW = 4, NP = 8; };
+constexpr float kMagicOff = 1024.f;       // fp16 0x6400 | q == 1024 + q for q < 1024
+constexpr uint32_t kMagic2 = 0x64006400u;
 
-// Position of code kk of a chunk inside the chunk's bf16 pair stream.
+// Position of code kk of a chunk inside the chunk's fp16 pair stream.
 template <int BITS> LFM3_DEV int pair_pos(int kk) {
   if (BITS == 4) {
     // dword d holds codes 8d..8d+7 as nibbles; pair 4d+j = (code 8d+j, code 8d+j+4)
     const int d = kk >> 3, j = kk & 7;
     return 8 * d + (j < 4 ? 2 * j : 2 * (j - 4) + 1);
   }
-  return kk;  // 6- and 8-bit: pairs of consecutive codes
+  if (BITS == 8) {
+    // dword d holds codes 4d..4d+3 as bytes; pair 2d = (4d, 4d+2), pair 2d+1 = (4d+1, 4d+3)
+    const int d = kk >> 2, j = kk & 3;
+    return 4 * d + (j == 0 ? 0 : j == 1 ? 2 : j == 2 ? 1 : 3);
+  }
+  return kk;  // 6-bit: pairs of consecutive codes
 }
 
 template <int BITS> LFM3_DEV void unpack(const uint32_t (&w)[QT<BITS>::NDW], uint32_t (&p)[QT<BITS>::NP]) {
@@ -35,7 +42,7 @@ template <int BITS> LFM3_DEV void unpack(const uint32_t (&w)[QT<BITS>::NDW], uin
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[4 * d + j] = ((w[d] >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+      for (int j = 0; j < 4; ++j) p[4 * d + j] = ((w[d] >> (4 * j)) & 0x000F000Fu) | kMagic2;
   } else if constexpr (BITS == 6) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -46,23 +53,21 @@ template <int BITS> LFM3_DEV void unpack(const uint32_t (&w)[QT<BITS>::NDW], uin
         const int d = bit >> 5, sh = bit & 31;
         uint32_t v = w[d] >> sh;
         if (sh > 26) v |= w[d + 1] << (32 - sh);
-        c[h] = (v & 63u) | 0x4300u;
+        c[h] = v & 63u;
       }
-      p[i] = c[0] | (c[1] << 16);
+      p[i] = (c[0] | (c[1] << 16)) | kMagic2;
     }
   } else {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const float f0 = (float)(w[d] & 0xffu), f1 = (float)((w[d] >> 8) & 0xffu);
-      const float f2 = (float)((w[d] >> 16) & 0xffu), f3 = (float)(w[d] >> 24);
-      p[2 * d] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-      p[2 * d + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+      p[2 * d] = (w[d] & 0x00FF00FFu) | kMagic2;
+      p[2 * d + 1] = ((w[d] >> 8) & 0x00FF00FFu) | kMagic2;
     }
   }
 }
 
 LFM3_DEV float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), c, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_v, a), __builtin_bit_cast(f16x2_v, b), c, false);
 }
 
 template <int BITS, int BT, int EPI>
@@ -71,7 +76,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int K = a.w.k;
   const int NC = K / Q::CH;
-  uint16_t* xp = (uint16_t*)smem;                 // [BT][K] bf16 in pair order
+  uint16_t* xp = (uint16_t*)smem;                 // [BT][K] fp16 in pair order
   float* xsum = (float*)(smem + (BT * K) / 2);    // [BT][NC]
   for (int i = threadIdx.x; i < BT * K; i += blockDim.x) {
     const int b = i / K, k = i - b * K;
@@ -84,7 +89,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     const int b = i / NC, c = i - b * NC;
     const uint16_t* p = xp + b * K + c * Q::CH;
     float s = 0.f;
-    for (int j = 0; j < Q::CH; ++j) s += bf2f(p[j]);
+    for (int j = 0; j < Q::CH; ++j) s += h2f(p[j]);
     xsum[i] = s;
   }
   __syncthreads();
@@ -147,7 +152,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
           float d = 0.f;
 #pragma unroll
           for (int p = 0; p < Q::NP; ++p) d = dot2(wp[r][p], xv[p], d);
-          acc[r][b] += fmaf(sc[r], d - Q::OFF * X, bi[r] * X);
+          acc[r][b] += fmaf(sc[r], d - kMagicOff * X, bi[r] * X);
         }
       }
     }
@@ -164,6 +169,8 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
           for (int b = 0; b < BT; ++b)
             if (b < a.batch && 4 * g + r < N) a.yf[(size_t)b * a.ldy + 4 * g + r] = acc[r][b];
       } else if (EPI == GEMV_SWIGLU) {
+        // silu(a) * b is rounded to fp32, then to fp16, in every batch-size instance, so a row's
+        // result does not depend on the batch it is decoded in
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -171,7 +178,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
             if (b >= a.batch) continue;
             const float gt = acc[j][b], up = acc[2 + j][b];
             const float sv = gt / (1.f + __expf(-gt)) * up;
-            a.y[(size_t)b * a.ldy + 2 * g + j] = f2bf(sv);
+            a.y[(size_t)b * a.ldy + 2 * g + j] = f2h_sep(sv);
           }
       } else {
 #pragma unroll

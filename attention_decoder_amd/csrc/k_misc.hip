@@ -61,7 +61,7 @@ hipError_t launch_bf16_to_f32(hipStream_t s, const bf16_t* in, int rows, int col
   return hipGetLastError();
 }
 
-__global__ void __launch_bounds__(256) k_dequant_rows(QLinear w, int row0, float* f32, bf16_t* bf) {
+__global__ void __launch_bounds__(256) k_dequant_rows(QLinear w, int row0, float* f32, f16_t* hv) {
   const int r = blockIdx.x;
   const int n = row0 + r;
   const size_t row_bytes = (size_t)w.k * w.bits / 8;
@@ -72,13 +72,13 @@ __global__ void __launch_bounds__(256) k_dequant_rows(QLinear w, int row0, float
     const float v = deq_value(code_at(row, k, w.bits), bf2f(w.scales[(size_t)n * ng + g]),
                               bf2f(w.biases[(size_t)n * ng + g]));
     if (f32) f32[(size_t)r * w.k + k] = v;
-    if (bf) bf[(size_t)r * w.k + k] = f2bf(v);
+    if (hv) hv[(size_t)r * w.k + k] = f2h(v);
   }
 }
 
-hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int rows, float* f32, bf16_t* bf) {
+hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int rows, float* f32, f16_t* h) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dequant_rows, dim3(rows), dim3(256), 0, s, w, row0, f32, bf);
+  hipLaunchKernelGGL(k_dequant_rows, dim3(rows), dim3(256), 0, s, w, row0, f32, h);
   return hipGetLastError();
 }
 
@@ -121,9 +121,9 @@ __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
     const int k = threadIdx.x + i * blockDim.x;
     if (a.m) a.h_out[base + k] = hv[i];
     if (a.capture) a.capture[base + k] = hv[i];
-    const bf16_t xb = f2bf(hv[i] * rh * bf2f(a.w_pre[k]));
-    a.x_out[base + k] = xb;
-    if (a.x_copy) a.x_copy[base + k] = xb;
+    const float xv = hv[i] * rh * bf2f(a.w_pre[k]);
+    a.x_out[base + k] = f2h(xv);
+    if (a.x_copy) a.x_copy[base + k] = xv;
   }
 }
 
@@ -140,7 +140,7 @@ hipError_t launch_resid_norm(hipStream_t s, const NormArgs& a) {
 // One block per row, 4 waves; lane l holds dims l and l + 64 of a head.
 // ---------------------------------------------------------------------------------------------
 
-LFM3_DEV bf16_t* kv_row(const KvRef& kv, bf16_t* base, int slot, int pos, int kvh, int n_kv) {
+LFM3_DEV f16_t* kv_row(const KvRef& kv, f16_t* base, int slot, int pos, int kvh, int n_kv) {
   if (kv.ring == 0) {
     const int page = kv.page_table[(size_t)slot * kv.max_pages + pos / kPageTokens];
     return base + (((size_t)page * n_kv + kvh) * kPageTokens + (pos % kPageTokens)) * kHeadDim;
@@ -168,21 +168,21 @@ __global__ void __launch_bounds__(256) k_qk_rope(QkRopeArgs a) {
     const float n1 = x1 * rr * bf2f(nw[l + kHalfDim]);
     const float o0 = n0 * c - n1 * sn;
     const float o1 = n1 * c + n0 * sn;
-    bf16_t* dst;
+    f16_t* dst;
     if (is_q) {
       dst = a.q_out + ((size_t)r * nq + h) * kHeadDim;
     } else {
       dst = kv_row(a.kv, a.kv.k, slot, pos, h - nq, nkv);
     }
-    dst[l] = f2bf(o0);
-    dst[l + kHalfDim] = f2bf(o1);
+    dst[l] = f2h(o0);
+    dst[l + kHalfDim] = f2h(o1);
   }
-  // v heads: stored bf16 as produced
+  // v heads: stored fp16 as produced
   for (int h = w; h < nkv; h += 4) {
     const float* vp = src + (size_t)(nq + nkv + h) * kHeadDim;
-    bf16_t* dst = kv_row(a.kv, a.kv.v, slot, pos, h, nkv);
-    dst[l] = f2bf(vp[l]);
-    dst[l + kHalfDim] = f2bf(vp[l + kHalfDim]);
+    f16_t* dst = kv_row(a.kv, a.kv.v, slot, pos, h, nkv);
+    dst[l] = f2h(vp[l]);
+    dst[l + kHalfDim] = f2h(vp[l + kHalfDim]);
   }
 }
 
@@ -210,35 +210,35 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   for (int j = 0; j < T; ++j) ker[j] = bf2f(a.kernel[(size_t)c * T + j]);
   auto zrow = [&](int r) -> float {
     const float* p = a.bcx + (size_t)r * a.ld;
-    return bf2f(f2bf(p[c] * p[2 * H + c]));
+    return h2f(f2h(p[c] * p[2 * H + c]));
   };
   auto crow = [&](int r) -> float { return a.bcx[(size_t)r * a.ld + H + c]; };
   float win[kMaxTaps];
   if (a.rows.mode == 1) {
     const int r = blockIdx.y;
-    bf16_t* st = a.state + (size_t)a.rows.slot[r] * a.slot_stride;
-    for (int j = 0; j < S; ++j) win[j] = bf2f(st[(size_t)j * H + c]);
+    f16_t* st = a.state + (size_t)a.rows.slot[r] * a.slot_stride;
+    for (int j = 0; j < S; ++j) win[j] = h2f(st[(size_t)j * H + c]);
     const float z = zrow(r);
     float y = ker[S] * z;
     for (int j = 0; j < S; ++j) y = fmaf(ker[j], win[j], y);
-    a.out[(size_t)r * H + c] = f2bf(crow(r) * y);
-    for (int j = 0; j + 1 < S; ++j) st[(size_t)j * H + c] = f2bf(win[j + 1]);
-    st[(size_t)(S - 1) * H + c] = f2bf(z);
+    a.out[(size_t)r * H + c] = f2h(crow(r) * y);
+    for (int j = 0; j + 1 < S; ++j) st[(size_t)j * H + c] = f2h(win[j + 1]);
+    st[(size_t)(S - 1) * H + c] = f2h(z);
     return;
   }
   const int M = a.rows.n;
   const int r0 = blockIdx.y * kConvRowBlock;
   const int r1 = min(M, r0 + kConvRowBlock);
-  bf16_t* st = a.state + (size_t)a.rows.slot0 * a.slot_stride;
+  f16_t* st = a.state + (size_t)a.rows.slot0 * a.slot_stride;
   for (int j = 0; j < S; ++j) {
     const int t = r0 - S + j;
-    win[j] = t >= 0 ? zrow(t) : bf2f(st[(size_t)(S + t) * H + c]);
+    win[j] = t >= 0 ? zrow(t) : h2f(st[(size_t)(S + t) * H + c]);
   }
   for (int r = r0; r < r1; ++r) {
     const float z = zrow(r);
     float y = ker[S] * z;
     for (int j = 0; j < S; ++j) y = fmaf(ker[j], win[j], y);
-    a.out[(size_t)r * H + c] = f2bf(crow(r) * y);
+    a.out[(size_t)r * H + c] = f2h(crow(r) * y);
     for (int j = 0; j + 1 < S; ++j) win[j] = win[j + 1];
     win[S - 1] = z;
   }
@@ -247,8 +247,8 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
     // (M >= 1) before it is overwritten.
     for (int j = 0; j < S; ++j) {
       const int t = M - S + j;
-      const float v = t >= 0 ? zrow(t) : bf2f(st[(size_t)(S + t) * H + c]);
-      st[(size_t)j * H + c] = f2bf(v);
+      const float v = t >= 0 ? zrow(t) : h2f(st[(size_t)(S + t) * H + c]);
+      st[(size_t)j * H + c] = f2h(v);
     }
   }
 }

@@ -14,19 +14,19 @@ hipError_t launch_embed(hipStream_t s, const QLinear& emb, const int32_t* tokens
 hipError_t launch_bf16_to_f32(hipStream_t s, const bf16_t* in, int rows, int cols, float* out);
 
 // Residual + sandwich norm, one row per block; the residual stream h and the mixer/FFN output m
-// are fp32, the normed matmul input x is bf16:
+// are fp32, the normed matmul input x is fp16:
 //   if m:  h_out = h_in + rmsnorm(m) * w_post   else h_out = h_in (may alias)
-//   x_out = bf16(rmsnorm(h_out) * w_pre)
-// capture (nullable) receives h_out; x_copy (nullable) receives x_out too.
+//   x_out = f16(rmsnorm(h_out) * w_pre)
+// capture (nullable) receives h_out; x_copy (nullable) receives rmsnorm(h_out) * w_pre in fp32.
 struct NormArgs {
   const float* h_in;
   const float* m;
   const bf16_t* w_post;
   const bf16_t* w_pre;
   float* h_out;
-  bf16_t* x_out;
+  f16_t* x_out;
   float* capture;
-  bf16_t* x_copy;
+  float* x_copy;
   int rows, hidden;
   float eps;
 };
@@ -35,8 +35,8 @@ hipError_t launch_resid_norm(hipStream_t s, const NormArgs& a);
 // Where attention K/V live: full layers in pool pages through the slot page table, sliding layers
 // in a per-slot ring of `ring` rows indexed by position mod ring.
 struct KvRef {
-  bf16_t* k;
-  bf16_t* v;
+  f16_t* k;            // fp16 keys after norm + RoPE
+  f16_t* v;            // fp16 values
   const int32_t* page_table;  // full: [max_slots, max_pages]
   int32_t max_pages;
   int32_t ring;               // sliding: rows per slot ring (0 for paged)
@@ -51,7 +51,7 @@ struct QkRopeArgs {
   const bf16_t* k_norm;
   const float* cos_t;
   const float* sin_t;
-  bf16_t* q_out;
+  f16_t* q_out;
   KvRef kv;
   Rows rows;
   int n_q_heads, n_kv_heads;
@@ -59,15 +59,15 @@ struct QkRopeArgs {
 };
 hipError_t launch_qk_rope(hipStream_t s, const QkRopeArgs& a);
 
-// Gated short conv with kept state: z = bf16(B*x); y = sum_j ker[c, j] * [state | z]_j;
-// out = bf16(C * y); state <- last (taps-1) z. bcx [rows, ld] holds B | C | x (fp32).
+// Gated short conv with kept state: z = f16(B*x); y = sum_j ker[c, j] * [state | z]_j;
+// out = f16(C * y); state <- last (taps-1) z. bcx [rows, ld] holds B | C | x (fp32).
 struct ConvArgs {
   const float* bcx;
   int ld;
   const bf16_t* kernel;  // [hidden, taps]
-  bf16_t* state;         // this layer's state of slot 0: [taps-1, hidden]; slot stride below
+  f16_t* state;          // this layer's state of slot 0: [taps-1, hidden]; slot stride below
   int64_t slot_stride;
-  bf16_t* out;           // [rows, hidden]
+  f16_t* out;            // [rows, hidden]
   Rows rows;
   int hidden, taps;
 };
@@ -76,21 +76,21 @@ hipError_t launch_conv(hipStream_t s, const ConvArgs& a);
 hipError_t launch_set_pages(hipStream_t s, int32_t* page_table, int index0, int count, const int32_t* pages);
 hipError_t launch_zero(hipStream_t s, void* p, size_t bytes);
 hipError_t launch_argmax_finalize(hipStream_t s, uint64_t* keys, int32_t* ids, int rows);
-hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int rows, float* f32, bf16_t* bf);
+hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int rows, float* f32, f16_t* h);
 
 // ---- k_gemv.hip --------------------------------------------------------------------------------
 
 enum GemvEpi { GEMV_STORE = 0, GEMV_SWIGLU = 1, GEMV_LOGITS = 2 };
 // y[b, n] = sum_k x[b, k] * (q[n, k] * s + bias) for b < batch (<= 8), exact weights (the per-group
-// factored form). STORE: fp32 yf [batch, ldy]. SWIGLU: rows n and n + N/2 -> bf16 silu(a) * b in
+// factored form). STORE: fp32 yf [batch, ldy]. SWIGLU: rows n and n + N/2 -> fp16 silu(a) * b in
 // y. LOGITS: fp32 logits (nullable) + per-row argmax keys (atomicMax).
 struct GemvArgs {
   QLinear w;
-  const bf16_t* x;  // [batch, ldx]
+  const f16_t* x;   // [batch, ldx]
   int ldx;
   int batch;
   int epi;
-  bf16_t* y;
+  f16_t* y;
   float* yf;
   int ldy;
   float* logits;
@@ -102,15 +102,15 @@ hipError_t launch_gemv(hipStream_t s, const GemvArgs& a);
 // ---- k_gemm.hip --------------------------------------------------------------------------------
 
 enum GemmEpi { GEMM_STORE = 0, GEMM_SWIGLU = 1 };
-// Y[m, n] = sum_k X[m, k] * bf16(q[n, k] * s + bias), MFMA bf16 with fp32 accumulation.
-// STORE writes fp32 yf; SWIGLU writes bf16 y.
+// Y[m, n] = sum_k X[m, k] * f16(q[n, k] * s + bias), MFMA fp16 with fp32 accumulation.
+// STORE writes fp32 yf; SWIGLU writes fp16 y.
 struct GemmArgs {
   QLinear w;
-  const bf16_t* x;  // [M, ldx]
+  const f16_t* x;   // [M, ldx]
   int ldx;
   int m;
   int epi;
-  bf16_t* y;        // [M, ldy]
+  f16_t* y;         // [M, ldy]
   float* yf;
   int ldy;
 };
@@ -119,16 +119,16 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a);
 // ---- k_attn.hip --------------------------------------------------------------------------------
 
 // Causal (full) or sliding-window attention over the cache for a pass's rows; output gated by
-// sigmoid(g) per head and stored bf16 [rows, n_q_heads * 128].
+// sigmoid(g) per head and stored fp16 [rows, n_q_heads * 128].
 struct AttnArgs {
-  const bf16_t* q;     // [rows, n_q_heads, 128] (after norm + RoPE)
+  const f16_t* q;      // [rows, n_q_heads, 128] (after norm + RoPE)
   const float* gate;   // [rows, ldg] (g columns, fp32 linear output)
   int ldg;
   KvRef kv;
   Rows rows;
   int window;          // 0 = full causal
   int n_q_heads, n_kv_heads;
-  bf16_t* out;         // [rows, n_q_heads * 128]
+  f16_t* out;          // [rows, n_q_heads * 128]
   float* part;         // split-K partials (decode)
   int max_splits;
 };

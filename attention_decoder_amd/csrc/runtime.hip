@@ -210,6 +210,14 @@ struct LayerW {
 
 }  // namespace
 
+// Optional per-launch timing: HIP events bracket each launch of a kernel family on the context's
+// stream, with the algorithmic bytes and flops that launch implies.
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+  double bytes, flops;
+};
+
 struct lfm3_ctx {
   lfm3_config cfg;
   Layout L;
@@ -226,6 +234,23 @@ struct lfm3_ctx {
   int capture_rows = 0;
   std::string err;
   std::unordered_map<std::string, QLinear> lin_by_name;
+  bool prof = false;
+  std::vector<ProfRec> prof_recs;
+  std::vector<hipEvent_t> prof_pool;
+  hipEvent_t ev() {
+    if (prof_pool.empty()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      return e;
+    }
+    hipEvent_t e = prof_pool.back();
+    prof_pool.pop_back();
+    return e;
+  }
+  ~lfm3_ctx() {
+    for (auto& r : prof_recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+    for (auto e : prof_pool) (void)hipEventDestroy(e);
+  }
 
   template <class T> T* at(size_t off) { return (T*)(ws + off); }
   lfm3_status fail(lfm3_status s, const std::string& m) {
@@ -276,6 +301,25 @@ size_t blob_size_for(const lfm3_config& c) {
   return off;
 }
 
+// Launch `fn` (returning hipError_t); when profiling, bracket it with events.
+template <class F>
+hipError_t timed(lfm3_ctx* ctx, int kind, double bytes, double flops, F fn) {
+  if (!ctx->prof) return fn();
+  ProfRec r{kind, ctx->ev(), ctx->ev(), bytes, flops};
+  if (!r.a || !r.b) return fn();
+  hipError_t e = hipEventRecord(r.a, ctx->stream);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(r.b, ctx->stream);
+  ctx->prof_recs.push_back(r);
+  return e;
+}
+
+double lin_bytes(const QLinear& w) {
+  return (double)w.n * ((double)w.k * w.bits / 8.0 + 4.0 * w.k / w.group);
+}
+
 #define LFM3_TRY(expr)                                                                      \
   do {                                                                                      \
     hipError_t _e = (expr);                                                                 \
@@ -286,14 +330,14 @@ KvRef kv_for(lfm3_ctx* ctx, const LayerW& lw) {
   KvRef kv{};
   const Layout& L = ctx->L;
   if (lw.type == LFM3_LAYER_FULL) {
-    kv.k = ctx->at<bf16_t>(L.pool_k) + (size_t)lw.sub * L.pool_layer;
-    kv.v = ctx->at<bf16_t>(L.pool_v) + (size_t)lw.sub * L.pool_layer;
+    kv.k = ctx->at<f16_t>(L.pool_k) + (size_t)lw.sub * L.pool_layer;
+    kv.v = ctx->at<f16_t>(L.pool_v) + (size_t)lw.sub * L.pool_layer;
     kv.page_table = ctx->at<int32_t>(L.page_table);
     kv.max_pages = L.max_pages;
     kv.ring = 0;
   } else {
-    kv.k = ctx->at<bf16_t>(L.ring_k) + (size_t)lw.sub * L.ring_layer;
-    kv.v = ctx->at<bf16_t>(L.ring_v) + (size_t)lw.sub * L.ring_layer;
+    kv.k = ctx->at<f16_t>(L.ring_k) + (size_t)lw.sub * L.ring_layer;
+    kv.v = ctx->at<f16_t>(L.ring_v) + (size_t)lw.sub * L.ring_layer;
     kv.ring = L.ring_rows;
   }
   return kv;
@@ -301,33 +345,37 @@ KvRef kv_for(lfm3_ctx* ctx, const LayerW& lw) {
 
 // One pass of the layer stack over `rows` rows whose hidden input is already in h.
 // decode = one row per slot (GEMV path), else a prefill chunk of one slot (GEMM path).
-lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture_row0, bf16_t* hidden_out) {
+lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture_row0, float* hidden_out) {
   const lfm3_config& c = ctx->cfg;
   const Layout& L = ctx->L;
   hipStream_t s = ctx->stream;
   const int M = rows.n;
   const int H = c.hidden;
   float* h = ctx->at<float>(L.h);
-  bf16_t* x = ctx->at<bf16_t>(L.x);
+  f16_t* x = ctx->at<f16_t>(L.x);
   float* big = ctx->at<float>(L.big);
-  bf16_t* sb = ctx->at<bf16_t>(L.sbuf);
-  bf16_t* mix = ctx->at<bf16_t>(L.mix);
-  bf16_t* qrot = ctx->at<bf16_t>(L.qrot);
+  f16_t* sb = ctx->at<f16_t>(L.sbuf);
+  f16_t* mix = ctx->at<f16_t>(L.mix);
+  f16_t* qrot = ctx->at<f16_t>(L.qrot);
   float* m = ctx->at<float>(L.m);
-  bf16_t* xf = ctx->at<bf16_t>(L.xf);
+  f16_t* xf = ctx->at<f16_t>(L.xf);
 
-  // fp32 output (STORE) or bf16 SwiGLU output
-  auto linear = [&](const QLinear& w, const bf16_t* in, int ldin, float* outf, bf16_t* outb, int ldout, int epi) -> hipError_t {
+  // fp32 output (STORE) or fp16 SwiGLU output
+  auto linear = [&](const QLinear& w, const f16_t* in, int ldin, float* outf, f16_t* outb, int ldout, int epi) -> hipError_t {
+    const double out_bytes = epi == GEMM_SWIGLU ? (double)M * (w.n / 2) * 2.0 : (double)M * w.n * 4.0;
+    const double bytes = lin_bytes(w) + (double)M * w.k * 2.0 + out_bytes;
+    const double flops = 2.0 * M * (double)w.n * w.k;
     if (decode) {
       GemvArgs g{};
       g.w = w; g.x = in; g.ldx = ldin; g.batch = M; g.y = outb; g.yf = outf; g.ldy = ldout;
       g.epi = epi == GEMM_SWIGLU ? GEMV_SWIGLU : GEMV_STORE;
-      return launch_gemv(s, g);
+      return timed(ctx, LFM3_PROF_GEMV, bytes, flops, [&] { return launch_gemv(s, g); });
     }
     GemmArgs g{};
     g.w = w; g.x = in; g.ldx = ldin; g.m = M; g.epi = epi; g.y = outb; g.yf = outf; g.ldy = ldout;
-    return launch_gemm(s, g);
+    return timed(ctx, LFM3_PROF_GEMM, bytes, flops, [&] { return launch_gemm(s, g); });
   };
+  const double norm_bytes = (double)M * H * (4 + 4 + 4 + 2);
   auto cap = [&](int layer) -> float* {
     if (!ctx->capture || layer < 0) return nullptr;
     return ctx->capture + ((size_t)layer * ctx->capture_rows + capture_row0) * H;
@@ -340,16 +388,17 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
     na.h_in = h; na.h_out = h; na.x_out = x; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
     na.w_pre = lw.op_norm;
     if (i > 0) { na.m = m; na.w_post = ctx->layers[i - 1].post_ffn; na.capture = cap(i - 1); }
-    LFM3_TRY(launch_resid_norm(s, na));
+    LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, na); }));
 
     if (lw.type == LFM3_LAYER_CONV) {
       LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE));
       ConvArgs ca{};
       ca.bcx = big; ca.ld = L.big_ld; ca.kernel = lw.conv_kernel;
-      ca.state = ctx->at<bf16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
+      ca.state = ctx->at<f16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
       ca.slot_stride = (int64_t)L.conv_slot;
       ca.out = mix; ca.rows = rows; ca.hidden = H; ca.taps = c.conv_taps;
-      LFM3_TRY(launch_conv(s, ca));
+      LFM3_TRY(timed(ctx, LFM3_PROF_CONV, (double)M * H * (12 + 2) + (decode ? (double)M * H * 2 * 2 * (c.conv_taps - 1) : 2.0 * H * 2 * (c.conv_taps - 1)), 0,
+                     [&] { return launch_conv(s, ca); }));
     } else {
       LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE));
       const bool full = lw.type == LFM3_LAYER_FULL;
@@ -359,7 +408,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
       qa.sin_t = ctx->at<float>(full ? L.sin_f : L.sin_s);
       qa.q_out = qrot; qa.kv = kv_for(ctx, lw); qa.rows = rows;
       qa.n_q_heads = c.n_q_heads; qa.n_kv_heads = c.n_kv_heads; qa.eps = c.norm_eps;
-      LFM3_TRY(launch_qk_rope(s, qa));
+      LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, (double)M * L.big_ld * 4, 0, [&] { return launch_qk_rope(s, qa); }));
       AttnArgs aa{};
       aa.q = qrot;
       aa.gate = big + (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
@@ -374,9 +423,20 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
           ms = std::max(ms, (rows.pos[r] - lo) / attn_decode_split_keys() + 1);
         }
         aa.max_splits = ms;
-        LFM3_TRY(launch_attn_decode(s, aa));
+        double kv_bytes = 0;
+        for (int r = 0; r < M; ++r) {
+          const int lo = full ? 0 : std::max(0, rows.pos[r] - (c.window - 1));
+          kv_bytes += (double)(rows.pos[r] - lo + 1) * c.n_kv_heads * kHeadDim * 2 * 2;
+        }
+        LFM3_TRY(timed(ctx, LFM3_PROF_ATTN_DECODE, kv_bytes, 0, [&] { return launch_attn_decode(s, aa); }));
       } else {
-        LFM3_TRY(launch_attn_prefill(s, aa));
+        double fl = 0;
+        for (int r = 0; r < M; ++r) {
+          const double p = rows.pos0 + r;
+          const double t = full ? p + 1 : std::min(p + 1, (double)c.window);
+          fl += 4.0 * kHeadDim * c.n_q_heads * t;
+        }
+        LFM3_TRY(timed(ctx, LFM3_PROF_ATTN_PREFILL, 0, fl, [&] { return launch_attn_prefill(s, aa); }));
       }
     }
     LFM3_TRY(linear(lw.mix_out, mix, H, m, nullptr, H, GEMM_STORE));
@@ -384,7 +444,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
     NormArgs nb{};
     nb.h_in = h; nb.h_out = h; nb.x_out = x; nb.rows = M; nb.hidden = H; nb.eps = c.norm_eps;
     nb.m = m; nb.w_post = lw.post_op; nb.w_pre = lw.ffn_norm;
-    LFM3_TRY(launch_resid_norm(s, nb));
+    LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, nb); }));
     LFM3_TRY(linear(lw.w13, x, H, nullptr, sb, c.ffn, GEMM_SWIGLU));
     LFM3_TRY(linear(lw.w2, sb, c.ffn, m, nullptr, H, GEMM_STORE));
   }
@@ -393,16 +453,17 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
   nf.m = m; nf.w_post = ctx->layers[c.n_layers - 1].post_ffn; nf.w_pre = ctx->emb_norm;
   nf.capture = cap(c.n_layers - 1);
   nf.x_copy = hidden_out;
-  LFM3_TRY(launch_resid_norm(s, nf));
+  LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, nf); }));
   return LFM3_OK;
 }
 
-lfm3_status head(lfm3_ctx* ctx, const bf16_t* xrows, int n, float* logits, int32_t* ids) {
+lfm3_status head(lfm3_ctx* ctx, const f16_t* xrows, int n, float* logits, int32_t* ids) {
   if (!logits && !ids) return LFM3_OK;
   GemvArgs g{};
   g.w = ctx->emb; g.x = xrows; g.ldx = ctx->cfg.hidden; g.batch = n; g.epi = GEMV_LOGITS;
   g.logits = logits; g.ld_logits = ctx->cfg.vocab; g.keys = ctx->at<uint64_t>(ctx->L.keys);
-  LFM3_TRY(launch_gemv(ctx->stream, g));
+  const double bytes = lin_bytes(g.w) + (double)n * g.w.k * 2 + (logits ? (double)n * g.w.n * 4 : 0.0);
+  LFM3_TRY(timed(ctx, LFM3_PROF_GEMV, bytes, 2.0 * n * g.w.n * g.w.k, [&] { return launch_gemv(ctx->stream, g); }));
   LFM3_TRY(launch_argmax_finalize(ctx->stream, g.keys, ids, n));
   return LFM3_OK;
 }
@@ -572,7 +633,7 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
 void lfm3_destroy(lfm3_ctx* ctx) { delete ctx; }
 
 lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev, const uint16_t* hidden_dev, int32_t n_rows,
-                         float* logits_last_dev, int32_t* argmax_last_dev, uint16_t* hidden_out_dev) {
+                         float* logits_last_dev, int32_t* argmax_last_dev, float* hidden_out_dev) {
   if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
   const lfm3_config& c = ctx->cfg;
   if (slot < 0 || slot >= c.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
@@ -599,11 +660,11 @@ lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
     } else {
       LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev + (size_t)r0 * H, M, H, h));
     }
-    st = run_layers(ctx, rows, false, r0, hidden_out_dev ? (bf16_t*)hidden_out_dev + (size_t)r0 * H : nullptr);
+    st = run_layers(ctx, rows, false, r0, hidden_out_dev ? hidden_out_dev + (size_t)r0 * H : nullptr);
     if (st != LFM3_OK) return st;
     ctx->len[slot] += M;
     if (r0 + M == n_rows) {
-      st = head(ctx, ctx->at<bf16_t>(ctx->L.xf) + (size_t)(M - 1) * H, 1, logits_last_dev, argmax_last_dev);
+      st = head(ctx, ctx->at<f16_t>(ctx->L.xf) + (size_t)(M - 1) * H, 1, logits_last_dev, argmax_last_dev);
       if (st != LFM3_OK) return st;
     }
   }
@@ -611,7 +672,7 @@ lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
 }
 
 lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_host, const int32_t* tokens_dev,
-                              const uint16_t* hidden_dev, float* logits_dev, int32_t* argmax_dev, uint16_t* hidden_out_dev) {
+                              const uint16_t* hidden_dev, float* logits_dev, int32_t* argmax_dev, float* hidden_out_dev) {
   if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
   const lfm3_config& c = ctx->cfg;
   if (n < 1 || n > std::min(c.max_slots, (int)kMaxBatch)) return ctx->fail(LFM3_ERR_ARG, "batch n outside [1, min(max_slots, 64)]");
@@ -645,17 +706,17 @@ lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_hos
   } else {
     LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev, n, c.hidden, h));
   }
-  lfm3_status st = run_layers(ctx, rows, true, 0, (bf16_t*)hidden_out_dev);
+  lfm3_status st = run_layers(ctx, rows, true, 0, hidden_out_dev);
   if (st != LFM3_OK) return st;
   for (int b = 0; b < n; ++b) ctx->len[slots_host[b]] += 1;
-  return head(ctx, ctx->at<bf16_t>(ctx->L.xf), n, logits_dev, argmax_dev);
+  return head(ctx, ctx->at<f16_t>(ctx->L.xf), n, logits_dev, argmax_dev);
 }
 
 lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot) {
   if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
   if (slot < 0 || slot >= ctx->cfg.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
   const Layout& L = ctx->L;
-  if (L.conv_slot) LFM3_TRY(launch_zero(ctx->stream, ctx->at<bf16_t>(L.conv_state) + (size_t)slot * L.conv_slot, L.conv_slot * 2));
+  if (L.conv_slot) LFM3_TRY(launch_zero(ctx->stream, ctx->at<f16_t>(L.conv_state) + (size_t)slot * L.conv_slot, L.conv_slot * 2));
   for (auto it = ctx->pages[slot].rbegin(); it != ctx->pages[slot].rend(); ++it) ctx->free_pages.push_back(*it);
   ctx->pages[slot].clear();
   ctx->len[slot] = 0;
@@ -679,13 +740,72 @@ lfm3_status lfm3_capture_layers(lfm3_ctx* ctx, float* dev_buf, int32_t max_rows)
   return LFM3_OK;
 }
 
-lfm3_status lfm3_dequant_rows(lfm3_ctx* ctx, const char* name, int32_t row0, int32_t n_rows, float* out_f32_dev, uint16_t* out_bf16_dev) {
+lfm3_status lfm3_dequant_rows(lfm3_ctx* ctx, const char* name, int32_t row0, int32_t n_rows, float* out_f32_dev, uint16_t* out_f16_dev) {
   if (!ctx || !name) { g_err = "NULL argument"; return LFM3_ERR_ARG; }
   auto it = ctx->lin_by_name.find(name);
   if (it == ctx->lin_by_name.end()) return ctx->fail(LFM3_ERR_ARG, std::string("no quantized linear named ") + name);
   const QLinear& w = it->second;
   if (row0 < 0 || n_rows < 1 || row0 + n_rows > w.n) return ctx->fail(LFM3_ERR_ARG, "rows outside the tensor");
-  LFM3_TRY(launch_dequant_rows(ctx->stream, w, row0, n_rows, out_f32_dev, (bf16_t*)out_bf16_dev));
+  LFM3_TRY(launch_dequant_rows(ctx->stream, w, row0, n_rows, out_f32_dev, (f16_t*)out_f16_dev));
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uint16_t* x_dev, int32_t rows, float* y_dev) {
+  if (!ctx || !name || !x_dev || !y_dev) { g_err = "NULL argument"; return LFM3_ERR_ARG; }
+  auto it = ctx->lin_by_name.find(name);
+  if (it == ctx->lin_by_name.end()) return ctx->fail(LFM3_ERR_ARG, std::string("no quantized linear named ") + name);
+  const QLinear& w = it->second;
+  if (path == 0) {
+    if (rows < 1 || rows > 8) return ctx->fail(LFM3_ERR_ARG, "GEMV rows must be in [1, 8]");
+    GemvArgs g{};
+    g.w = w; g.x = x_dev; g.ldx = w.k; g.batch = rows; g.epi = GEMV_STORE; g.yf = y_dev; g.ldy = w.n;
+    LFM3_TRY(launch_gemv(ctx->stream, g));
+  } else if (path == 2) {
+    if (rows < 1 || rows > 8) return ctx->fail(LFM3_ERR_ARG, "GEMV rows must be in [1, 8]");
+    GemvArgs g{};
+    g.w = w; g.x = x_dev; g.ldx = w.k; g.batch = rows; g.epi = GEMV_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2;
+    LFM3_TRY(launch_gemv(ctx->stream, g));
+  } else if (path == 3) {
+    if (rows < 1) return ctx->fail(LFM3_ERR_ARG, "GEMM rows must be >= 1");
+    GemmArgs g{};
+    g.w = w; g.x = x_dev; g.ldx = w.k; g.m = rows; g.epi = GEMM_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2;
+    LFM3_TRY(launch_gemm(ctx->stream, g));
+  } else if (path == 1) {
+    if (rows < 1) return ctx->fail(LFM3_ERR_ARG, "GEMM rows must be >= 1");
+    GemmArgs g{};
+    g.w = w; g.x = x_dev; g.ldx = w.k; g.m = rows; g.epi = GEMM_STORE; g.yf = y_dev; g.ldy = w.n;
+    LFM3_TRY(launch_gemm(ctx->stream, g));
+  } else {
+    return ctx->fail(LFM3_ERR_ARG, "path must be 0..3");
+  }
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_profile(lfm3_ctx* ctx, int32_t enable) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  if (hipStreamSynchronize(ctx->stream) != hipSuccess) return ctx->fail(LFM3_ERR_DEVICE, "stream sync failed");
+  for (auto& r : ctx->prof_recs) { ctx->prof_pool.push_back(r.a); ctx->prof_pool.push_back(r.b); }
+  ctx->prof_recs.clear();
+  ctx->prof = enable != 0;
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_profile_read(lfm3_ctx* ctx, int32_t kind, double* total_ms, int64_t* launches, double* bytes, double* flops) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  if (kind < 0 || kind >= LFM3_PROF_KINDS) return ctx->fail(LFM3_ERR_ARG, "unknown profile kind");
+  if (hipStreamSynchronize(ctx->stream) != hipSuccess) return ctx->fail(LFM3_ERR_DEVICE, "stream sync failed");
+  double ms = 0, by = 0, fl = 0;
+  int64_t n = 0;
+  for (auto& r : ctx->prof_recs) {
+    if (r.kind != kind) continue;
+    float t = 0;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return ctx->fail(LFM3_ERR_DEVICE, "event timing failed");
+    ms += t; by += r.bytes; fl += r.flops; ++n;
+  }
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = n;
+  if (bytes) *bytes = by;
+  if (flops) *flops = fl;
   return LFM3_OK;
 }
 

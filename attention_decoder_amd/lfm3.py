@@ -72,6 +72,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lfm3_last_error": (ctypes.c_char_p, [_vp]),
         "lfm3_capture_layers": (_i32, [_vp, _vp, _i32]),
         "lfm3_dequant_rows": (_i32, [_vp, ctypes.c_char_p, _i32, _i32, _vp, _vp]),
+        "lfm3_linear": (_i32, [_vp, ctypes.c_char_p, _i32, _vp, _i32, _vp]),
+        "lfm3_profile": (_i32, [_vp, _i32]),
+        "lfm3_profile_read": (_i32, [_vp, _i32, P(ctypes.c_double), P(ctypes.c_int64), P(ctypes.c_double),
+                                     P(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -145,12 +149,30 @@ def lfm3_capture_layers(ctx, buf, max_rows):
     _check(load_library().lfm3_capture_layers(ctx, _ptr(buf), max_rows), ctx)
 
 
-def lfm3_dequant_rows(ctx, name: str, row0: int, n_rows: int, out_f32, out_bf16):
-    _check(load_library().lfm3_dequant_rows(ctx, name.encode(), row0, n_rows, _ptr(out_f32), _ptr(out_bf16)), ctx)
+def lfm3_dequant_rows(ctx, name: str, row0: int, n_rows: int, out_f32, out_f16):
+    _check(load_library().lfm3_dequant_rows(ctx, name.encode(), row0, n_rows, _ptr(out_f32), _ptr(out_f16)), ctx)
 
 
 def lfm3_destroy(ctx):
     load_library().lfm3_destroy(ctx)
+
+
+def lfm3_linear(ctx, name: str, path: int, x, rows: int, y):
+    _check(load_library().lfm3_linear(ctx, name.encode(), path, _ptr(x), rows, _ptr(y)), ctx)
+
+
+PROF_KINDS = {"gemv": 0, "gemm": 1, "attn_decode": 2, "attn_prefill": 3, "conv": 4, "norm": 5, "other": 6}
+
+
+def lfm3_profile(ctx, enable: bool):
+    _check(load_library().lfm3_profile(ctx, 1 if enable else 0), ctx)
+
+
+def lfm3_profile_read(ctx, kind: int):
+    ms, n, by, fl = ctypes.c_double(), ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
+    _check(load_library().lfm3_profile_read(ctx, kind, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(by),
+                                            ctypes.byref(fl)), ctx)
+    return {"ms": ms.value, "launches": n.value, "bytes": by.value, "flops": fl.value}
 
 
 # ---- a small owner of the device regions -----------------------------------------------------------
@@ -197,7 +219,7 @@ class Engine:
         has_head = bool(self.cfg["has_embedding"])
         out["logits"] = self._empty((self.cfg["vocab"],), t.float32) if (logits and has_head) else None
         out["argmax"] = self._empty((1,), t.int32) if (argmax and has_head) else None
-        out["hidden"] = self._empty((n, self.cfg["hidden"]), t.int16) if hidden_out else None
+        out["hidden"] = self._empty((n, self.cfg["hidden"]), t.float32) if hidden_out else None
         lfm3_prefill(self.ctx, slot, tokens, hidden, n, out["logits"], out["argmax"], out["hidden"])
         return out
 
@@ -209,7 +231,7 @@ class Engine:
             out = {}
             out["logits"] = self._empty((n, self.cfg["vocab"]), t.float32) if (logits and has_head) else None
             out["argmax"] = self._empty((n,), t.int32) if (argmax and has_head) else None
-            out["hidden"] = self._empty((n, self.cfg["hidden"]), t.int16) if hidden_out else None
+            out["hidden"] = self._empty((n, self.cfg["hidden"]), t.float32) if hidden_out else None
         lfm3_decode_batch(self.ctx, slots, tokens, hidden, out.get("logits"), out.get("argmax"), out.get("hidden"))
         return out
 
@@ -225,7 +247,29 @@ class Engine:
     def capture(self, buf, max_rows):
         lfm3_capture_layers(self.ctx, buf, max_rows)
 
-    def dequant_rows(self, name, row0, n, f32=True, bf16=True):
+    def linear(self, name, x_f16, path):
+        """y fp32 [rows, N] = x (torch fp16 [rows, K]) through the GEMV (path 0) or GEMM (path 1)."""
+        n = None
+        from .synth import tensor_plan
+        for nm, kind, shape, bits, group in tensor_plan(self.cfg):
+            if nm == name:
+                n = shape[0]
+        if n is None:
+            raise LFM3Error(1, f"no quantized linear named {name}")
+        if path in (2, 3):
+            y = self._empty((x_f16.shape[0], n // 2), self.torch.float16)
+        else:
+            y = self._empty((x_f16.shape[0], n), self.torch.float32)
+        lfm3_linear(self.ctx, name, path, x_f16, x_f16.shape[0], y)
+        return y
+
+    def profile(self, enable: bool):
+        lfm3_profile(self.ctx, enable)
+
+    def profile_read(self):
+        return {k: lfm3_profile_read(self.ctx, v) for k, v in PROF_KINDS.items()}
+
+    def dequant_rows(self, name, row0, n, f32=True, f16=True):
         t = self.torch
         k = None
         # K from the blob-side shape is not needed: the library knows it; ask via a probe size
@@ -236,7 +280,7 @@ class Engine:
         if k is None:
             raise LFM3Error(1, f"no quantized linear named {name}")
         of = self._empty((n, k), t.float32) if f32 else None
-        ob = self._empty((n, k), t.int16) if bf16 else None
+        ob = self._empty((n, k), t.float16) if f16 else None
         lfm3_dequant_rows(self.ctx, name, row0, n, of, ob)
         return of, ob
 

@@ -1,0 +1,261 @@
+"""Throughput of the LFM3-1.7B forward pass on one MI355X, through the C ABI.
+
+Headline (one JSON line on stdout): decode tokens/s at batch 1 on the 24-layer geometry with 4-bit
+g64 weights -- a step is one whole job: a 2048-token prompt prefilled in one 2048-row pass, then
+256 greedy decode steps; value = decode tokens / decode time over the timed steps. The same line
+carries the 2048-token prefill rate, the 8-stream decode and the 8192-token prefill (extras), the
+roofline figure of the dominant kernel (the dequant-GEMV: algorithmic bytes per launch over its
+event-timed launch duration) and the float64 oracle timed on the host cores (cpu_baseline).
+
+Inputs are seeded and synthetic (random-init weights quantized from N(0, 0.02), token ids uniform
+in [0, 128000)); they are resident in HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--prompt", type=int, default=2048)
+    ap.add_argument("--decode", type=int, default=256)
+    ap.add_argument("--no-extras", action="store_true", help="skip the 8-stream decode and 8k prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=48, help="oracle decode steps timed for cpu_baseline")
+    ap.add_argument("--profile-only", action="store_true", help="one short step for rocprofv3 runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is described in DESIGN.md, not built",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from attention_decoder_amd import synth
+    from attention_decoder_amd.lfm3 import Engine
+
+    cfg = synth.full_config(bits=4, group=64, max_slots=8, max_ctx=8704, max_chunk=2048)
+    t0 = time.time()
+    blob = synth.cached_blob(cfg, seed=0)
+    log(f"blob {len(blob) / 1e9:.3f} GB in {time.time() - t0:.1f}s")
+    eng = Engine(cfg, blob)
+    dev = torch.device("cuda:0")
+    prompt = torch.from_numpy(synth.prompt_tokens(2, args.prompt)).to(dev)
+    # device-side greedy loop: the id of step t feeds step t + 1 without a host sync
+    ids = torch.empty((args.decode + 1,), dtype=torch.int32, device=dev)
+    stream = eng.stream
+
+    def job(timing=None):
+        eng.reset(0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        out = eng.prefill(0, tokens=prompt, logits=False, argmax=True)
+        ids[0:1].copy_(out["argmax"])
+        e1.record(stream)
+        for t in range(args.decode):
+            eng.decode([0], tokens=ids[t:t + 1], logits=False, argmax=True,
+                       out={"argmax": ids[t + 1:t + 2]})
+        e2.record(stream)
+        if timing is not None:
+            timing.append((e0, e1, e2))
+
+    if args.profile_only:
+        args.decode = min(args.decode, 32)
+        job()
+        torch.cuda.synchronize()
+        log("profile-only step done")
+        return
+
+    for _ in range(args.warmup):
+        job()
+    torch.cuda.synchronize()
+    log("warmup done")
+    timing = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        job(timing)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    pre_ms = [a.elapsed_time(b) for a, b, _ in timing]
+    dec_ms = [b.elapsed_time(c) for _, b, c in timing]
+    decode_tok_s = args.decode * args.steps / (sum(dec_ms) / 1e3)
+    prefill_tok_s = args.prompt * args.steps / (sum(pre_ms) / 1e3)
+    log(f"decode {decode_tok_s:.1f} tok/s ({np.mean(dec_ms) / args.decode * 1e3:.1f} us/token), "
+        f"prefill {args.prompt} {prefill_tok_s:.0f} tok/s ({np.mean(pre_ms):.2f} ms)")
+
+    # roofline of the dominant decode kernel: one more job with event-bracketed launches
+    eng.profile(True)
+    eng.reset(0)
+    out = eng.prefill(0, tokens=prompt, logits=False, argmax=True)
+    eng.profile(False)
+    eng.profile(True)
+    ids[0:1].copy_(out["argmax"])
+    for t in range(args.decode):
+        eng.decode([0], tokens=ids[t:t + 1], logits=False, argmax=True, out={"argmax": ids[t + 1:t + 2]})
+    prof = eng.profile_read()
+    eng.profile(False)
+    g = prof["gemv"]
+    per_launch_bytes = g["bytes"] / g["launches"]
+    per_launch_us = g["ms"] * 1e3 / g["launches"]
+    achieved = per_launch_bytes / (per_launch_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "k_gemv (decode dequant-GEMV, all linears + tied head)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": round(per_launch_bytes), "us_per_launch": round(per_launch_us, 3),
+                "launches_per_token": g["launches"] // args.decode}
+    breakdown = {k: {"ms_per_token": round(v["ms"] / args.decode, 4), "launches_per_token": v["launches"] / args.decode}
+                 for k, v in prof.items() if v["launches"]}
+    log(f"decode breakdown per token: {breakdown}")
+
+    extras = {"prefill_2048_tok_s": round(prefill_tok_s, 1)}
+    if not args.no_extras:
+        extras.update(run_extras(eng, synth, torch, dev))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, blob, args.cpu_steps)
+
+    tokens_per_step = args.decode
+    line = {
+        "metric": "decode tok/s (1 & 8 streams), prefill tok/s @8k, LFM3-1.7B q4 g64",
+        "value": round(decode_tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded random-init weights, uniform token ids)",
+        "config": {"workload": "LFM3-1.7B geometry (24 layers: 13 conv, 6 full, 5 sliding), affine 4-bit g64; "
+                               "2048-token prompt in one pass, then 256 greedy decode steps at batch 1",
+                   "prompt": args.prompt, "decode_steps": args.decode, "batch": 1, "bits": 4, "group": 64,
+                   "tokens_per_step": tokens_per_step},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+        "decode_breakdown": breakdown,
+    }
+    print(json.dumps(line))
+    eng.close()
+
+
+def run_extras(eng, synth, torch, dev):
+    out = {}
+    # 8 concurrent streams: prompts U[300, 2960] (untimed prefill), then 128 greedy steps at B = 8
+    lens = synth.stream_prompt_lengths(4, 8)
+    prompts = synth.stream_prompts(4, lens)
+    for i in range(8):
+        eng.reset(i)
+        eng.prefill(i, tokens=torch.from_numpy(prompts[i]).to(dev), logits=False, argmax=False)
+    n_steps = 128
+    ids = torch.empty((n_steps + 1, 8), dtype=torch.int32, device=dev)
+    ids[0] = torch.from_numpy(np.array([p[-1] for p in prompts], dtype=np.int32)).to(dev)
+    slots = list(range(8))
+    eng.decode(slots, tokens=ids[0], logits=False, argmax=True, out={"argmax": ids[1]})  # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(eng.stream)
+    for t in range(1, n_steps):
+        eng.decode(slots, tokens=ids[t], logits=False, argmax=True, out={"argmax": ids[t + 1]})
+    e1.record(eng.stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    out["decode_8stream_tok_s"] = round(8 * (n_steps - 1) / (ms / 1e3), 1)
+    out["decode_8stream_prompt_lengths"] = [int(x) for x in lens]
+    log(f"8-stream decode {out['decode_8stream_tok_s']} tok/s")
+    # 8192-token prefill in four 2048-row passes (weights resident; median of 3)
+    toks = torch.from_numpy(synth.prompt_tokens(5, 8192)).to(dev)
+    times = []
+    for r in range(4):
+        eng.reset(0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(eng.stream)
+        eng.prefill(0, tokens=toks, logits=True, argmax=True)
+        b.record(eng.stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    out["prefill_8k_tok_s"] = round(8192 / (ms / 1e3), 1)
+    out["prefill_8k_ms"] = round(ms, 3)
+    # MFMA fraction of the prefill GEMM on the same workload
+    eng.reset(0)
+    eng.profile(True)
+    eng.prefill(0, tokens=toks, logits=True, argmax=True)
+    prof = eng.profile_read()
+    eng.profile(False)
+    g = prof["gemm"]
+    a = prof["attn_prefill"]
+    tf = g["flops"] / (g["ms"] * 1e-3) / 1e12
+    out["prefill_8k_gemm_tflops"] = round(tf, 1)
+    out["prefill_8k_gemm_frac_of_f16_peak"] = round(tf / MFMA_F16_PEAK_TFLOPS, 4)
+    out["prefill_8k_attn_tflops"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1) if a["ms"] else None
+    out["prefill_8k_breakdown_ms"] = {k: round(v["ms"], 3) for k, v in prof.items() if v["launches"]}
+    total_flops = sum(v["flops"] for v in prof.values()) + 2.0 * 128000 * 2048
+    out["prefill_8k_frac_of_f16_peak"] = round(total_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+    log(f"8k prefill {out['prefill_8k_tok_s']} tok/s ({ms:.2f} ms); {out['prefill_8k_breakdown_ms']}")
+    return out
+
+
+def cpu_baseline(cfg, blob, steps):
+    """The float64 oracle on the host cores: decode tokens/s on the same geometry and weights
+    (setup -- weight dequantisation -- untimed; a 16-token prompt, then `steps` decode steps)."""
+    from oracle import Oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    orc = Oracle(cfg, blob)
+    t0 = time.time()
+    orc.preload(min(16, os.cpu_count() or 1))
+    log(f"oracle preload {time.time() - t0:.1f}s")
+    st = orc.new_slot()
+    toks = synth_tokens(16)
+    out = orc.forward(st, tokens=toks, logits="last")
+    tok = int(np.argmax(out["logits"][0]))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out = orc.forward(st, tokens=[tok], logits="last")
+        tok = int(np.argmax(out["logits"][0]))
+    dt = time.perf_counter() - t0
+    orc.drop_cache()
+    val = steps / dt
+    log(f"oracle decode {val:.3f} tok/s on {threads} BLAS threads ({dt:.1f}s)")
+    return {"value": round(val, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle, full 24-layer q4 geometry, {steps} greedy decode steps after a "
+                      f"16-token prompt ({dt:.1f} s timed; weight dequantisation untimed)"}
+
+
+def synth_tokens(n):
+    from attention_decoder_amd import synth
+    return synth.prompt_tokens(9, n)
+
+
+if __name__ == "__main__":
+    main()

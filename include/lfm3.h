@@ -7,7 +7,9 @@
  * at theta 1e6 and five sliding layers over 256 tokens with RoPE at theta 1e4, a per-head sigmoid
  * output gate, sandwich RMSNorms with eps 1e-5, a SwiGLU FFN of 7680 and a tied 128000-row head),
  * with MLX-style affine-quantized linears (TensorFold issue #1491, "Checkpoint handling": 4/6/8-bit
- * codes in groups of 64 or 32, bf16 scale and bias per group). It runs as chunked prompt prefill
+ * codes in groups of 64 or 32, bf16 scale and bias per group). Matmul operands, the KV cache and
+ * the conv state are fp16; reductions, linear outputs and the residual stream are fp32; the
+ * quantized weights are used as stored (exact in decode). It runs as chunked prompt prefill
  * and as batched one-token decode over per-slot streams (TensorFold PR #1508: per-slot conv
  * states, sliding rings and full-attention KV in pool pages; --parallel lanes).
  *
@@ -20,7 +22,7 @@
  *  - Errors: every argument, capacity and slot check runs on the host before anything is enqueued;
  *    on error nothing is enqueued, the state is unchanged, and lfm3_last_error() names the cause.
  *  - Threading: one context per stream; a context is not thread-safe.
- *  - Layouts: row-major. bf16 is passed as uint16_t bit patterns. Hidden rows are [rows, hidden].
+ *  - Layouts: row-major. bf16/fp16 are passed as uint16_t bit patterns. Hidden rows are [rows, hidden].
  */
 #ifndef LFM3_H
 #define LFM3_H
@@ -98,22 +100,22 @@ void lfm3_destroy(lfm3_ctx* ctx);
  * most max_chunk rows that carry the conv states, sliding rings and pages across passes ("LFM3-1.7B
  * port", "Chunked prefill"). Exactly one input: tokens_dev int32 [n_rows] (needs has_embedding) or
  * hidden_dev bf16 [n_rows, hidden]. Optional outputs (NULL to skip): logits_last_dev fp32 [vocab]
- * and argmax_last_dev int32 [1] for the last row (needs has_embedding); hidden_out_dev bf16
+ * and argmax_last_dev int32 [1] for the last row (needs has_embedding); hidden_out_dev fp32
  * [n_rows, hidden], the final normed hidden state of every row.
  */
 lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
                          const uint16_t* hidden_dev, int32_t n_rows, float* logits_last_dev,
-                         int32_t* argmax_last_dev, uint16_t* hidden_out_dev);
+                         int32_t* argmax_last_dev, float* hidden_out_dev);
 
 /*
  * One decode step for n distinct slots (1 <= n <= min(max_slots, LFM3_MAX_BATCH)): row b appends
  * one position to slots_host[b]. Input: tokens_dev int32 [n] or hidden_dev bf16 [n, hidden].
  * Outputs (NULL to skip): logits_dev fp32 [n, vocab], argmax_dev int32 [n] (greedy id: ties go to
- * the lower id, NaN ranks as -inf), hidden_out_dev bf16 [n, hidden].
+ * the lower id, NaN ranks as -inf), hidden_out_dev fp32 [n, hidden].
  */
 lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_host,
                               const int32_t* tokens_dev, const uint16_t* hidden_dev,
-                              float* logits_dev, int32_t* argmax_dev, uint16_t* hidden_out_dev);
+                              float* logits_dev, int32_t* argmax_dev, float* hidden_out_dev);
 
 /* Empty a slot: length 0, conv state zero, its pages back to the pool. */
 lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot);
@@ -139,12 +141,47 @@ lfm3_status lfm3_capture_layers(lfm3_ctx* ctx, float* dev_buf, int32_t max_rows)
 /*
  * Run the library's own dequantisation of one stored linear (name as in the blob, without the
  * .q/.scales/.biases suffix) for rows [row0, row0 + n_rows): out_f32_dev [n_rows, K] receives
- * q * scale + bias as computed on the device in fp32 (the decode GEMV's value) and out_bf16_dev
- * [n_rows, K] its round-to-nearest-even bf16 (the value the prefill GEMM stages in LDS). Either
- * output may be NULL. For the bit-exact dequant parity test.
+ * q * scale + bias as computed on the device in fp32 (the embedding's value; the decode GEMV never
+ * forms it, using scale * sum(x q) + bias * sum(x) with exact q) and out_f16_dev [n_rows, K] its
+ * round-to-nearest-even fp16 (the value the prefill GEMM stages in LDS). Either output may be
+ * NULL. For the bit-exact dequant parity test.
  */
 lfm3_status lfm3_dequant_rows(lfm3_ctx* ctx, const char* name, int32_t row0, int32_t n_rows,
-                              float* out_f32_dev, uint16_t* out_bf16_dev);
+                              float* out_f32_dev, uint16_t* out_f16_dev);
+
+/*
+ * One stored linear (name without the .q/.scales/.biases suffix) applied to caller rows, for
+ * kernel-level parity: y_dev fp32 [rows, N] = x_dev fp16 [rows, K] times the dequantised weight,
+ * through the decode dequant-GEMV (path 0, rows in [1, 8], exact weights) or the prefill
+ * dequant-to-LDS MFMA GEMM (path 1, weights rounded to fp16 in LDS). Paths 2 (GEMV) and 3 (GEMM)
+ * apply the SwiGLU epilogue of a fused [gate | up] weight instead: y_dev then receives fp16
+ * [rows, N/2] = silu(gate) * up.
+ */
+lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uint16_t* x_dev,
+                        int32_t rows, float* y_dev);
+
+/*
+ * Kernel-family timing for roofline figures. lfm3_profile(ctx, 1) starts recording: every later
+ * launch of a family is bracketed by HIP events on the context's stream and tagged with the
+ * algorithmic bytes and flops it implies (weights + activations read and written; 2*M*N*K for a
+ * linear; 4*128*heads per visible key for attention). lfm3_profile(ctx, 0) stops; either call
+ * drops earlier records. lfm3_profile_read synchronises the stream and returns, for one family,
+ * the summed event time (ms), the launch count and the summed bytes and flops. Any output may be
+ * NULL. The events cost a little time, so throughput is measured with recording off.
+ */
+enum {
+  LFM3_PROF_GEMV = 0,          /* decode dequant-GEMV (linears and the tied head)   */
+  LFM3_PROF_GEMM = 1,          /* prefill dequant-to-LDS MFMA GEMM                  */
+  LFM3_PROF_ATTN_DECODE = 2,   /* split-K decode attention + merge                  */
+  LFM3_PROF_ATTN_PREFILL = 3,  /* flash prefill attention                           */
+  LFM3_PROF_CONV = 4,          /* gated short conv                                  */
+  LFM3_PROF_NORM = 5,          /* residual + RMSNorm                                */
+  LFM3_PROF_OTHER = 6,         /* q/k norm + RoPE + KV store                        */
+  LFM3_PROF_KINDS = 7
+};
+lfm3_status lfm3_profile(lfm3_ctx* ctx, int32_t enable);
+lfm3_status lfm3_profile_read(lfm3_ctx* ctx, int32_t kind, double* total_ms, int64_t* launches,
+                              double* bytes, double* flops);
 
 #ifdef __cplusplus
 }

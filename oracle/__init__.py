@@ -16,5 +16,5 @@ Parity status of each part is listed in ``oracle/ref.py``'s module docstring.
 """
 from .ref import (  # noqa: F401
     Blob, Oracle, SlotState, dequant, unpack_codes, rmsnorm, rope_angles, rope_apply, silu, sigmoid,
-    attention_rows, conv_step, greedy_argmax, bf16_round,
+    attention_rows, conv_step, greedy_argmax, bf16_round, f16_round, top2_margin,
 )

@@ -113,12 +113,17 @@ def load_linear(blob: Blob, name: str, bits: int, group: int, row_chunk: int = 8
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Nearest bf16 value (ties to even) of float64 data; used only by the bf16 diagnostic mode."""
+    """Nearest bf16 value (ties to even) of float64 data."""
     f = np.asarray(x, dtype=np.float64)
     m, e = np.frexp(f)                      # f = m * 2^e, 0.5 <= |m| < 1
     scaled = np.ldexp(m, 8)                 # 8 significant bits
     r = np.round(scaled)                    # numpy rounds half to even
     return np.ldexp(r, e - 8)
+
+
+def f16_round(x: np.ndarray) -> np.ndarray:
+    """Nearest IEEE fp16 value (ties to even, with fp16 range); used only by the storage diagnostic."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
 def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
@@ -220,11 +225,11 @@ class Oracle:
     """The decoder in float64. ``controls`` plants model-level mistakes for negative tests:
     'no_gate', 'rotate_all' (full layers rotate every pair), 'no_window', 'no_conv_state'."""
 
-    def __init__(self, cfg: dict, blob: bytes, controls: tuple = (), bf16_points: bool = False):
+    def __init__(self, cfg: dict, blob: bytes, controls: tuple = (), storage_points: bool = False):
         self.cfg = cfg
         self.blob = Blob(blob)
         self.controls = set(controls)
-        self.bf16 = bf16_points
+        self.storage = storage_points
         self._w = {}
 
     # weights -------------------------------------------------------------------------------
@@ -241,6 +246,20 @@ class Oracle:
     def drop_cache(self):
         self._w.clear()
 
+    def preload(self, threads: int = 8):
+        """Dequantize every linear up front (setup only; the same load_linear per tensor)."""
+        from concurrent.futures import ThreadPoolExecutor
+        c = self.cfg
+        names = [(n, None, None) for n in sorted({k.rsplit(".", 1)[0] for k in self.blob.entries
+                                                    if k.endswith(".q") and not k.startswith("embedding")})]
+        if c["has_embedding"]:
+            names.append(("embedding", c["embed_bits"], c["embed_group"]))
+        todo = [t for t in names if t[0] not in self._w]
+        with ThreadPoolExecutor(threads) as ex:
+            for (n, _, _), w in zip(todo, ex.map(lambda t: load_linear(self.blob, t[0], t[1] or c["bits"],
+                                                                      t[2] or c["group"]), todo)):
+                self._w[n] = w
+
     def new_slot(self) -> SlotState:
         c = self.cfg
         st = SlotState()
@@ -253,10 +272,11 @@ class Oracle:
         return st
 
     def _r(self, x):
-        """bf16 diagnostic mode: round where a value is stored in bf16 -- every matmul input (the
-        normed rows, the mixer outputs z and C*y, the gated attention output, the SwiGLU product),
-        the cached k and v, and the conv state. Linear outputs and the residual stream stay wide."""
-        return bf16_round(x) if self.bf16 else x
+        """Storage diagnostic mode (off by default; parity is judged against plain float64): round
+        to fp16 where the GPU stores fp16 -- every matmul input (the normed rows, the conv's z and
+        C*y, the gated attention output, the SwiGLU product), the cached k and v, and the conv
+        state. Linear outputs and the residual stream stay wide."""
+        return f16_round(x) if self.storage else x
 
     # layers ---------------------------------------------------------------------------------
     def _conv_mixer(self, i, st, u):

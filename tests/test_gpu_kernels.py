@@ -1,0 +1,88 @@
+"""Kernel-level GPU parity: the decode dequant-GEMV and the prefill dequant-to-LDS MFMA GEMM on
+real layer shapes of the seeded three-layer slice, against the float64 oracle's dequantised
+weights times the same fp16 rows (MLX affine: w = q * scale + bias per group of 64)."""
+import numpy as np
+import pytest
+
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = ["layers.0.conv.in_proj", "layers.1.attn.qkvg_proj", "layers.2.ffn.w13", "layers.2.ffn.w2",
+          "layers.2.attn.o_proj"]
+
+
+@pytest.fixture(scope="module")
+def eng(slice3):
+    from attention_decoder_amd.lfm3 import Engine
+    cfg, blob = slice3
+    e = Engine(dict(cfg, max_slots=8, max_chunk=512), blob)
+    yield e
+    e.close()
+
+
+@pytest.fixture(scope="module")
+def weights(slice3):
+    cfg, blob = slice3
+    b = ref.Blob(blob)
+    return {n: ref.load_linear(b, n, cfg["bits"], cfg["group"]) for n in SHAPES}
+
+
+def _x(torch, rows, k, seed):
+    x = np.random.default_rng(seed).standard_normal((rows, k)).astype(np.float16)
+    return x, torch.from_numpy(x).cuda()
+
+
+@pytest.mark.parametrize("name", SHAPES)
+def test_gemv_matches_float64(eng, weights, name):
+    import torch
+    w = weights[name]
+    for rows in (1, 3, 8):
+        x, xd = _x(torch, rows, w.shape[1], rows)
+        y = eng.linear(name, xd, 0).cpu().numpy().astype(np.float64)
+        want = x.astype(np.float64) @ w.T
+        err = np.abs(y - want).max() / np.abs(want).max()
+        # exact weights and fp16 inputs; the 1024 + q operand form costs ~2^10/q of the fp32
+        # accumulation precision (about 3e-5 relative), still far below fp16 input rounding
+        assert err < 1e-4, (name, rows, err)
+
+
+@pytest.mark.parametrize("name", SHAPES)
+def test_gemm_matches_float64(eng, weights, name):
+    import torch
+    w = weights[name]
+    for rows in (1, 77, 300):
+        x, xd = _x(torch, rows, w.shape[1], 10 + rows)
+        y = eng.linear(name, xd, 1).cpu().numpy().astype(np.float64)
+        want_exact = x.astype(np.float64) @ w.T
+        want_f16w = x.astype(np.float64) @ ref.f16_round(w).T      # the GEMM's stated rounding point
+        assert np.abs(y - want_f16w).max() / np.abs(want_f16w).max() < 2e-5, (name, rows)
+        rel = np.linalg.norm(y - want_exact) / np.linalg.norm(want_exact)
+        assert rel < 1e-3, (name, rows, rel)
+
+
+@pytest.mark.parametrize("name,path", [(n, 0) for n in SHAPES] + [("layers.2.ffn.w13", 2)])
+def test_gemv_rows_independent_of_batch(eng, weights, name, path):
+    """A row's GEMV result does not depend on the other rows of the batch or its position."""
+    import torch
+    x, xd = _x(torch, 8, weights[name].shape[1], 99)
+    solo = [eng.linear(name, xd[i:i + 1].contiguous(), path) for i in range(8)]
+    for rows in (2, 3, 4, 8):
+        y = eng.linear(name, xd[:rows].contiguous(), path)
+        for i in range(rows):
+            d = (y[i].float() - solo[i][0].float()).abs().max().item()
+            assert d == 0.0, (rows, i, d)
+
+
+def test_swiglu_epilogues(eng, weights):
+    """silu(gate) * up of the fused [w1 | w3] weight, GEMV and GEMM, against float64."""
+    import torch
+    w = weights["layers.2.ffn.w13"]
+    F = w.shape[0] // 2
+    for path, rows in ((2, 4), (3, 96)):
+        x, xd = _x(torch, rows, w.shape[1], 7 + path)
+        y = eng.linear("layers.2.ffn.w13", xd, path).float().cpu().numpy().astype(np.float64)
+        ab = x.astype(np.float64) @ w.T
+        want = ab[:, :F] / (1 + np.exp(-ab[:, :F])) * ab[:, F:]
+        rel = np.linalg.norm(y - want) / np.linalg.norm(want)
+        assert rel < 2e-3, (path, rel)

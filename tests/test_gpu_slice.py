@@ -2,7 +2,7 @@
 
 Calls go through the C ABI (liblfm3.so via the ctypes binding) and are compared with the float64
 oracle on the same seeded inputs:
-- dequantised weights bit-exact (fp32 value and its RNE bf16);
+- dequantised weights bit-exact (fp32 value and its RNE fp16, the prefill GEMM's LDS value);
 - hidden state after every layer within rel-L2 1e-2, final normed hidden within rel-L2 1e-2;
 - prompt prefill vs one-row decode at cut points; chunked prefill across the 256-token seam;
 - concurrent == solo: a batched decode row is bitwise equal to the same row decoded alone.
@@ -16,7 +16,7 @@ from oracle import Oracle, ref
 pytestmark = pytest.mark.gpu
 
 REL_L2 = 1e-2        # per layer, over the rows of the pass (the stated bar)
-ROW_REL_L2 = 2e-2    # any single row: sanity bound; the oracle's own bf16-storage mode sits at ~1.1%
+ROW_REL_L2 = 1e-2    # and any single row
 
 
 def _rel(a, b):
@@ -59,8 +59,8 @@ def test_dequant_bit_exact(eng, slice3, torch_dev):
         want = ref.load_linear(b, name, cfg["bits"], cfg["group"], row_chunk=4096)[rows[0]:rows[0] + rows[1]]
         got = f32.cpu().numpy().astype(np.float64)
         assert np.array_equal(got, want), name
-        got_bf = _f32(bf)
-        assert np.array_equal(got_bf, ref.bf16_round(want)), name
+        got_h = bf.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got_h, ref.f16_round(want)), name
 
 
 def _run_gpu(eng, torch, x_bits, n_prefill, slot=0):
@@ -72,7 +72,7 @@ def _run_gpu(eng, torch, x_bits, n_prefill, slot=0):
     eng.reset(slot)
     eng.capture(cap, n)
     xd = _rows_dev(torch, x_bits)
-    final = torch.zeros((n, H), dtype=torch.int16, device="cuda")
+    final = torch.zeros((n, H), dtype=torch.float32, device="cuda")
     out = eng.prefill(slot, hidden=xd[:n_prefill], hidden_out=True)
     final[:n_prefill] = out["hidden"]
     layers = [[cap[l, :n_prefill].clone()] for l in range(L)]
@@ -83,7 +83,7 @@ def _run_gpu(eng, torch, x_bits, n_prefill, slot=0):
             layers[l].append(cap[l, :1].clone())
     eng.capture(None, 0)
     torch.cuda.synchronize()
-    return [torch.cat(x).cpu().numpy().astype(np.float64) for x in layers], _f32(final)
+    return [torch.cat(x).cpu().numpy().astype(np.float64) for x in layers], final.cpu().numpy().astype(np.float64)
 
 
 @pytest.fixture(scope="module")

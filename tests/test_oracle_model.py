@@ -91,11 +91,11 @@ def test_conv_state_not_written_back_moves_the_output(slice3, rows300, whole300)
     assert _rel(out["final"], whole300["final"][100:110]) > 1e-3
 
 
-def test_bf16_points_stay_close(slice3, rows300, whole300):
-    """The bf16-storage diagnostic mode stays within the per-layer rel-L2 bar of float64."""
+def test_storage_points_stay_close(slice3, rows300, whole300):
+    """The fp16-storage diagnostic mode stays well within the per-layer rel-L2 bar of float64."""
     cfg, blob = slice3
-    orc = Oracle(cfg, blob, bf16_points=True)
+    orc = Oracle(cfg, blob, storage_points=True)
     st = orc.new_slot()
     out = orc.forward(st, hidden=rows300[:80], capture=True)
     for li in range(3):
-        assert _rel(out["layers"][li], whole300["layers"][li][:80]) < 1e-2
+        assert _rel(out["layers"][li], whole300["layers"][li][:80]) < 2e-3

@@ -333,6 +333,14 @@ def test_argmax_ties_and_nan():
     assert ref.greedy_argmax(x).tolist() == [1, 2]
 
 
+def test_f16_round_properties():
+    # exact on fp16 values, ties to even, 11 significant bits
+    assert ref.f16_round(np.array([1.0 + 2 ** -10]))[0] == 1.0 + 2 ** -10
+    assert ref.f16_round(np.array([1.0 + 2 ** -11]))[0] == 1.0            # tie -> even
+    assert ref.f16_round(np.array([1.0 + 3 * 2 ** -11]))[0] == 1.0 + 2 ** -9  # tie -> even (up)
+    assert ref.f16_round(np.array([2049.0]))[0] == 2048.0
+
+
 def test_bf16_round_matches_storage_rounding():
     rng = np.random.default_rng(8)
     x = rng.standard_normal(10000).astype(np.float32)
