@@ -4,12 +4,14 @@
 #include <stdint.h>
 
 #define LFM3_DEV __device__ __forceinline__
+#define LFM3_HOST_DEV __host__ __device__ __forceinline__
 
 typedef uint16_t bf16_t;  // bf16 bit pattern (the stored scales and biases, norm and conv weights)
 typedef uint16_t f16_t;   // IEEE fp16 bit pattern (matmul operands, KV cache, conv state)
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_v;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_v;
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_v;
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 
 namespace lfm3 {
@@ -66,6 +68,28 @@ LFM3_DEV float warp_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// DPP lane moves: quad_perm [1,0,3,2] (0xb1), [2,3,0,1] (0x4e), row_half_mirror (0x141),
+// row_mirror (0x140).
+template <int CTRL> LFM3_DEV float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// Sum over each 16-lane row, returned in every lane of the row.
+LFM3_DEV float row16_sum(float v) {
+  v += dpp_mov<0xb1>(v);
+  v += dpp_mov<0x4e>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+LFM3_DEV float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Sum over the 64 lanes of a wave in a fixed order; the result is wave-uniform.
+LFM3_DEV float wave_sum(float v) {
+  const float s = row16_sum(v);
+  return ((readlane_f(s, 0) + readlane_f(s, 16)) + readlane_f(s, 32)) + readlane_f(s, 48);
 }
 
 // Block-wide sum for blockDim.x a multiple of 64 (<= 1024); `red` holds >= 16 floats of LDS.

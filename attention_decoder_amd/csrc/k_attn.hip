@@ -164,111 +164,229 @@ hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// decode: block (split, kv head, row); 256 keys per split, 4 query heads of one KV head; partials
-// (max, sum, o[128]) per (row, head, split) are merged by k_attn_merge.
+// decode: block (split of 64 keys, kv head, row). The prologue normalises and rotates the block's 4
+// query heads from the raw qkvg row; the block whose split holds the current position also forms
+// its key and value (per-head k RMSNorm + RoPE) and stores them in the cache. Scores: 16 lanes per
+// key row (8 dims each, coalesced), 4 keys per wave step; softmax per head over the split; P V
+// with one V row per wave step. Partials (max, sum, o) go to scratch; the last block of a (row,
+// kv head) to finish merges them, applies the sigmoid gate and stores fp16 -- one launch.
 // ---------------------------------------------------------------------------------------------
 
-constexpr int SPLIT = 256;
+constexpr int SPLIT = 64;
+constexpr int KVS = kHeadDim + 8;   // LDS row stride of the K and V tiles (elements)
 int attn_decode_split_keys() { return SPLIT; }
 
-__global__ void __launch_bounds__(256) k_attn_decode(AttnArgs a) {
+constexpr int kMaxMergeSplits = 512;   // 512 x 64 keys: contexts up to 32768
+
+template <bool PAGED>
+LFM3_DEV size_t kv_off(const KvRef& kv, int slot, int pos, int page, int kvh, int n_kv) {
+  if constexpr (PAGED) return (((size_t)page * n_kv + kvh) * kPageTokens + (pos % kPageTokens)) * kHeadDim;
+  else return (((size_t)slot * n_kv + kvh) * kv.ring + (pos % kv.ring)) * kHeadDim;
+}
+
+template <bool PAGED>
+__global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) f16_t kt[SPLIT * KVS];
+  __shared__ __attribute__((aligned(16))) f16_t vt[SPLIT * KVS];
   __shared__ float qs[kQPerKv][kHeadDim];
-  __shared__ float ps[kQPerKv][SPLIT];
-  __shared__ float stat[kQPerKv][2];
+  __shared__ float sc[kQPerKv][SPLIT];
+  __shared__ int is_last;
   const int split = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int slot = a.rows.slot[r], pos = a.rows.pos[r];
   const int nq = a.n_q_heads, nkv = a.n_kv_heads;
   const int k_lo = a.window > 0 ? max(0, pos - (a.window - 1)) : 0;
+  const int ns = (pos - k_lo) / SPLIT + 1;
+  if (split >= ns) return;
   const int j0 = k_lo + split * SPLIT;
-  float* part = a.part + (((size_t)r * nq + kvh * kQPerKv) * a.max_splits + split) * (kHeadDim + 2);
-  const size_t head_stride = (size_t)a.max_splits * (kHeadDim + 2);
-  if (j0 > pos) {
-    if (tid < kQPerKv) { part[tid * head_stride] = -__builtin_huge_valf(); part[tid * head_stride + 1] = 0.f; }
-    return;
+  const int nk = min(SPLIT, pos - j0 + 1);
+  const bool has_new = split == ns - 1;   // the current position is this split's last key
+  const int32_t* pt = PAGED ? a.kv.page_table + (size_t)slot * a.kv.max_pages : nullptr;
+
+  // 1. K/V tile loads, branch-free: thread t loads 16-byte chunks t + 256 q (q < 4) of the
+  //    64 key x 16 chunk tile for K and V; keys past the split load the split's last key (not
+  //    stored), the current position's row is replaced by the freshly formed key and value.
+  int jq[4], pg[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    jq[q] = j0 + min(((tid + 256 * q) >> 4), nk - 1);
+    pg[q] = PAGED ? pt[jq[q] / kPageTokens] : 0;
   }
-  const int j1 = min(pos, j0 + SPLIT - 1);
-  for (int i = tid; i < kQPerKv * kHeadDim; i += 256) {
-    const int hh = i / kHeadDim, d = i % kHeadDim;
-    qs[hh][d] = h2f(a.q[((size_t)r * nq + kvh * kQPerKv + hh) * kHeadDim + d]);
+  uint4 kr[4], vr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const size_t o = kv_off<PAGED>(a.kv, slot, jq[q], pg[q], kvh, nkv) + 8 * ((tid + 256 * q) & 15);
+    kr[q] = *(const uint4*)(a.kv.k + o);
+    vr[q] = *(const uint4*)(a.kv.v + o);
+  }
+  // 2. query heads 4 kvh + w (wave w), and the step's own key and value (per-head k RMSNorm +
+  //    RoPE, "LFM3-1.7B port": partial RoPE on the full layers); lane holds dims lane, lane + 64
+  const float* row = a.qkvg + (size_t)r * a.ld;
+  const float c = a.cos_t[(size_t)pos * kHalfDim + lane];
+  const float sn = a.sin_t[(size_t)pos * kHalfDim + lane];
+  {
+    const int h = kvh * kQPerKv + wave;
+    const float x0 = row[(size_t)h * kHeadDim + lane], x1 = row[(size_t)h * kHeadDim + lane + kHalfDim];
+    const float rr = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)kHeadDim + a.eps);
+    const float n0 = x0 * rr * bf2f(a.q_norm[lane]), n1 = x1 * rr * bf2f(a.q_norm[lane + kHalfDim]);
+    // q is rounded to fp16 as the prefill path stores it
+    qs[wave][lane] = h2f(f2h(n0 * c - n1 * sn));
+    qs[wave][lane + kHalfDim] = h2f(f2h(n1 * c + n0 * sn));
+  }
+  if (has_new && wave < 2) {
+    float o0, o1;
+    if (wave == 0) {
+      const float* kp = row + (size_t)(nq + kvh) * kHeadDim;
+      const float x0 = kp[lane], x1 = kp[lane + kHalfDim];
+      const float rr = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)kHeadDim + a.eps);
+      const float n0 = x0 * rr * bf2f(a.k_norm[lane]), n1 = x1 * rr * bf2f(a.k_norm[lane + kHalfDim]);
+      o0 = n0 * c - n1 * sn;
+      o1 = n1 * c + n0 * sn;
+    } else {
+      const float* vp = row + (size_t)(nq + nkv + kvh) * kHeadDim;
+      o0 = vp[lane];
+      o1 = vp[lane + kHalfDim];
+    }
+    const int page = PAGED ? pt[pos / kPageTokens] : 0;
+    f16_t* dst = (wave == 0 ? a.kv.k : a.kv.v) + kv_off<PAGED>(a.kv, slot, pos, page, kvh, nkv);
+    const f16_t h0 = f2h(o0), h1 = f2h(o1);
+    dst[lane] = h0;
+    dst[lane + kHalfDim] = h1;
+    f16_t* t = (wave == 0 ? kt : vt) + (nk - 1) * KVS;
+    t[lane] = h0;
+    t[lane + kHalfDim] = h1;
+  }
+  // 3. tiles to LDS (the current position's row came from step 2)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + 256 * q, key = idx >> 4, c8 = idx & 15;
+    if (key < nk && j0 + key != pos) {
+      *(uint4*)(kt + key * KVS + 8 * c8) = kr[q];
+      *(uint4*)(vt + key * KVS + 8 * c8) = vr[q];
+    }
   }
   __syncthreads();
-  const int j = j0 + tid;
-  float sc[kQPerKv] = {0.f, 0.f, 0.f, 0.f};
-  if (j <= j1) {
-    const uint4* kr = (const uint4*)kv_src(a.kv, a.kv.k, slot, j, kvh, nkv);
-#pragma unroll 4
-    for (int c = 0; c < kHeadDim / 8; ++c) {
-      const uint4 v = kr[c];
-      const f16_t* e = (const f16_t*)&v;
+  // 4. scores: thread -> key t / 4, dims [32 (t % 4), + 32) for the 4 heads; sum over 4 lanes
+  const float scale = 0.08838834764831845f;
+  {
+    const int key = tid >> 2, qd = tid & 3;
+    float d[kQPerKv] = {0.f, 0.f, 0.f, 0.f};
+    const f16_t* kp = kt + key * KVS + 32 * qd;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float kf = h2f(e[t]);
+    for (int e8 = 0; e8 < 4; ++e8) {
+      const uint4 v = *(const uint4*)(kp + 8 * e8);
+      const f16_t* e16 = (const f16_t*)&v;
 #pragma unroll
-        for (int hh = 0; hh < kQPerKv; ++hh) sc[hh] = fmaf(qs[hh][8 * c + t], kf, sc[hh]);
+      for (int e = 0; e < 8; ++e) {
+        const float kf = h2f(e16[e]);
+#pragma unroll
+        for (int hh = 0; hh < kQPerKv; ++hh) d[hh] = fmaf(qs[hh][32 * qd + 8 * e8 + e], kf, d[hh]);
       }
     }
-  }
-  const float scale = 0.08838834764831845f;
 #pragma unroll
-  for (int hh = 0; hh < kQPerKv; ++hh) ps[hh][tid] = j <= j1 ? sc[hh] * scale : -__builtin_huge_valf();
-  __syncthreads();
-  {
-    // wave w: softmax statistics of head w over this split
-    float mx = -__builtin_huge_valf();
-    for (int i = lane; i < SPLIT; i += 64) mx = fmaxf(mx, ps[wave][i]);
-    mx = warp_max(mx);
-    float sum = 0.f;
-    for (int i = lane; i < SPLIT; i += 64) {
-      const float p = ps[wave][i] == -__builtin_huge_valf() ? 0.f : __expf(ps[wave][i] - mx);
-      ps[wave][i] = p;
-      sum += p;
+    for (int hh = 0; hh < kQPerKv; ++hh) {
+      d[hh] += dpp_mov<0xb1>(d[hh]);
+      d[hh] += dpp_mov<0x4e>(d[hh]);
     }
-    sum = warp_sum(sum);
-    if (lane == 0) { stat[wave][0] = mx; stat[wave][1] = sum; }
+    if (qd == 0)
+#pragma unroll
+      for (int hh = 0; hh < kQPerKv; ++hh) sc[hh][key] = key < nk ? d[hh] * scale : -__builtin_huge_valf();
   }
   __syncthreads();
-  {
-    // thread: head wave, dims 2*lane, 2*lane + 1
-    float o0 = 0.f, o1 = 0.f;
-    for (int jj = j0; jj <= j1; ++jj) {
-      const uint32_t vv = *(const uint32_t*)(kv_src(a.kv, a.kv.v, slot, jj, kvh, nkv) + 2 * lane);
-      const float p = ps[wave][jj - j0];
-      o0 = fmaf(p, h2f((f16_t)(vv & 0xffffu)), o0);
-      o1 = fmaf(p, h2f((f16_t)(vv >> 16)), o1);
+  // 5. wave w = head 4 kvh + w: softmax over the split (lane = key), then P V over the tile with
+  //    lane holding dims 2 lane, 2 lane + 1
+  const float v_ = sc[wave][lane];
+  const float mx = warp_max(v_);
+  const float p = v_ == -__builtin_huge_valf() ? 0.f : __expf(v_ - mx);
+  const float l = wave_sum(p);
+  sc[wave][lane] = p;
+  __syncthreads();
+  float o0 = 0.f, o1 = 0.f;
+  for (int kk = 0; kk < nk; ++kk) {
+    const float pk = sc[wave][kk];
+    const uint32_t vv = *(const uint32_t*)(vt + kk * KVS + 2 * lane);
+    o0 = fmaf(pk, h2f((f16_t)(vv & 0xffffu)), o0);
+    o1 = fmaf(pk, h2f((f16_t)(vv >> 16)), o1);
+  }
+  const int h = kvh * kQPerKv + wave;
+  const int d0 = 2 * lane;
+  const float gate = sigmoidf_(row[a.gate_col + h]);
+  f16_t* out = a.out + (size_t)r * nq * kHeadDim + (size_t)h * kHeadDim;
+  if (ns == 1) {
+    const float inv = gate / l;
+    out[d0] = f2h(o0 * inv);
+    out[d0 + 1] = f2h(o1 * inv);
+    return;
+  }
+  // 6. partials; the last block of this (row, kv head) merges them
+  constexpr int PS = kHeadDim + 2;
+  float* part = a.part + (((size_t)r * nq + h) * a.max_splits + split) * PS;
+  if (lane == 0) { part[0] = mx; part[1] = l; }
+  part[2 + d0] = o0;
+  part[2 + d0 + 1] = o1;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    int* cnt = a.counters + (size_t)r * nkv + kvh;
+    const int old = atomicAdd(cnt, 1);
+    is_last = old == ns - 1;
+    if (is_last) *cnt = 0;   // ready for the next launch
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  // merge, wave = head: split statistics spread over lanes (branch-free clamped loads), the
+  // weights go through LDS (reusing the score buffer area), then the o sums over splits
+  float* wbuf = reinterpret_cast<float*>(kt) + wave * kMaxMergeSplits;   // 4 x 512 floats fit in kt
+  const float* ph = a.part + ((size_t)r * nq + h) * a.max_splits * PS;
+  float gmx = -__builtin_huge_valf();
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s2 = min(s0 + lane, ns - 1);
+    gmx = fmaxf(gmx, ph[(size_t)s2 * PS]);
+  }
+  gmx = warp_max(gmx);
+  float lt = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s2 = min(s0 + lane, ns - 1);
+    const float pm = ph[(size_t)s2 * PS];
+    const float pl = ph[(size_t)s2 * PS + 1];
+    const float w = (s0 + lane < ns && pm != -__builtin_huge_valf()) ? __expf(pm - gmx) : 0.f;
+    if (s0 + lane < ns) wbuf[s0 + lane] = w;
+    lt += w * pl;
+  }
+  lt = wave_sum(lt);
+  __syncthreads();
+  float a0 = 0.f, a1 = 0.f;
+  int s2 = 0;
+  for (; s2 + 8 <= ns; s2 += 8) {
+    float2 ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ov[u] = *(const float2*)(ph + (size_t)(s2 + u) * PS + 2 + d0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = wbuf[s2 + u];
+      a0 = fmaf(w, ov[u].x, a0);
+      a1 = fmaf(w, ov[u].y, a1);
     }
-    float* dst = part + (size_t)wave * head_stride;
-    if (lane == 0) { dst[0] = stat[wave][0]; dst[1] = stat[wave][1]; }
-    dst[2 + 2 * lane] = o0;
-    dst[3 + 2 * lane] = o1;
   }
+  for (; s2 < ns; ++s2) {
+    const float2 ov = *(const float2*)(ph + (size_t)s2 * PS + 2 + d0);
+    const float w = wbuf[s2];
+    a0 = fmaf(w, ov.x, a0);
+    a1 = fmaf(w, ov.y, a1);
+  }
+  const float inv = lt > 0.f ? gate / lt : 0.f;
+  out[d0] = f2h(a0 * inv);
+  out[d0 + 1] = f2h(a1 * inv);
 }
 
-__global__ void __launch_bounds__(128) k_attn_merge(AttnArgs a) {
-  const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  const int pos = a.rows.pos[r];
-  const int k_lo = a.window > 0 ? max(0, pos - (a.window - 1)) : 0;
-  const int ns = (pos - k_lo) / SPLIT + 1;
-  const float* part = a.part + ((size_t)r * a.n_q_heads + h) * a.max_splits * (kHeadDim + 2);
-  float mx = -__builtin_huge_valf();
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part[(size_t)s * (kHeadDim + 2)]);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* p = part + (size_t)s * (kHeadDim + 2);
-    const float w = p[0] == -__builtin_huge_valf() ? 0.f : __expf(p[0] - mx);
-    l = fmaf(w, p[1], l);
-    o = fmaf(w, p[2 + d], o);
-  }
-  const float gate = sigmoidf_(a.gate[(size_t)r * a.ldg + h]);
-  a.out[(size_t)r * a.n_q_heads * kHeadDim + (size_t)h * kHeadDim + d] = f2h(l > 0.f ? o / l * gate : 0.f);
-}
-
-hipError_t launch_attn_decode(hipStream_t s, const AttnArgs& a) {
+hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a) {
   if (a.rows.n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_attn_decode, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(a.rows.n, a.n_q_heads), dim3(kHeadDim), 0, s, a);
+  if (a.max_splits > kMaxMergeSplits) return hipErrorInvalidValue;
+  if (a.kv.ring == 0)
+    hipLaunchKernelGGL(k_attn_decode<true>, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_attn_decode<false>, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -89,40 +89,47 @@ hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int ro
 // ---------------------------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
+  // the arithmetic (per-thread k = tid + 256 i, explicit fma order, 4-wave sum in wave order) is
+  // the same as the decode GEMV's norm prologue, so fused and unfused steps agree bitwise
   __shared__ float red[16];
   const int r = blockIdx.x;
   const int H = a.hidden;
   const size_t base = (size_t)r * H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int kPer = 16;
   float hv[kPer];
-  const int per = H / blockDim.x;
+  const int per = H / 256;
   if (a.m) {
     float mv[kPer];
     float ss = 0.f;
     for (int i = 0; i < per; ++i) {
-      const int k = threadIdx.x + i * blockDim.x;
-      mv[i] = a.m[base + k];
-      ss += mv[i] * mv[i];
+      mv[i] = a.m[base + tid + 256 * i];
+      ss = fmaf(mv[i], mv[i], ss);
     }
-    ss = block_sum(ss, red);
-    const float rm = rsqrtf(ss / (float)H + a.eps);
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    const float rm = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + a.eps);
     for (int i = 0; i < per; ++i) {
-      const int k = threadIdx.x + i * blockDim.x;
-      hv[i] = a.h_in[base + k] + mv[i] * rm * bf2f(a.w_post[k]);
+      const int k = tid + 256 * i;
+      hv[i] = fmaf(mv[i] * rm, bf2f(a.w_post[k]), a.h_in[base + k]);
     }
+    __syncthreads();
   } else {
-    for (int i = 0; i < per; ++i) hv[i] = a.h_in[base + threadIdx.x + i * blockDim.x];
+    for (int i = 0; i < per; ++i) hv[i] = a.h_in[base + tid + 256 * i];
   }
   float ss = 0.f;
-  for (int i = 0; i < per; ++i) ss += hv[i] * hv[i];
-  ss = block_sum(ss, red);
-  const float rh = rsqrtf(ss / (float)H + a.eps);
+  for (int i = 0; i < per; ++i) ss = fmaf(hv[i], hv[i], ss);
+  ss = wave_sum(ss);
+  if (lane == 0) red[4 + wave] = ss;
+  __syncthreads();
+  const float rh = rsqrtf((red[4] + red[5] + red[6] + red[7]) / (float)H + a.eps);
   for (int i = 0; i < per; ++i) {
-    const int k = threadIdx.x + i * blockDim.x;
+    const int k = tid + 256 * i;
     if (a.m) a.h_out[base + k] = hv[i];
     if (a.capture) a.capture[base + k] = hv[i];
-    const float xv = hv[i] * rh * bf2f(a.w_pre[k]);
-    a.x_out[base + k] = f2h(xv);
+    const float xv = (hv[i] * rh) * bf2f(a.w_pre[k]);
+    a.x_out[base + k] = f2h_sep(xv);
     if (a.x_copy) a.x_copy[base + k] = xv;
   }
 }
@@ -161,7 +168,7 @@ __global__ void __launch_bounds__(256) k_qk_rope(QkRopeArgs a) {
     const bool is_q = h < nq;
     const float* hp = src + (size_t)h * kHeadDim;  // k heads follow q heads contiguously
     const float x0 = hp[l], x1 = hp[l + kHalfDim];
-    const float ss = warp_sum(x0 * x0 + x1 * x1);
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
     const float rr = rsqrtf(ss / (float)kHeadDim + a.eps);
     const bf16_t* nw = is_q ? a.q_norm : a.k_norm;
     const float n0 = x0 * rr * bf2f(nw[l]);
@@ -210,7 +217,7 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   for (int j = 0; j < T; ++j) ker[j] = bf2f(a.kernel[(size_t)c * T + j]);
   auto zrow = [&](int r) -> float {
     const float* p = a.bcx + (size_t)r * a.ld;
-    return h2f(f2h(p[c] * p[2 * H + c]));
+    return h2f(f2h_sep(p[c] * p[2 * H + c]));
   };
   auto crow = [&](int r) -> float { return a.bcx[(size_t)r * a.ld + H + c]; };
   float win[kMaxTaps];
@@ -221,7 +228,7 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
     const float z = zrow(r);
     float y = ker[S] * z;
     for (int j = 0; j < S; ++j) y = fmaf(ker[j], win[j], y);
-    a.out[(size_t)r * H + c] = f2h(crow(r) * y);
+    a.out[(size_t)r * H + c] = f2h_sep(crow(r) * y);
     for (int j = 0; j + 1 < S; ++j) st[(size_t)j * H + c] = f2h(win[j + 1]);
     st[(size_t)(S - 1) * H + c] = f2h(z);
     return;
@@ -238,7 +245,7 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
     const float z = zrow(r);
     float y = ker[S] * z;
     for (int j = 0; j < S; ++j) y = fmaf(ker[j], win[j], y);
-    a.out[(size_t)r * H + c] = f2h(crow(r) * y);
+    a.out[(size_t)r * H + c] = f2h_sep(crow(r) * y);
     for (int j = 0; j + 1 < S; ++j) win[j] = win[j + 1];
     win[S - 1] = z;
   }

@@ -80,10 +80,14 @@ hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int ro
 
 // ---- k_gemv.hip --------------------------------------------------------------------------------
 
-enum GemvEpi { GEMV_STORE = 0, GEMV_SWIGLU = 1, GEMV_LOGITS = 2 };
+enum GemvEpi { GEMV_STORE = 0, GEMV_SWIGLU = 1, GEMV_LOGITS = 2, GEMV_CONV = 3 };
 // y[b, n] = sum_k x[b, k] * (q[n, k] * s + bias) for b < batch (<= 8), exact weights (the per-group
 // factored form). STORE: fp32 yf [batch, ldy]. SWIGLU: rows n and n + N/2 -> fp16 silu(a) * b in
-// y. LOGITS: fp32 logits (nullable) + per-row argmax keys (atomicMax).
+// y. LOGITS: fp32 logits (nullable) + per-row argmax keys (atomicMax). CONV (in_proj, N = 3H): the
+// gated short conv of each channel with its kept state, fp16 out in y [batch, ldy].
+// Input: x fp16 [batch, ldx], or (h_src set) the decode norm prologue:
+//   h_new = h_src + (m ? rmsnorm(m) * w_post : 0), x = f16(rmsnorm(h_new) * w_pre),
+// with block 0 writing h_new to h_dst (when m is set), capture rows and the fp32 x copy.
 struct GemvArgs {
   QLinear w;
   const f16_t* x;   // [batch, ldx]
@@ -96,6 +100,23 @@ struct GemvArgs {
   float* logits;
   int ld_logits;
   uint64_t* keys;
+  // norm prologue (rows of length K, contiguous)
+  const float* h_src;
+  const float* m;
+  const bf16_t* w_post;
+  const bf16_t* w_pre;
+  float eps;
+  float* h_dst;
+  float* capture;
+  int capture_ld;
+  float* x_copy;
+  // conv epilogue
+  const bf16_t* conv_kernel;  // [H, taps]
+  f16_t* conv_state;          // this layer's state of slot 0; slot stride below
+  int64_t conv_slot_stride;
+  int conv_taps;
+  int32_t conv_slot[kMaxBatch];
+  int max_blocks;             // grid cap (0: default)
 };
 hipError_t launch_gemv(hipStream_t s, const GemvArgs& a);
 
@@ -133,7 +154,29 @@ struct AttnArgs {
   int max_splits;
 };
 hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a);
-hipError_t launch_attn_decode(hipStream_t s, const AttnArgs& a);
+
+// Decode attention for one row per slot, fused with the q/k norm + RoPE of the step's own query
+// and key and the store of its key and value; split-K over 64-key splits with the merge done by
+// the last block of each (row, kv head) (counters start at zero and are left at zero).
+struct AttnDecodeArgs {
+  const float* qkvg;   // raw fp32 linear output [rows, ld]: q | k | v | g
+  int ld;
+  int gate_col;        // column of g_0
+  const bf16_t* q_norm;
+  const bf16_t* k_norm;
+  const float* cos_t;
+  const float* sin_t;
+  KvRef kv;
+  Rows rows;
+  int window;          // 0 = full causal
+  int n_q_heads, n_kv_heads;
+  float eps;
+  f16_t* out;          // [rows, n_q_heads * 128]
+  float* part;         // [rows, n_q_heads, max_splits, 130]
+  int* counters;       // [rows, n_kv_heads]
+  int max_splits;      // grid extent: the most splits any row needs
+};
+hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a);
 int attn_decode_split_keys();
 
 }  // namespace lfm3

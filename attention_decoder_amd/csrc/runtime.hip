@@ -138,7 +138,7 @@ bool check_config(const lfm3_config& c, std::string& err) {
   for (int i = 0; i < c.n_layers; ++i)
     if (c.layer_type[i] > LFM3_LAYER_SLIDING) return bad("layer %d has unknown type %d", i, c.layer_type[i]);
   if (c.max_slots < 1) return bad("max_slots %d", c.max_slots);
-  if (c.max_ctx < 1) return bad("max_ctx %d", c.max_ctx);
+  if (c.max_ctx < 1 || c.max_ctx > 32768) return bad("max_ctx %d outside [1, 32768]", c.max_ctx);
   if (c.page_tokens != kPageTokens) return bad("page_tokens %d: this build runs 16", c.page_tokens);
   if (c.max_chunk < 1) return bad("max_chunk %d", c.max_chunk);
   if (c.n_pages < 0) return bad("n_pages %d", c.n_pages);
@@ -152,7 +152,7 @@ bool check_config(const lfm3_config& c, std::string& err) {
 struct Layout {
   size_t cos_f, sin_f, cos_s, sin_s;
   size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
-  size_t h, x, big, sbuf, mix, qrot, m, xf, part, keys;
+  size_t h, h2, x, big, sbuf, mix, qrot, m, xf, part, keys, counters;
   size_t total;
   int max_rows, max_pages, ring_rows, max_splits, big_ld;
   size_t ring_layer, pool_layer, conv_slot;
@@ -188,6 +188,7 @@ Layout make_layout(const lfm3_config& c) {
   L.page_table = take((size_t)c.max_slots * L.max_pages * 4);
   const size_t R = L.max_rows;
   L.h = take(R * H * 4);
+  L.h2 = take(R * H * 4);
   L.x = take(R * H * 2);
   L.big = take(R * L.big_ld * 4);
   L.sbuf = take(R * F * 2);
@@ -197,6 +198,7 @@ Layout make_layout(const lfm3_config& c) {
   L.xf = take(R * H * 2);
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * (kHeadDim + 2) * 4);
   L.keys = take((size_t)std::max(kMaxBatch, (int)R) * 8);
+  L.counters = take((size_t)c.max_slots * c.n_kv_heads * 4);
   L.total = off;
   return L;
 }
@@ -343,9 +345,8 @@ KvRef kv_for(lfm3_ctx* ctx, const LayerW& lw) {
   return kv;
 }
 
-// One pass of the layer stack over `rows` rows whose hidden input is already in h.
-// decode = one row per slot (GEMV path), else a prefill chunk of one slot (GEMM path).
-lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture_row0, float* hidden_out) {
+// One prefill pass (a chunk of one slot's rows, GEMM path) whose hidden input is already in h.
+lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float* hidden_out) {
   const lfm3_config& c = ctx->cfg;
   const Layout& L = ctx->L;
   hipStream_t s = ctx->stream;
@@ -365,12 +366,6 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
     const double out_bytes = epi == GEMM_SWIGLU ? (double)M * (w.n / 2) * 2.0 : (double)M * w.n * 4.0;
     const double bytes = lin_bytes(w) + (double)M * w.k * 2.0 + out_bytes;
     const double flops = 2.0 * M * (double)w.n * w.k;
-    if (decode) {
-      GemvArgs g{};
-      g.w = w; g.x = in; g.ldx = ldin; g.batch = M; g.y = outb; g.yf = outf; g.ldy = ldout;
-      g.epi = epi == GEMM_SWIGLU ? GEMV_SWIGLU : GEMV_STORE;
-      return timed(ctx, LFM3_PROF_GEMV, bytes, flops, [&] { return launch_gemv(s, g); });
-    }
     GemmArgs g{};
     g.w = w; g.x = in; g.ldx = ldin; g.m = M; g.epi = epi; g.y = outb; g.yf = outf; g.ldy = ldout;
     return timed(ctx, LFM3_PROF_GEMM, bytes, flops, [&] { return launch_gemm(s, g); });
@@ -397,7 +392,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
       ca.state = ctx->at<f16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
       ca.slot_stride = (int64_t)L.conv_slot;
       ca.out = mix; ca.rows = rows; ca.hidden = H; ca.taps = c.conv_taps;
-      LFM3_TRY(timed(ctx, LFM3_PROF_CONV, (double)M * H * (12 + 2) + (decode ? (double)M * H * 2 * 2 * (c.conv_taps - 1) : 2.0 * H * 2 * (c.conv_taps - 1)), 0,
+      LFM3_TRY(timed(ctx, LFM3_PROF_CONV, (double)M * H * (12 + 2) + 2.0 * H * 2 * (c.conv_taps - 1), 0,
                      [&] { return launch_conv(s, ca); }));
     } else {
       LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE));
@@ -416,20 +411,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
       aa.window = full ? 0 : c.window;
       aa.n_q_heads = c.n_q_heads; aa.n_kv_heads = c.n_kv_heads; aa.out = mix;
       aa.part = ctx->at<float>(L.part);
-      if (decode) {
-        int ms = 1;
-        for (int r = 0; r < M; ++r) {
-          const int lo = full ? 0 : std::max(0, rows.pos[r] - (c.window - 1));
-          ms = std::max(ms, (rows.pos[r] - lo) / attn_decode_split_keys() + 1);
-        }
-        aa.max_splits = ms;
-        double kv_bytes = 0;
-        for (int r = 0; r < M; ++r) {
-          const int lo = full ? 0 : std::max(0, rows.pos[r] - (c.window - 1));
-          kv_bytes += (double)(rows.pos[r] - lo + 1) * c.n_kv_heads * kHeadDim * 2 * 2;
-        }
-        LFM3_TRY(timed(ctx, LFM3_PROF_ATTN_DECODE, kv_bytes, 0, [&] { return launch_attn_decode(s, aa); }));
-      } else {
+      {
         double fl = 0;
         for (int r = 0; r < M; ++r) {
           const double p = rows.pos0 + r;
@@ -454,6 +436,124 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, bool decode, int capture
   nf.capture = cap(c.n_layers - 1);
   nf.x_copy = hidden_out;
   LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, nf); }));
+  return LFM3_OK;
+}
+
+// One decode step: one row per slot, h input already in the first residual buffer. GEMVs take
+// their RMSNorm'd input through the fused prologue for batches of at most 2 rows (each block
+// recomputes the norm from L2-resident rows); larger batches run the norm once and feed plain
+// GEMVs. Both use the same arithmetic. Ends with the tied head and the argmax when asked.
+lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float* logits, int32_t* ids) {
+  const lfm3_config& c = ctx->cfg;
+  const Layout& L = ctx->L;
+  hipStream_t s = ctx->stream;
+  const int M = rows.n;
+  const int H = c.hidden;
+  float* cur = ctx->at<float>(L.h);
+  float* oth = ctx->at<float>(L.h2);
+  f16_t* x = ctx->at<f16_t>(L.x);
+  float* big = ctx->at<float>(L.big);
+  f16_t* sb = ctx->at<f16_t>(L.sbuf);
+  f16_t* mix = ctx->at<f16_t>(L.mix);
+  float* m = ctx->at<float>(L.m);
+  f16_t* xf = ctx->at<f16_t>(L.xf);
+  const bool fuse = M <= 2;
+  auto cap = [&](int layer) -> float* {
+    if (!ctx->capture || layer < 0) return nullptr;
+    return ctx->capture + (size_t)layer * ctx->capture_rows * H;
+  };
+  auto gemv_bytes = [&](const QLinear& w, double out_bytes) { return lin_bytes(w) + (double)M * w.k * 2.0 + out_bytes; };
+  auto gemv = [&](GemvArgs& g, double out_bytes) -> hipError_t {
+    return timed(ctx, LFM3_PROF_GEMV, gemv_bytes(g.w, out_bytes), 2.0 * M * (double)g.w.n * g.w.k,
+                 [&] { return launch_gemv(s, g); });
+  };
+  // GEMV whose input is rmsnorm(cur [+ rmsnorm(m) * w_post]) * w_pre
+  auto normed_gemv = [&](GemvArgs& g, const bf16_t* w_post, const bf16_t* w_pre, float* capture, float* x_copy,
+                         double out_bytes) -> hipError_t {
+    g.batch = M;
+    if (fuse) {
+      g.h_src = cur; g.m = w_post ? m : nullptr; g.w_post = w_post; g.w_pre = w_pre; g.eps = c.norm_eps;
+      g.h_dst = oth; g.capture = capture; g.capture_ld = H; g.x_copy = x_copy;
+      hipError_t e = gemv(g, out_bytes);
+      if (w_post) std::swap(cur, oth);
+      return e;
+    }
+    NormArgs na{};
+    na.h_in = cur; na.h_out = cur; na.m = w_post ? m : nullptr; na.w_post = w_post; na.w_pre = w_pre;
+    na.x_out = x; na.capture = capture; na.x_copy = x_copy; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
+    hipError_t e = timed(ctx, LFM3_PROF_NORM, (double)M * H * 14, 0, [&] { return launch_resid_norm(s, na); });
+    if (e != hipSuccess) return e;
+    g.x = x; g.ldx = H;
+    return gemv(g, out_bytes);
+  };
+
+  for (int i = 0; i < c.n_layers; ++i) {
+    const LayerW& lw = ctx->layers[i];
+    const bf16_t* w_post = i > 0 ? ctx->layers[i - 1].post_ffn : nullptr;
+    if (lw.type == LFM3_LAYER_CONV) {
+      GemvArgs g{};
+      g.w = lw.mix_in; g.epi = GEMV_CONV; g.y = mix; g.ldy = H;
+      g.conv_kernel = lw.conv_kernel;
+      g.conv_state = ctx->at<f16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
+      g.conv_slot_stride = (int64_t)L.conv_slot;
+      g.conv_taps = c.conv_taps;
+      for (int b = 0; b < M; ++b) g.conv_slot[b] = rows.slot[b];
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * H * (2 + 4 * (c.conv_taps - 1))));
+    } else {
+      GemvArgs g{};
+      g.w = lw.mix_in; g.epi = GEMV_STORE; g.yf = big; g.ldy = L.big_ld;
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4));
+      const bool full = lw.type == LFM3_LAYER_FULL;
+      AttnDecodeArgs aa{};
+      aa.qkvg = big; aa.ld = L.big_ld; aa.gate_col = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
+      aa.q_norm = lw.q_norm; aa.k_norm = lw.k_norm;
+      aa.cos_t = ctx->at<float>(full ? L.cos_f : L.cos_s);
+      aa.sin_t = ctx->at<float>(full ? L.sin_f : L.sin_s);
+      aa.kv = kv_for(ctx, lw); aa.rows = rows;
+      aa.window = full ? 0 : c.window;
+      aa.n_q_heads = c.n_q_heads; aa.n_kv_heads = c.n_kv_heads; aa.eps = c.norm_eps;
+      aa.out = mix; aa.part = ctx->at<float>(L.part); aa.counters = ctx->at<int>(L.counters);
+      int ms = 1;
+      double kv_bytes = 0;
+      for (int r = 0; r < M; ++r) {
+        const int lo = full ? 0 : std::max(0, rows.pos[r] - (c.window - 1));
+        ms = std::max(ms, (rows.pos[r] - lo) / attn_decode_split_keys() + 1);
+        kv_bytes += (double)(rows.pos[r] - lo + 1) * c.n_kv_heads * kHeadDim * 2 * 2;
+      }
+      aa.max_splits = ms;
+      LFM3_TRY(timed(ctx, LFM3_PROF_ATTN_DECODE, kv_bytes, 0, [&] { return launch_attn_decode(s, aa); }));
+    }
+    {
+      GemvArgs g{};
+      g.w = lw.mix_out; g.x = mix; g.ldx = H; g.batch = M; g.epi = GEMV_STORE; g.yf = m; g.ldy = H;
+      LFM3_TRY(gemv(g, (double)M * H * 4));
+    }
+    {
+      GemvArgs g{};
+      g.w = lw.w13; g.epi = GEMV_SWIGLU; g.y = sb; g.ldy = c.ffn;
+      LFM3_TRY(normed_gemv(g, lw.post_op, lw.ffn_norm, nullptr, nullptr, (double)M * c.ffn * 2));
+    }
+    {
+      GemvArgs g{};
+      g.w = lw.w2; g.x = sb; g.ldx = c.ffn; g.batch = M; g.epi = GEMV_STORE; g.yf = m; g.ldy = H;
+      LFM3_TRY(gemv(g, (double)M * H * 4));
+    }
+  }
+  const bf16_t* last_post = ctx->layers[c.n_layers - 1].post_ffn;
+  if (c.has_embedding && (logits || ids)) {
+    GemvArgs g{};
+    g.w = ctx->emb; g.epi = GEMV_LOGITS; g.logits = logits; g.ld_logits = c.vocab;
+    g.keys = ctx->at<uint64_t>(L.keys);
+    LFM3_TRY(normed_gemv(g, last_post, ctx->emb_norm, cap(c.n_layers - 1), hidden_out, logits ? (double)M * c.vocab * 4 : 0.0));
+    LFM3_TRY(launch_argmax_finalize(s, g.keys, ids, M));
+  } else {
+    NormArgs nf{};
+    nf.h_in = cur; nf.h_out = cur; nf.x_out = xf; nf.rows = M; nf.hidden = H; nf.eps = c.norm_eps;
+    nf.m = m; nf.w_post = last_post; nf.w_pre = ctx->emb_norm;
+    nf.capture = cap(c.n_layers - 1);
+    nf.x_copy = hidden_out;
+    LFM3_TRY(timed(ctx, LFM3_PROF_NORM, (double)M * H * 14, 0, [&] { return launch_resid_norm(s, nf); }));
+  }
   return LFM3_OK;
 }
 
@@ -621,7 +721,8 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
   // zero the conv states, page table and argmax keys
   if (launch_zero(ctx->stream, ctx->at<void>(L.conv_state), (size_t)c.max_slots * L.conv_slot * 2) != hipSuccess ||
       launch_zero(ctx->stream, ctx->at<void>(L.page_table), (size_t)c.max_slots * L.max_pages * 4) != hipSuccess ||
-      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)std::max(kMaxBatch, L.max_rows) * 8) != hipSuccess) {
+      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)std::max(kMaxBatch, L.max_rows) * 8) != hipSuccess ||
+      launch_zero(ctx->stream, ctx->at<void>(L.counters), (size_t)c.max_slots * c.n_kv_heads * 4) != hipSuccess) {
     delete ctx;
     g_err = "workspace clear failed";
     return LFM3_ERR_DEVICE;
@@ -660,7 +761,7 @@ lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
     } else {
       LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev + (size_t)r0 * H, M, H, h));
     }
-    st = run_layers(ctx, rows, false, r0, hidden_out_dev ? hidden_out_dev + (size_t)r0 * H : nullptr);
+    st = run_layers(ctx, rows, r0, hidden_out_dev ? hidden_out_dev + (size_t)r0 * H : nullptr);
     if (st != LFM3_OK) return st;
     ctx->len[slot] += M;
     if (r0 + M == n_rows) {
@@ -706,10 +807,10 @@ lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_hos
   } else {
     LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev, n, c.hidden, h));
   }
-  lfm3_status st = run_layers(ctx, rows, true, 0, hidden_out_dev);
+  lfm3_status st = run_decode(ctx, rows, hidden_out_dev, logits_dev, argmax_dev);
   if (st != LFM3_OK) return st;
   for (int b = 0; b < n; ++b) ctx->len[slots_host[b]] += 1;
-  return head(ctx, ctx->at<f16_t>(ctx->L.xf), n, logits_dev, argmax_dev);
+  return LFM3_OK;
 }
 
 lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot) {

@@ -10,7 +10,7 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblfm3.so")
+LIB_PATH = os.environ.get("LFM3_LIBRARY", os.path.join(HERE, "liblfm3.so"))
 HEADER = os.path.join(os.path.dirname(HERE), "include", "lfm3.h")
 
 STATUS = {0: "LFM3_OK", 1: "LFM3_ERR_ARG", 2: "LFM3_ERR_CONFIG", 3: "LFM3_ERR_BLOB", 4: "LFM3_ERR_SLOT",
