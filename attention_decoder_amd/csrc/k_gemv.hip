@@ -12,6 +12,7 @@
 // 6-bit codes) and the chunk's scale/bias; x is staged once per block in LDS in the pair order the
 // unpacked codes come in, with per-chunk sums of x.
 #include "kernels.h"
+#include "norm_vec.h"
 
 namespace lfm3 {
 
@@ -71,7 +72,8 @@ LFM3_DEV float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // Rows handled together by one wave: 8 for STORE / LOGITS, 4 gate + the 4 matching up rows for
-// SWIGLU, B, C and x rows of 2 channels (6) for the conv epilogue.
+// SWIGLU, B, C and x rows of 2 channels (6, reduced as 8 with two zero rows) for the conv epilogue.
+constexpr int kRG = 8;
 template <int EPI> struct RowsPerGroup { static constexpr int v = EPI == GEMV_CONV ? 6 : 8; };
 
 template <int EPI> LFM3_HOST_DEV int n_groups_of(int N) {
@@ -95,130 +97,186 @@ template <int EPI> LFM3_DEV void rows_of(int g, int N, int (&rows)[RowsPerGroup<
   }
 }
 
-// Stage the fp16 input rows in LDS in chunk pair order, with per-chunk sums of the staged values.
-// Either x comes from global fp16 rows (PRO = 0), or (PRO = 1) the decode norm prologue forms it:
-// h_new = h_src + rmsnorm(m) * w_post (or h_src), x = f16(rmsnorm(h_new) * w_pre); block 0 also
-// stores h_new, the capture rows and the fp32 x. The arithmetic matches k_resid_norm exactly.
-constexpr int kP = 16;  // prologue elements per thread: K = hidden <= 4096
+// Sum of 8 per-lane values over the wave, transposed: lanes 8r .. 8r+7 end with the total of
+// value r. Cross-half and cross-row exchanges use the gfx950 permlane swaps, the rest DPP; every
+// lane evaluates the same addition tree (up to operand order), so the 8 copies are identical and
+// the result does not depend on anything but the values.
+LFM3_DEV float bfly8(const float (&in)[8]) {
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(in[i]), __float_as_uint(in[i + 4]), false, false);
+    v[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  float w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 2]), false, false);
+    w[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  const bool hi = (threadIdx.x & 8) != 0;
+  const float keep = hi ? w[1] : w[0], send = hi ? w[0] : w[1];
+  float t = keep + dpp_mov<0x140>(send);  // row_mirror: lane i <-> 15 - i
+  t += dpp_mov<0xb1>(t);
+  t += dpp_mov<0x4e>(t);
+  t += dpp_mov<0x141>(t);                 // row_half_mirror: lane i <-> 7 - i
+  return t;
+}
 
+// Stage the fp16 input rows in LDS in chunk pair order with per-chunk sums of the staged values.
+// Vector block v (8 consecutive k) lands at fp16 offset 8v, permuted into the order in which the
+// unpacked codes pair up.
+template <int BITS> LFM3_DEV uint4 pair_order8(const uint32_t (&h)[4]) {
+  // h: 8 fp16 in natural order, two per word
+  if constexpr (BITS == 4) {
+    // (x0, x4), (x1, x5), (x2, x6), (x3, x7)
+    return make_uint4(__builtin_amdgcn_perm(h[2], h[0], 0x05040100u), __builtin_amdgcn_perm(h[2], h[0], 0x07060302u),
+                      __builtin_amdgcn_perm(h[3], h[1], 0x05040100u), __builtin_amdgcn_perm(h[3], h[1], 0x07060302u));
+  } else if constexpr (BITS == 8) {
+    // (x0, x2), (x1, x3), (x4, x6), (x5, x7)
+    return make_uint4(__builtin_amdgcn_perm(h[1], h[0], 0x05040100u), __builtin_amdgcn_perm(h[1], h[0], 0x07060302u),
+                      __builtin_amdgcn_perm(h[3], h[2], 0x05040100u), __builtin_amdgcn_perm(h[3], h[2], 0x07060302u));
+  } else {
+    return make_uint4(h[0], h[1], h[2], h[3]);
+  }
+}
+
+// One vector block of one batch row into LDS: the pair-ordered fp16 values and, from the first lane
+// of each chunk, the chunk sum (8 values in order, then the lanes of the chunk by a DPP tree).
+template <int BITS>
+LFM3_DEV void put_x8(uint16_t* xp, float* xsum, int K, int b, int v, const uint32_t (&h)[4], bool valid) {
+  using Q = QT<BITS>;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += h2f((f16_t)(h[i] & 0xffffu));
+    s += h2f((f16_t)(h[i] >> 16));
+  }
+  s = valid ? s : 0.f;
+  s += dpp_mov<0xb1>(s);                    // chunk = 2 vector blocks (16 codes) ...
+  if (Q::CH == 32) s += dpp_mov<0x4e>(s);   // ... or 4 (32 codes): adjacent lanes
+  if (!valid) return;
+  *(uint4*)(xp + (size_t)b * K + 8 * v) = pair_order8<BITS>(h);
+  if ((v & (Q::CH / 8 - 1)) == 0) xsum[b * (K / Q::CH) + v / (Q::CH / 8)] = s;
+}
+
+// Decode norm prologue registers: the h / m rows of every batch row and the two norm weights.
 template <int BT> struct PrologueRegs {
-  float hv[BT][kP], mv[BT][kP], wpo[kP], wpr[kP];
+  float hv[BT][kVecBlocks][8], mv[BT][kVecBlocks][8], wpo[kVecBlocks][8], wpr[kVecBlocks][8];
 };
 
-// All prologue loads, unconditional (absent inputs read a valid stand-in and are masked later),
-// so they are issued back to back before the weight prefetch.
+// All prologue loads, unconditional (absent inputs read a valid stand-in, masked later), so they
+// are issued back to back before the weight prefetch.
 template <int BT>
 LFM3_DEV void prologue_load(const GemvArgs& a, PrologueRegs<BT>& p) {
-  const int K = a.w.k, tid = threadIdx.x;
+  const int K = a.w.k, nv = K / 8;
   const float* mp = a.m ? a.m : a.h_src;
   const bf16_t* wpo = a.w_post ? a.w_post : a.w_pre;
 #pragma unroll
-  for (int i = 0; i < kP; ++i) {
-    const int k = min(tid + 256 * i, K - 1);
-    p.wpr[i] = bf2f(a.w_pre[k]);
-    p.wpo[i] = bf2f(wpo[k]);
+  for (int j = 0; j < kVecBlocks; ++j) {
+    const int v = min((int)threadIdx.x + 256 * j, nv - 1);
+    bf16x8_to_f32(load_u16x8(a.w_pre + 8 * v), p.wpr[j]);
+    bf16x8_to_f32(load_u16x8(wpo + 8 * v), p.wpo[j]);
 #pragma unroll
     for (int b = 0; b < BT; ++b) {
-      const size_t o = (size_t)min(b, a.batch - 1) * K + k;
-      p.hv[b][i] = a.h_src[o];
-      p.mv[b][i] = mp[o];
+      const size_t o = (size_t)min(b, a.batch - 1) * K + 8 * v;
+      load_f32x8(a.h_src + o, p.hv[b][j]);
+      load_f32x8(mp + o, p.mv[b][j]);
     }
   }
 }
 
-template <int BITS>
-LFM3_DEV void put_x(uint16_t* xp, float* xsum, int K, int b, int k, float x) {
-  using Q = QT<BITS>;
-  const int lane = threadIdx.x & 63;
-  const int c = k / Q::CH, kk = k - c * Q::CH;
-  xp[b * K + c * Q::CH + pair_pos<BITS>(kk)] = f2h(x);
-  // element k = tid + 256 i: chunks of CH consecutive k sit in CH consecutive lanes of one wave
-  float s16 = row16_sum(x);
-  if (Q::CH == 32) s16 += __shfl_xor(s16, 16, 64);
-  if ((lane & (Q::CH - 1)) == 0) xsum[b * (K / Q::CH) + c] = s16;
-}
-
+// The norm arithmetic of k_resid_norm (norm_vec.h) per batch row, then the staging.
 template <int BITS, int BT>
 LFM3_DEV void prologue_compute(const GemvArgs& a, PrologueRegs<BT>& p, uint16_t* xp, float* xsum, float* red) {
-  const int K = a.w.k;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int per = K / 256;
-  if (a.m) {
+  const int K = a.w.k, nv = K / 8;
+  bool ok[kVecBlocks];
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < kP; ++i)
-        if (i < per) ss = fmaf(p.mv[b][i], p.mv[b][i], ss);
-      ss = wave_sum(ss);
-      if (lane == 0) red[wave * BT + b] = ss;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const float rm = rsqrtf((red[b] + red[BT + b] + red[2 * BT + b] + red[3 * BT + b]) / (float)K + a.eps);
-#pragma unroll
-      for (int i = 0; i < kP; ++i) p.hv[b][i] = fmaf(p.mv[b][i] * rm, p.wpo[i], p.hv[b][i]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int b = 0; b < BT; ++b) {
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < kP; ++i)
-      if (i < per) ss = fmaf(p.hv[b][i], p.hv[b][i], ss);
-    ss = wave_sum(ss);
-    if (lane == 0) red[wave * BT + b] = ss;
-  }
-  __syncthreads();
+  for (int j = 0; j < kVecBlocks; ++j) ok[j] = (int)threadIdx.x + 256 * j < nv;
   const bool first = blockIdx.x == 0;
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
-    const float rh = rsqrtf((red[b] + red[BT + b] + red[2 * BT + b] + red[3 * BT + b]) / (float)K + a.eps);
+    if (a.m) {
+      float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < kP; ++i) {
-      if (i < per) {
-        const int k = tid + 256 * i;
-        const float x = (p.hv[b][i] * rh) * p.wpr[i];
-        put_x<BITS>(xp, xsum, K, b, k, b < a.batch ? h2f(f2h_sep(x)) : 0.f);
-        if (first && b < a.batch) {
-          if (a.m && a.h_dst) a.h_dst[(size_t)b * K + k] = p.hv[b][i];
-          if (a.capture) a.capture[(size_t)b * a.capture_ld + k] = p.hv[b][i];
-          if (a.x_copy) a.x_copy[(size_t)b * K + k] = x;
-        }
+      for (int j = 0; j < kVecBlocks; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = ok[j] ? fmaf(p.mv[b][j][e], p.mv[b][j][e], ss) : ss;
+      const float rm = rsqrtf(block_sum4(ss, red + 8 * b) / (float)K + a.eps);
+#pragma unroll
+      for (int j = 0; j < kVecBlocks; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p.hv[b][j][e] = fmaf(p.mv[b][j][e] * rm, p.wpo[j][e], p.hv[b][j][e]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kVecBlocks; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = ok[j] ? fmaf(p.hv[b][j][e], p.hv[b][j][e], ss) : ss;
+    const float rh = rsqrtf(block_sum4(ss, red + 8 * b + 4) / (float)K + a.eps);
+    const bool live = b < a.batch;
+#pragma unroll
+    for (int j = 0; j < kVecBlocks; ++j) {
+      const int v = (int)threadIdx.x + 256 * j;
+      float xv[8];
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = (p.hv[b][j][e] * rh) * p.wpr[j][e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = live ? ((uint32_t)f2h_sep(xv[2 * e]) | ((uint32_t)f2h_sep(xv[2 * e + 1]) << 16)) : 0u;
+      put_x8<BITS>(xp, xsum, K, b, v, h, ok[j]);
+      if (first && live && ok[j]) {
+        if (a.m && a.h_dst) store_f32x8(a.h_dst + (size_t)b * K + 8 * v, p.hv[b][j]);
+        if (a.capture) store_f32x8(a.capture + (size_t)b * a.capture_ld + 8 * v, p.hv[b][j]);
+        if (a.x_copy) store_f32x8(a.x_copy + (size_t)b * K + 8 * v, xv);
       }
     }
   }
 }
 
-template <int BITS, int BT>
-LFM3_DEV void stage_plain(const GemvArgs& a, uint16_t* xp, float* xsum) {
-  const int K = a.w.k, tid = threadIdx.x;
-  const int per = K / 256;
-  for (int i0 = 0; i0 < per; i0 += kP) {
+// Plain fp16 input rows, PVB vector blocks per thread at a time: all loads first, then the
+// staging.
+template <int BT> struct PlainVB { static constexpr int v = BT <= 2 ? 4 : 2; };
+template <int BT> struct PlainRegs { uint4 h[BT][PlainVB<BT>::v]; };
+
+template <int BT>
+LFM3_DEV void plain_load(const GemvArgs& a, PlainRegs<BT>& p, int j0) {
+  const int nv = a.w.k / 8;
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      uint16_t xr[kP];
-      const f16_t* row = a.x + (size_t)min(b, a.batch - 1) * a.ldx;
+  for (int j = 0; j < PlainVB<BT>::v; ++j) {
+    const int v = min((int)threadIdx.x + 256 * (j0 + j), nv - 1);
 #pragma unroll
-      for (int i = 0; i < kP; ++i) xr[i] = row[min(tid + 256 * (i0 + i), K - 1)];
-#pragma unroll
-      for (int i = 0; i < kP; ++i)
-        if (i0 + i < per) put_x<BITS>(xp, xsum, K, b, tid + 256 * (i0 + i), b < a.batch ? h2f(xr[i]) : 0.f);
-    }
+    for (int b = 0; b < BT; ++b) p.h[b][j] = load_u16x8(a.x + (size_t)min(b, a.batch - 1) * a.ldx + 8 * v);
   }
 }
 
-template <int BITS, int BT, int EPI, int PRO>
+template <int BITS, int BT>
+LFM3_DEV void plain_stage(const GemvArgs& a, const PlainRegs<BT>& p, int j0, uint16_t* xp, float* xsum) {
+  const int K = a.w.k, nv = K / 8;
+#pragma unroll
+  for (int b = 0; b < BT; ++b)
+#pragma unroll
+    for (int j = 0; j < PlainVB<BT>::v; ++j) {
+      const int v = (int)threadIdx.x + 256 * (j0 + j);
+      const bool live = b < a.batch;
+      const uint32_t h[4] = {live ? p.h[b][j].x : 0u, live ? p.h[b][j].y : 0u, live ? p.h[b][j].z : 0u, live ? p.h[b][j].w : 0u};
+      put_x8<BITS>(xp, xsum, K, b, v, h, v < nv);
+    }
+}
+
+// KW waves share one row group (each takes every KW-th k iteration; the partial totals are added
+// in wave order through LDS), or KW = 1: each wave owns its groups.
+template <int BITS, int BT, int EPI, int PRO, int KW>
 __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   using Q = QT<BITS>;
   constexpr int RG = RowsPerGroup<EPI>::v;
   extern __shared__ uint32_t smem[];
-  __shared__ float red[4 * BT];
+  __shared__ float red[8 * BT];
+  __shared__ float part[KW > 1 ? KW * BT * kRG : 1];
   const int K = a.w.k;
   const int NC = K / Q::CH;
-  const int NIT = (NC + 63) / 64;
+  const int NIT = (NC + 63) / 64;          // k iterations of a group (a multiple of KW)
+  const int NITW = NIT / KW;               // of them per wave
   uint16_t* xp = (uint16_t*)smem;                 // [BT][K] fp16 in pair order
   float* xsum = (float*)(smem + (BT * K) / 2);    // [BT][NC]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -226,20 +284,22 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   const int n_groups = n_groups_of<EPI>(N);
   const size_t row_bytes = (size_t)K * BITS / 8;
   const int ngr = K / a.w.group;
-  const int gstride = gridDim.x * 4;
+  // group walk: a wave (KW = 1) or a block (KW > 1) takes groups g0, g0 + gstride, ...
+  const int g0 = KW == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
+  const int gstride = KW == 1 ? gridDim.x * 4 : gridDim.x;
+  const int kw = KW == 1 ? 0 : wave;
+  const int ngw = g0 < n_groups ? (n_groups - 1 - g0) / gstride + 1 : 0;
+  const int nsteps = ngw * NITW;
 
-  // The wave walks a flat sequence of (group, chunk) steps. Weights for step s + 1 are loaded
-  // into the other of two register sets while step s is computed (no copies between them, so no
-  // wait beyond the one the compute needs). Loads are branch-free: out-of-range steps load a valid
-  // clamped address and are not computed.
+  // The wave walks a flat sequence of (group, k iteration) steps. Weights for step s + 1 are
+  // loaded into the other of two register sets while step s is computed. Loads are branch-free:
+  // out-of-range steps load a valid clamped address and are not computed.
   struct WRegs {
     uint32_t q[RG][Q::NDW];
     bf16_t s[RG], b[RG];   // raw bits: converted when used
   };
-  const int g0 = blockIdx.x * 4 + wave;
-  const int nsteps = g0 < n_groups ? ((n_groups - 1 - g0) / gstride + 1) * NIT : 0;
   auto fetch = [&](WRegs& W, int step) {
-    const int gi = step / NIT, it = step - gi * NIT;
+    const int gi = step / NITW, it = kw + KW * (step - gi * NITW);
     const int c = min(lane + 64 * it, NC - 1);
     int rows[RG];
     rows_of<EPI>(min(g0 + gi * gstride, n_groups - 1), N, rows);
@@ -262,7 +322,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   WRegs wa, wb;
   if constexpr (PRO) {
     // prologue loads first, then the weight prefetch, then the prologue arithmetic: the in-order
-    // load counter then lets the weights stay in flight through the prologue
+    // load counter lets the weights stay in flight through the prologue
     PrologueRegs<BT> p;
     prologue_load<BT>(a, p);
     __builtin_amdgcn_sched_barrier(0);
@@ -270,23 +330,31 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     prologue_compute<BITS, BT>(a, p, xp, xsum, red);
   } else {
-    stage_plain<BITS, BT>(a, xp, xsum);
+    PlainRegs<BT> p;
+    plain_load<BT>(a, p, 0);
+    __builtin_amdgcn_sched_barrier(0);
     fetch(wa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    plain_stage<BITS, BT>(a, p, 0, xp, xsum);
+    for (int j0 = PlainVB<BT>::v; 256 * j0 < K / 8; j0 += PlainVB<BT>::v) {
+      plain_load<BT>(a, p, j0);
+      plain_stage<BITS, BT>(a, p, j0, xp, xsum);
+    }
   }
   __syncthreads();
 
   uint64_t best[BT];
 #pragma unroll
   for (int b = 0; b < BT; ++b) best[b] = 0;
-  float acc[RG][BT];
+  float acc[kRG][BT];
 #pragma unroll
-  for (int r = 0; r < RG; ++r)
+  for (int r = 0; r < kRG; ++r)
 #pragma unroll
     for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
 
   auto consume = [&](const WRegs& W, int step) {
-    const int gi = step / NIT, it = step - gi * NIT;
-    const int c = lane + 64 * it;
+    const int gi = step / NITW, sw = step - gi * NITW;
+    const int c = lane + 64 * (kw + KW * sw);
     if (c < NC) {
       uint32_t xv[BT][Q::NP];
       float X[BT];
@@ -310,78 +378,97 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
           float d = 0.f;
 #pragma unroll
           for (int p = 0; p < Q::NP; ++p) d = dot2(wp[p], xv[b][p], d);
-          acc[r][b] += fmaf(sc, d - kMagicOff * X[b], bi * X[b]);
+          acc[r][b] += fmaf(sc, fmaf(-kMagicOff, X[b], d), bi * X[b]);
         }
       }
     }
-    if (it != NIT - 1) return;
+    if (sw != NITW - 1) return;
     const int g = g0 + gi * gstride;
-    // totals are wave-uniform after wave_sum
+    // t[b]: lanes 8r .. 8r+7 hold the total of row r of the group
+    float t[BT];
 #pragma unroll
-    for (int r = 0; r < RG; ++r)
+    for (int b = 0; b < BT; ++b) {
+      float v8[8];
 #pragma unroll
-      for (int b = 0; b < BT; ++b) acc[r][b] = wave_sum(acc[r][b]);
-    if (lane == 0) {
-      if constexpr (EPI == GEMV_STORE) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int b = 0; b < BT; ++b)
-            if (b < a.batch && 8 * g + r < N) a.yf[(size_t)b * a.ldy + 8 * g + r] = acc[r][b];
-      } else if constexpr (EPI == GEMV_SWIGLU) {
-        // silu(a) * b is rounded to fp32, then to fp16, in every batch-size instance, so a row's
-        // result does not depend on the batch it is decoded in
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int b = 0; b < BT; ++b) {
-            if (b >= a.batch) continue;
-            const float gt = acc[j][b], up = acc[4 + j][b];
-            const float sv = gt / (1.f + __expf(-gt)) * up;
-            a.y[(size_t)b * a.ldy + 4 * g + j] = f2h_sep(sv);
-          }
-      } else if constexpr (EPI == GEMV_CONV) {
-        // gated short conv of channels 2g, 2g+1 ("LFM3-1.7B port" table row 1): z = f16(B * x),
-        // y = sum_j ker[c, j] * [state | z]_j, out = f16(C * y), state <- last taps-1 z
-        const int H = N / 3, T = a.conv_taps, S = T - 1;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int ch = 2 * g + j;
-          float ker[kMaxTaps];
-          for (int t = 0; t < T; ++t) ker[t] = bf2f(a.conv_kernel[(size_t)ch * T + t]);
-#pragma unroll
-          for (int b = 0; b < BT; ++b) {
-            if (b >= a.batch) continue;
-            f16_t* st = a.conv_state + (size_t)a.conv_slot[b] * a.conv_slot_stride;
-            const float z = h2f(f2h_sep(acc[j][b] * acc[4 + j][b]));
-            float win[kMaxTaps];
-            for (int t = 0; t < S; ++t) win[t] = h2f(st[(size_t)t * H + ch]);
-            float y = ker[S] * z;
-            for (int t = 0; t < S; ++t) y = fmaf(ker[t], win[t], y);
-            for (int t = 0; t + 1 < S; ++t) st[(size_t)t * H + ch] = f2h(win[t + 1]);
-            st[(size_t)(S - 1) * H + ch] = f2h(z);
-            a.y[(size_t)b * a.ldy + ch] = f2h_sep(acc[2 + j][b] * y);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int n = 8 * g + r;
-          if (n >= N) continue;
-#pragma unroll
-          for (int b = 0; b < BT; ++b) {
-            if (b >= a.batch) continue;
-            if (a.logits) a.logits[(size_t)b * a.ld_logits + n] = acc[r][b];
-            const uint64_t key = ((uint64_t)order_key(acc[r][b]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)n);
-            best[b] = key > best[b] ? key : best[b];
-          }
-        }
-      }
+      for (int r = 0; r < kRG; ++r) v8[r] = acc[r][b];
+      t[b] = bfly8(v8);
     }
 #pragma unroll
-    for (int r = 0; r < RG; ++r)
+    for (int r = 0; r < kRG; ++r)
 #pragma unroll
       for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
+    if constexpr (KW > 1) {
+      if ((lane & 7) == 0)
+#pragma unroll
+        for (int b = 0; b < BT; ++b) part[(wave * BT + b) * kRG + (lane >> 3)] = t[b];
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        float s = part[b * kRG + (lane >> 3)];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) s += part[(w * BT + b) * kRG + (lane >> 3)];
+        t[b] = s;
+      }
+      __syncthreads();
+      if (wave != 0) return;
+    }
+    const int r = lane >> 3;
+    if constexpr (EPI == GEMV_STORE) {
+      if ((lane & 7) == 0 && 8 * g + r < N)
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+          if (b < a.batch) a.yf[(size_t)b * a.ldy + 8 * g + r] = t[b];
+    } else if constexpr (EPI == GEMV_SWIGLU) {
+      // silu(a) * b is rounded to fp32, then to fp16, in every batch-size instance, so a row's
+      // result does not depend on the batch it is decoded in
+      float up[BT];
+#pragma unroll
+      for (int b = 0; b < BT; ++b) up[b] = __shfl_xor(t[b], 32, 64);
+      if ((lane & 7) == 0 && r < 4)
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          if (b >= a.batch) continue;
+          const float gt = t[b];
+          const float sv = gt / (1.f + __expf(-gt)) * up[b];
+          a.y[(size_t)b * a.ldy + 4 * g + r] = f2h_sep(sv);
+        }
+    } else if constexpr (EPI == GEMV_CONV) {
+      // gated short conv of channels 2g, 2g+1 ("LFM3-1.7B port" table row 1): z = f16(B * x),
+      // y = sum_j ker[c, j] * [state | z]_j, out = f16(C * y), state <- last taps-1 z.
+      // Rows: B of the two channels in lanes 0 / 8, C in 16 / 24, x in 32 / 40.
+      float cg[BT], xg[BT];
+#pragma unroll
+      for (int b = 0; b < BT; ++b) { cg[b] = __shfl(t[b], (lane + 16) & 63, 64); xg[b] = __shfl(t[b], (lane + 32) & 63, 64); }
+      if ((lane & 7) == 0 && r < 2) {
+        const int H = N / 3, T = a.conv_taps, S = T - 1;
+        const int ch = 2 * g + r;
+        float ker[kMaxTaps];
+        for (int q = 0; q < T; ++q) ker[q] = bf2f(a.conv_kernel[(size_t)ch * T + q]);
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          if (b >= a.batch) continue;
+          f16_t* st = a.conv_state + (size_t)a.conv_slot[b] * a.conv_slot_stride;
+          const float z = h2f(f2h_sep(t[b] * xg[b]));
+          float win[kMaxTaps];
+          for (int q = 0; q < S; ++q) win[q] = h2f(st[(size_t)q * H + ch]);
+          float y = ker[S] * z;
+          for (int q = 0; q < S; ++q) y = fmaf(ker[q], win[q], y);
+          for (int q = 0; q + 1 < S; ++q) st[(size_t)q * H + ch] = f2h(win[q + 1]);
+          st[(size_t)(S - 1) * H + ch] = f2h(z);
+          a.y[(size_t)b * a.ldy + ch] = f2h_sep(cg[b] * y);
+        }
+      }
+    } else {
+      const int n = 8 * g + r;
+      if ((lane & 7) == 0 && n < N)
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          if (b >= a.batch) continue;
+          if (a.logits) a.logits[(size_t)b * a.ld_logits + n] = t[b];
+          const uint64_t key = ((uint64_t)order_key(t[b]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)n);
+          best[b] = key > best[b] ? key : best[b];
+        }
+    }
   };
 
   for (int step = 0; step < nsteps; step += 2) {
@@ -390,10 +477,32 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     fetch(wa, step + 2);
     if (step + 1 < nsteps) consume(wb, step + 1);
   }
-  if (EPI == GEMV_LOGITS && lane == 0) {
+  if constexpr (EPI == GEMV_LOGITS) {
 #pragma unroll
-    for (int b = 0; b < BT; ++b)
-      if (b < a.batch && best[b]) atomicMax((unsigned long long*)&a.keys[b], (unsigned long long)best[b]);
+    for (int b = 0; b < BT; ++b) {
+      uint64_t k = best[b];
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)k, o, 64), hi = __shfl_xor((uint32_t)(k >> 32), o, 64);
+        const uint64_t other = ((uint64_t)hi << 32) | lo;
+        k = other > k ? other : k;
+      }
+      if (lane == 0 && b < a.batch && k) atomicMax((unsigned long long*)&a.keys[b], (unsigned long long)k);
+    }
+  }
+}
+
+#ifndef LFM3_GEMV_MAX_BLOCKS
+#define LFM3_GEMV_MAX_BLOCKS 512
+#endif
+
+template <int BITS, int BT, int PRO, int KW>
+static void launch_epi(hipStream_t s, const GemvArgs& a, int grid, size_t lds) {
+  switch (a.epi) {
+    case GEMV_STORE: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
+    case GEMV_SWIGLU: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_SWIGLU, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
+    case GEMV_CONV: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_CONV, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
+    default: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_LOGITS, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
   }
 }
 
@@ -405,27 +514,23 @@ static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
   const int N = a.w.n;
   const int n_groups = a.epi == GEMV_SWIGLU ? n_groups_of<GEMV_SWIGLU>(N)
                        : a.epi == GEMV_CONV ? n_groups_of<GEMV_CONV>(N) : n_groups_of<GEMV_STORE>(N);
-  int grid = (n_groups + 3) / 4;
-  const int cap = a.max_blocks > 0 ? a.max_blocks : 1024;
+  // Long rows (4 or more k iterations of 64 chunks) are shared by the 4 waves of a block, so that
+  // narrow matrices still spread over the whole chip.
+  const int nit = (K / Q::CH + 63) / 64;
+  const bool split = nit % 4 == 0;
+  const int cap = a.max_blocks > 0 ? a.max_blocks : LFM3_GEMV_MAX_BLOCKS;
+  int grid = split ? n_groups : (n_groups + 3) / 4;
   if (grid > cap) grid = cap;
   if (a.h_src) {
     if constexpr (BT <= 2) {
-      switch (a.epi) {
-        case GEMV_STORE: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, 1>), dim3(grid), dim3(256), lds, s, a); break;
-        case GEMV_SWIGLU: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_SWIGLU, 1>), dim3(grid), dim3(256), lds, s, a); break;
-        case GEMV_CONV: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_CONV, 1>), dim3(grid), dim3(256), lds, s, a); break;
-        default: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_LOGITS, 1>), dim3(grid), dim3(256), lds, s, a); break;
-      }
+      if (split) launch_epi<BITS, BT, 1, 4>(s, a, grid, lds);
+      else launch_epi<BITS, BT, 1, 1>(s, a, grid, lds);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
-    switch (a.epi) {
-      case GEMV_STORE: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, 0>), dim3(grid), dim3(256), lds, s, a); break;
-      case GEMV_SWIGLU: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_SWIGLU, 0>), dim3(grid), dim3(256), lds, s, a); break;
-      case GEMV_CONV: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_CONV, 0>), dim3(grid), dim3(256), lds, s, a); break;
-      default: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_LOGITS, 0>), dim3(grid), dim3(256), lds, s, a); break;
-    }
+    if (split) launch_epi<BITS, BT, 0, 4>(s, a, grid, lds);
+    else launch_epi<BITS, BT, 0, 1>(s, a, grid, lds);
   }
   return hipGetLastError();
 }
@@ -464,6 +569,12 @@ static hipError_t launch_bits(hipStream_t s, const GemvArgs& a) {
 
 hipError_t launch_gemv(hipStream_t s, const GemvArgs& a) {
   if (a.batch <= 0) return hipSuccess;
+  // vector staging: rows of 8-element blocks, 16-byte aligned; the norm prologue takes K <= 4096
+  if (a.w.k % 8 || (a.h_src && a.w.k > 256 * 8 * kVecBlocks)) return hipErrorInvalidValue;
+  if (a.h_src ? ((uintptr_t)a.h_src % 16 || (a.m && (uintptr_t)a.m % 16) || (uintptr_t)a.w_pre % 16 ||
+                 (a.w_post && (uintptr_t)a.w_post % 16))
+              : ((uintptr_t)a.x % 16 || a.ldx % 8))
+    return hipErrorInvalidValue;
   switch (a.w.bits) {
     case 4: return launch_bits<4>(s, a);
     case 6: return launch_bits<6>(s, a);

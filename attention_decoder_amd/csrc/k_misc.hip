@@ -2,6 +2,7 @@
 // RMSNorm, per-head q/k norm + RoPE + KV store, the gated short conv with its kept state, and
 // bookkeeping (page table, argmax finalisation, fills, the dequant check).
 #include "kernels.h"
+#include "norm_vec.h"
 
 namespace lfm3 {
 
@@ -89,48 +90,59 @@ hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int ro
 // ---------------------------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
-  // the arithmetic (per-thread k = tid + 256 i, explicit fma order, 4-wave sum in wave order) is
-  // the same as the decode GEMV's norm prologue, so fused and unfused steps agree bitwise
-  __shared__ float red[16];
+  // the arithmetic is the decode GEMV's norm prologue (norm_vec.h), so fused and unfused steps
+  // agree bitwise
+  __shared__ float red[8];
   const int r = blockIdx.x;
   const int H = a.hidden;
   const size_t base = (size_t)r * H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int kPer = 16;
-  float hv[kPer];
-  const int per = H / 256;
+  const int nv = H / 8;
+  float hv[kVecBlocks][8], mv[kVecBlocks][8], wpo[kVecBlocks][8], wpr[kVecBlocks][8];
+  const float* mp = a.m ? a.m : a.h_in;
+  const bf16_t* wpo_p = a.w_post ? a.w_post : a.w_pre;
+#pragma unroll
+  for (int j = 0; j < kVecBlocks; ++j) {
+    const int v = min((int)threadIdx.x + 256 * j, nv - 1);
+    load_f32x8(a.h_in + base + 8 * v, hv[j]);
+    load_f32x8(mp + base + 8 * v, mv[j]);
+    bf16x8_to_f32(load_u16x8(wpo_p + 8 * v), wpo[j]);
+    bf16x8_to_f32(load_u16x8(a.w_pre + 8 * v), wpr[j]);
+  }
+  bool ok[kVecBlocks];
+#pragma unroll
+  for (int j = 0; j < kVecBlocks; ++j) ok[j] = (int)threadIdx.x + 256 * j < nv;
   if (a.m) {
-    float mv[kPer];
     float ss = 0.f;
-    for (int i = 0; i < per; ++i) {
-      mv[i] = a.m[base + tid + 256 * i];
-      ss = fmaf(mv[i], mv[i], ss);
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    const float rm = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + a.eps);
-    for (int i = 0; i < per; ++i) {
-      const int k = tid + 256 * i;
-      hv[i] = fmaf(mv[i] * rm, bf2f(a.w_post[k]), a.h_in[base + k]);
-    }
-    __syncthreads();
-  } else {
-    for (int i = 0; i < per; ++i) hv[i] = a.h_in[base + tid + 256 * i];
+#pragma unroll
+    for (int j = 0; j < kVecBlocks; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = ok[j] ? fmaf(mv[j][e], mv[j][e], ss) : ss;
+    const float rm = rsqrtf(block_sum4(ss, red) / (float)H + a.eps);
+#pragma unroll
+    for (int j = 0; j < kVecBlocks; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[j][e] = fmaf(mv[j][e] * rm, wpo[j][e], hv[j][e]);
   }
   float ss = 0.f;
-  for (int i = 0; i < per; ++i) ss = fmaf(hv[i], hv[i], ss);
-  ss = wave_sum(ss);
-  if (lane == 0) red[4 + wave] = ss;
-  __syncthreads();
-  const float rh = rsqrtf((red[4] + red[5] + red[6] + red[7]) / (float)H + a.eps);
-  for (int i = 0; i < per; ++i) {
-    const int k = tid + 256 * i;
-    if (a.m) a.h_out[base + k] = hv[i];
-    if (a.capture) a.capture[base + k] = hv[i];
-    const float xv = (hv[i] * rh) * bf2f(a.w_pre[k]);
-    a.x_out[base + k] = f2h_sep(xv);
-    if (a.x_copy) a.x_copy[base + k] = xv;
+#pragma unroll
+  for (int j = 0; j < kVecBlocks; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = ok[j] ? fmaf(hv[j][e], hv[j][e], ss) : ss;
+  const float rh = rsqrtf(block_sum4(ss, red + 4) / (float)H + a.eps);
+#pragma unroll
+  for (int j = 0; j < kVecBlocks; ++j) {
+    if (!ok[j]) continue;
+    const int k = 8 * ((int)threadIdx.x + 256 * j);
+    float xv[8];
+    uint32_t xh[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[e] = (hv[j][e] * rh) * wpr[j][e];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xh[e] = (uint32_t)f2h_sep(xv[2 * e]) | ((uint32_t)f2h_sep(xv[2 * e + 1]) << 16);
+    if (a.m) store_f32x8(a.h_out + base + k, hv[j]);
+    if (a.capture) store_f32x8(a.capture + base + k, hv[j]);
+    if (a.x_copy) store_f32x8(a.x_copy + base + k, xv);
+    *(uint4*)(a.x_out + base + k) = make_uint4(xh[0], xh[1], xh[2], xh[3]);
   }
 }
 
