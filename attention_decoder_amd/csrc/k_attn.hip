@@ -186,8 +186,8 @@ LFM3_DEV size_t kv_off(const KvRef& kv, int slot, int pos, int page, int kvh, in
 
 template <bool PAGED>
 __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) f16_t kt[SPLIT * KVS];
-  __shared__ __attribute__((aligned(16))) f16_t vt[SPLIT * KVS];
+  __shared__ __attribute__((aligned(16))) f16_t kt[(SPLIT + 1) * KVS];
+  __shared__ __attribute__((aligned(16))) f16_t vt[(SPLIT + 1) * KVS];
   __shared__ float qs[kQPerKv][kHeadDim];
   __shared__ float sc[kQPerKv][SPLIT];
   __shared__ int is_last;
@@ -212,12 +212,12 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
     jq[q] = j0 + min(((tid + 256 * q) >> 4), nk - 1);
     pg[q] = PAGED ? pt[jq[q] / kPageTokens] : 0;
   }
-  uint4 kr[4], vr[4];
+  u32x4_v kr[4], vr[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const size_t o = kv_off<PAGED>(a.kv, slot, jq[q], pg[q], kvh, nkv) + 8 * ((tid + 256 * q) & 15);
-    kr[q] = *(const uint4*)(a.kv.k + o);
-    vr[q] = *(const uint4*)(a.kv.v + o);
+    kr[q] = *(const u32x4_v*)(a.kv.k + o);
+    vr[q] = *(const u32x4_v*)(a.kv.v + o);
   }
   // 2. query heads 4 kvh + w (wave w), and the step's own key and value (per-head k RMSNorm +
   //    RoPE, "LFM3-1.7B port": partial RoPE on the full layers); lane holds dims lane, lane + 64
@@ -256,14 +256,14 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
     t[lane] = h0;
     t[lane + kHalfDim] = h1;
   }
-  // 3. tiles to LDS (the current position's row came from step 2)
+  // 3. tiles to LDS (the current position's row came from step 2); keys past the split and the
+  //    current position go to the spare row SPLIT, so the stores are unconditional
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int idx = tid + 256 * q, key = idx >> 4, c8 = idx & 15;
-    if (key < nk && j0 + key != pos) {
-      *(uint4*)(kt + key * KVS + 8 * c8) = kr[q];
-      *(uint4*)(vt + key * KVS + 8 * c8) = vr[q];
-    }
+    const int row_l = (key < nk && j0 + key != pos) ? key : SPLIT;
+    *(u32x4_v*)(kt + row_l * KVS + 8 * c8) = kr[q];
+    *(u32x4_v*)(vt + row_l * KVS + 8 * c8) = vr[q];
   }
   __syncthreads();
   // 4. scores: thread -> key t / 4, dims [32 (t % 4), + 32) for the 4 heads; sum over 4 lanes
@@ -275,10 +275,10 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
 #pragma unroll
     for (int e8 = 0; e8 < 4; ++e8) {
       const uint4 v = *(const uint4*)(kp + 8 * e8);
-      const f16_t* e16 = (const f16_t*)&v;
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float kf = h2f(e16[e]);
+        const float kf = h2f((f16_t)((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu)));
 #pragma unroll
         for (int hh = 0; hh < kQPerKv; ++hh) d[hh] = fmaf(qs[hh][32 * qd + 8 * e8 + e], kf, d[hh]);
       }

@@ -42,6 +42,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=48, help="oracle decode steps timed for cpu_baseline")
     ap.add_argument("--profile-only", action="store_true", help="one short step for rocprofv3 runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --profile-only: also run three 256 MiB device copies (the reference kernel that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is described in DESIGN.md, not built",
@@ -83,6 +86,13 @@ def main():
         args.decode = min(args.decode, 32)
         job()
         torch.cuda.synchronize()
+        if args.copy_calibration:
+            src = torch.empty((64 << 20,), dtype=torch.float32, device=dev).fill_(1.0)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
         log("profile-only step done")
         return
 
@@ -121,7 +131,7 @@ def main():
     achieved = per_launch_bytes / (per_launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": "k_gemv (decode dequant-GEMV, all linears + tied head)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": gemv_traffic(),
                 "bytes_per_launch": round(per_launch_bytes), "us_per_launch": round(per_launch_us, 3),
                 "launches_per_token": g["launches"] // args.decode}
     breakdown = {k: {"ms_per_token": round(v["ms"] / args.decode, 4), "launches_per_token": v["launches"] / args.decode}
@@ -161,6 +171,26 @@ def main():
     }
     print(json.dumps(line))
     eng.close()
+
+
+def gemv_traffic():
+    """HBM bytes per decode GEMV launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE record
+    (each counter scaled by a 256 MiB device copy of known size), or None when the kernel sources
+    have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_decode_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for p in rec["source_files"]:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def run_extras(eng, synth, torch, dev):

@@ -75,24 +75,33 @@ def _geometry():
     return H, V, n_conv, n_attn, conv_lin, attn_lin, ffn_lin, extras_bf16
 
 
+def _golden_totals():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "header_totals.json")) as f:
+        return json.load(f)
+
+
 def test_mlx_q4_header_totals():
     """594 tensors / 973,008,384 B for the MLX 4-bit export follow from the geometry."""
+    want = _golden_totals()["mlx_q4_g64"]
     H, V, n_conv, n_attn, conv_lin, attn_lin, ffn_lin, extras = _geometry()
     lins = n_conv * conv_lin + n_attn * attn_lin + 24 * ffn_lin + [(V, H)]
     qbytes = sum(n * k // 2 + 2 * 2 * n * (k // 64) for n, k in lins)
-    assert qbytes + 2 * extras == 973_008_384
+    assert qbytes + 2 * extras == want["bytes"]
     n_tensors = n_conv * (3 * 2 + 1 + 4 + 9) + n_attn * (3 * 5 + 2 + 4 + 9) + 3 + 1
-    assert n_tensors == 594
+    assert n_tensors == want["tensors"]
 
 
 def test_nvfp4_header_totals():
     """502 tensors / 1,829,689,408 B for the NVFP4 export (FFN fp4 g16 + e4m3 scales)."""
+    want = _golden_totals()["nvfp4"]
     H, V, n_conv, n_attn, conv_lin, attn_lin, ffn_lin, extras = _geometry()
     ffn = 24 * ffn_lin
     fp4 = sum(n * k // 2 + n * k // 16 + 4 + 4 for n, k in ffn)
     bf16 = 2 * sum(n * k for n, k in n_conv * conv_lin + n_attn * attn_lin + [(V, H)])
-    assert fp4 + bf16 + 2 * extras == 1_829_689_408
-    assert 72 * 4 + n_conv * 7 + n_attn * 11 + 2 == 502
+    assert fp4 + bf16 + 2 * extras == want["bytes"]
+    assert 72 * 4 + n_conv * 7 + n_attn * 11 + 2 == want["tensors"]
 
 
 def test_blob_plan_matches_header_total():
