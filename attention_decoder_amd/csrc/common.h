@@ -59,6 +59,14 @@ LFM3_DEV f16_t f2h_sep(float f) {
   return (f16_t)(r & 0xffffu);
 }
 
+// a - b, rounded once, that the compiler cannot contract with the multiply producing `a` (the
+// fp16 remainder x - f16(x) must be the same value in every kernel that forms it).
+LFM3_DEV float sub_sep(float a, float b) {
+  float r;
+  asm("v_sub_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 LFM3_DEV float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -39,29 +39,51 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
   const int kvh = blockIdx.y;
   const int h = kvh * kQPerKv + wave;
   const int M = a.rows.n;
-  const int r0 = blockIdx.x * 32;
+  // the causal work grows with the query block: the longest blocks are dispatched first
+  const int r0 = (gridDim.x - 1 - blockIdx.x) * 32;
   const int slot = a.rows.slot0;
   const int p_first = a.rows.pos0 + r0;
   const int r_last = min(M - 1, r0 + 31);
   const int p_last = a.rows.pos0 + r_last;
   const int nq = a.n_q_heads, nkv = a.n_kv_heads;
+  const bool paged = a.kv.ring == 0;
 
-  // this lane's query (column) and its position
+  // this lane's query (column) and its position; rows past M read row M - 1 and are not stored
   const int qr = r0 + (lane & 31);
   const int qpos = a.rows.pos0 + qr;
   const bool qvalid = qr < M;
   f16x8_v qv[8];
   {
-    const f16_t* qp = a.q + ((size_t)(qvalid ? qr : 0) * nq + h) * kHeadDim;
+    const f16_t* qp = a.q + ((size_t)min(qr, M - 1) * nq + h) * kHeadDim;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (qvalid) qv[s] = *(const f16x8_v*)(qp + 16 * s + 8 * (lane >> 5));
-      else for (int e = 0; e < 8; ++e) qv[s][e] = (_Float16)0.f;
-    }
+    for (int s = 0; s < 8; ++s) qv[s] = *(const f16x8_v*)(qp + 16 * s + 8 * (lane >> 5));
   }
   int k_lo = 0;
   if (a.window > 0) k_lo = max(0, p_first - (a.window - 1));
   const int kb0 = k_lo / KT * KT;
+
+  // K/V tile loads, branch-free and one tile ahead: thread t moves 16-byte chunks t and t + 256 of
+  // the 32 key x 16 chunk tile; keys outside [k_lo, p_last] read a clamped valid key (masked in the
+  // softmax). Page ids of full layers are loaded one tile further ahead.
+  const int32_t* pt = a.kv.page_table + (size_t)slot * a.kv.max_pages;
+  auto key_of = [&](int kb, int i) { return min(max(kb + ((tid + 256 * i) >> 4), k_lo), p_last); };
+  auto page_of = [&](int kb, int i) { return paged ? pt[key_of(kb, i) / kPageTokens] : 0; };
+  auto kv_at = [&](int j, int page) -> size_t {
+    return paged ? (((size_t)page * nkv + kvh) * kPageTokens + (j % kPageTokens)) * kHeadDim
+                 : (((size_t)slot * nkv + kvh) * a.kv.ring + (j % a.kv.ring)) * kHeadDim;
+  };
+  int pg[2], pg_next[2];
+  u32x4_v kr[2], vr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pg[i] = page_of(kb0, i);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const size_t o = kv_at(key_of(kb0, i), pg[i]) + 8 * ((tid + 256 * i) & 15);
+    kr[i] = *(const u32x4_v*)(a.kv.k + o);
+    vr[i] = *(const u32x4_v*)(a.kv.v + o);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pg_next[i] = page_of(kb0 + KT, i);
 
   f32x16_v o[4];
 #pragma unroll
@@ -74,24 +96,32 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
   const int kslot = (ks_r & ~12) | ((ks_r & 4) << 1) | ((ks_r & 8) >> 1);
 
   for (int kb = kb0; kb <= p_last; kb += KT) {
-    // cooperative load: 32 keys x 128 dims for K (row-major) and V (transposed into Vt)
+    // the tile's K rows and V^T columns into LDS
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;   // 512 chunks of 8 dims
+      const int idx = tid + 256 * i;
       const int key = idx >> 4, c8 = idx & 15;
-      const int j = kb + key;
-      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-      if (j >= k_lo && j <= p_last) {
-        kv4 = *(const uint4*)(kv_src(a.kv, a.kv.k, slot, j, kvh, nkv) + 8 * c8);
-        vv4 = *(const uint4*)(kv_src(a.kv, a.kv.v, slot, j, kvh, nkv) + 8 * c8);
-      }
-      *(uint4*)(Ks + key * KS + 8 * c8) = kv4;
-      const f16_t* ve = (const f16_t*)&vv4;
+      *(u32x4_v*)(Ks + key * KS + 8 * c8) = kr[i];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(8 * c8 + e) * VS + key] = ve[e];
+      for (int e = 0; e < 4; ++e) {
+        Vt[(8 * c8 + 2 * e) * VS + key] = (f16_t)(vr[i][e] & 0xffffu);
+        Vt[(8 * c8 + 2 * e + 1) * VS + key] = (f16_t)(vr[i][e] >> 16);
+      }
     }
     __syncthreads();
+    // next tile's loads (clamped: past the last tile they re-read valid keys, unused)
+    {
+      const int kn = kb + KT;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const size_t off = kv_at(key_of(kn, i), pg_next[i]) + 8 * ((tid + 256 * i) & 15);
+        kr[i] = *(const u32x4_v*)(a.kv.k + off);
+        vr[i] = *(const u32x4_v*)(a.kv.v + off);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) pg_next[i] = page_of(kn + KT, i);
+    }
 
     // S^T tile: rows = key slots, cols = queries
     f32x16_v st;

@@ -186,16 +186,21 @@ LFM3_DEV void prologue_load(const GemvArgs& a, PrologueRegs<BT>& p) {
   }
 }
 
-// The norm arithmetic of k_resid_norm (norm_vec.h) per batch row, then the staging.
+// The norm arithmetic of k_resid_norm (norm_vec.h) per batch row, then the staging. When the input
+// is carried as an fp16 pair (split), real row b stages its high parts as virtual row b and its
+// remainders as virtual row b + BT/2.
 template <int BITS, int BT>
-LFM3_DEV void prologue_compute(const GemvArgs& a, PrologueRegs<BT>& p, uint16_t* xp, float* xsum, float* red) {
+LFM3_DEV void prologue_compute(const GemvArgs& a, PrologueRegs<BT>& p, uint16_t* xp, float* xsum, float* red,
+                               bool split) {
   const int K = a.w.k, nv = K / 8;
+  constexpr int HB = BT / 2;
   bool ok[kVecBlocks];
 #pragma unroll
   for (int j = 0; j < kVecBlocks; ++j) ok[j] = (int)threadIdx.x + 256 * j < nv;
   const bool first = blockIdx.x == 0;
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
+    if (split && b >= HB) break;
     if (a.m) {
       float ss = 0.f;
 #pragma unroll
@@ -219,12 +224,17 @@ LFM3_DEV void prologue_compute(const GemvArgs& a, PrologueRegs<BT>& p, uint16_t*
     for (int j = 0; j < kVecBlocks; ++j) {
       const int v = (int)threadIdx.x + 256 * j;
       float xv[8];
-      uint32_t h[4];
+      uint32_t h[4], l[4];
 #pragma unroll
       for (int e = 0; e < 8; ++e) xv[e] = (p.hv[b][j][e] * rh) * p.wpr[j][e];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = live ? ((uint32_t)f2h_sep(xv[2 * e]) | ((uint32_t)f2h_sep(xv[2 * e + 1]) << 16)) : 0u;
+      for (int e = 0; e < 4; ++e) {
+        const f16_t h0 = f2h_sep(xv[2 * e]), h1 = f2h_sep(xv[2 * e + 1]);
+        h[e] = live ? ((uint32_t)h0 | ((uint32_t)h1 << 16)) : 0u;
+        l[e] = live ? ((uint32_t)f2h_sep(sub_sep(xv[2 * e], h2f(h0))) | ((uint32_t)f2h_sep(sub_sep(xv[2 * e + 1], h2f(h1))) << 16)) : 0u;
+      }
       put_x8<BITS>(xp, xsum, K, b, v, h, ok[j]);
+      if (split) put_x8<BITS>(xp, xsum, K, b + HB, v, l, ok[j]);
       if (first && live && ok[j]) {
         if (a.m && a.h_dst) store_f32x8(a.h_dst + (size_t)b * K + 8 * v, p.hv[b][j]);
         if (a.capture) store_f32x8(a.capture + (size_t)b * a.capture_ld + 8 * v, p.hv[b][j]);
@@ -239,26 +249,33 @@ LFM3_DEV void prologue_compute(const GemvArgs& a, PrologueRegs<BT>& p, uint16_t*
 template <int BT> struct PlainVB { static constexpr int v = BT <= 2 ? 4 : 2; };
 template <int BT> struct PlainRegs { uint4 h[BT][PlainVB<BT>::v]; };
 
+// Virtual row b of a split input reads row b % (BT/2) of x (b < BT/2) or of x_lo.
 template <int BT>
-LFM3_DEV void plain_load(const GemvArgs& a, PlainRegs<BT>& p, int j0) {
+LFM3_DEV void plain_load(const GemvArgs& a, PlainRegs<BT>& p, int j0, bool split) {
   const int nv = a.w.k / 8;
+  constexpr int HB = BT > 1 ? BT / 2 : 1;
 #pragma unroll
   for (int j = 0; j < PlainVB<BT>::v; ++j) {
     const int v = min((int)threadIdx.x + 256 * (j0 + j), nv - 1);
 #pragma unroll
-    for (int b = 0; b < BT; ++b) p.h[b][j] = load_u16x8(a.x + (size_t)min(b, a.batch - 1) * a.ldx + 8 * v);
+    for (int b = 0; b < BT; ++b) {
+      const int rb = split ? b % HB : b;
+      const f16_t* src = (split && b >= HB) ? a.x_lo : a.x;
+      p.h[b][j] = load_u16x8(src + (size_t)min(rb, a.batch - 1) * a.ldx + 8 * v);
+    }
   }
 }
 
 template <int BITS, int BT>
-LFM3_DEV void plain_stage(const GemvArgs& a, const PlainRegs<BT>& p, int j0, uint16_t* xp, float* xsum) {
+LFM3_DEV void plain_stage(const GemvArgs& a, const PlainRegs<BT>& p, int j0, uint16_t* xp, float* xsum, bool split) {
   const int K = a.w.k, nv = K / 8;
+  constexpr int HB = BT > 1 ? BT / 2 : 1;
 #pragma unroll
   for (int b = 0; b < BT; ++b)
 #pragma unroll
     for (int j = 0; j < PlainVB<BT>::v; ++j) {
       const int v = (int)threadIdx.x + 256 * (j0 + j);
-      const bool live = b < a.batch;
+      const bool live = (split ? b % HB : b) < a.batch;
       const uint32_t h[4] = {live ? p.h[b][j].x : 0u, live ? p.h[b][j].y : 0u, live ? p.h[b][j].z : 0u, live ? p.h[b][j].w : 0u};
       put_x8<BITS>(xp, xsum, K, b, v, h, v < nv);
     }
@@ -277,8 +294,11 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   const int NC = K / Q::CH;
   const int NIT = (NC + 63) / 64;          // k iterations of a group (a multiple of KW)
   const int NITW = NIT / KW;               // of them per wave
-  uint16_t* xp = (uint16_t*)smem;                 // [BT][K] fp16 in pair order
+  uint16_t* xp = (uint16_t*)smem;                 // [BT][K] fp16 in pair order (virtual rows)
   float* xsum = (float*)(smem + (BT * K) / 2);    // [BT][NC]
+  // split: the input is carried as an fp16 pair; virtual rows BT/2.. hold the remainders and the
+  // two partial totals of a row are added before the epilogue (the host guarantees BT >= 2)
+  const bool split = BT > 1 && (a.split_x || a.x_lo);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = a.w.n;
   const int n_groups = n_groups_of<EPI>(N);
@@ -328,17 +348,17 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     fetch(wa, 0);
     __builtin_amdgcn_sched_barrier(0);
-    prologue_compute<BITS, BT>(a, p, xp, xsum, red);
+    prologue_compute<BITS, BT>(a, p, xp, xsum, red, split);
   } else {
     PlainRegs<BT> p;
-    plain_load<BT>(a, p, 0);
+    plain_load<BT>(a, p, 0, split);
     __builtin_amdgcn_sched_barrier(0);
     fetch(wa, 0);
     __builtin_amdgcn_sched_barrier(0);
-    plain_stage<BITS, BT>(a, p, 0, xp, xsum);
+    plain_stage<BITS, BT>(a, p, 0, xp, xsum, split);
     for (int j0 = PlainVB<BT>::v; 256 * j0 < K / 8; j0 += PlainVB<BT>::v) {
-      plain_load<BT>(a, p, j0);
-      plain_stage<BITS, BT>(a, p, j0, xp, xsum);
+      plain_load<BT>(a, p, j0, split);
+      plain_stage<BITS, BT>(a, p, j0, xp, xsum, split);
     }
   }
   __syncthreads();
@@ -411,6 +431,11 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
       }
       __syncthreads();
       if (wave != 0) return;
+    }
+    if constexpr (BT > 1) {
+      if (split)
+#pragma unroll
+        for (int b = 0; b < BT / 2; ++b) t[b] = t[b] + t[b + BT / 2];
     }
     const int r = lane >> 3;
     if constexpr (EPI == GEMV_STORE) {
@@ -540,15 +565,21 @@ static hipError_t launch_bits(hipStream_t s, const GemvArgs& a) {
   using Q = QT<BITS>;
   const int K = a.w.k;
   auto lds_for = [&](int bt) { return (size_t)bt * K * 2 + (size_t)bt * (K / Q::CH) * 4; };
-  int bt = a.batch <= 1 ? 1 : a.batch <= 2 ? 2 : a.batch <= 4 ? 4 : 8;
-  while (bt > 1 && lds_for(bt) > 65536) bt >>= 1;
-  if (a.batch > bt) {
+  // a split input takes two virtual rows per row
+  const bool split = a.split_x || a.x_lo;
+  const int rows = split ? 2 * a.batch : a.batch;
+  int bt = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8;
+  while (bt > (split ? 2 : 1) && lds_for(bt) > 65536) bt >>= 1;
+  if (split && a.split_x && 2 * a.batch > bt) return hipErrorInvalidValue;   // prologue: one launch
+  if ((split ? 2 * a.batch : a.batch) > bt) {
+    const int per = split ? bt / 2 : bt;
     // split the batch into launches of at most bt rows (plain x input only)
     if (a.h_src) return hipErrorInvalidValue;
-    for (int b0 = 0; b0 < a.batch; b0 += bt) {
+    for (int b0 = 0; b0 < a.batch; b0 += per) {
       GemvArgs p = a;
-      p.batch = a.batch - b0 < bt ? a.batch - b0 : bt;
+      p.batch = a.batch - b0 < per ? a.batch - b0 : per;
       p.x = a.x + (size_t)b0 * a.ldx;
+      if (p.x_lo) p.x_lo = a.x_lo + (size_t)b0 * a.ldx;
       for (int i = 0; i < p.batch; ++i) p.conv_slot[i] = a.conv_slot[b0 + i];
       if (p.y) p.y = a.y + (size_t)b0 * a.ldy;
       if (p.yf) p.yf = a.yf + (size_t)b0 * a.ldy;
@@ -573,7 +604,7 @@ hipError_t launch_gemv(hipStream_t s, const GemvArgs& a) {
   if (a.w.k % 8 || (a.h_src && a.w.k > 256 * 8 * kVecBlocks)) return hipErrorInvalidValue;
   if (a.h_src ? ((uintptr_t)a.h_src % 16 || (a.m && (uintptr_t)a.m % 16) || (uintptr_t)a.w_pre % 16 ||
                  (a.w_post && (uintptr_t)a.w_post % 16))
-              : ((uintptr_t)a.x % 16 || a.ldx % 8))
+              : ((uintptr_t)a.x % 16 || a.ldx % 8 || (uintptr_t)a.x_lo % 16))
     return hipErrorInvalidValue;
   switch (a.w.bits) {
     case 4: return launch_bits<4>(s, a);

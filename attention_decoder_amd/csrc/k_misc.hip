@@ -134,11 +134,16 @@ __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
     if (!ok[j]) continue;
     const int k = 8 * ((int)threadIdx.x + 256 * j);
     float xv[8];
-    uint32_t xh[4];
+    uint32_t xh[4], xl[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) xv[e] = (hv[j][e] * rh) * wpr[j][e];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) xh[e] = (uint32_t)f2h_sep(xv[2 * e]) | ((uint32_t)f2h_sep(xv[2 * e + 1]) << 16);
+    for (int e = 0; e < 4; ++e) {
+      const f16_t h0 = f2h_sep(xv[2 * e]), h1 = f2h_sep(xv[2 * e + 1]);
+      xh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      xl[e] = (uint32_t)f2h_sep(sub_sep(xv[2 * e], h2f(h0))) | ((uint32_t)f2h_sep(sub_sep(xv[2 * e + 1], h2f(h1))) << 16);
+    }
+    if (a.x_lo) *(uint4*)(a.x_lo + base + k) = make_uint4(xl[0], xl[1], xl[2], xl[3]);
     if (a.m) store_f32x8(a.h_out + base + k, hv[j]);
     if (a.capture) store_f32x8(a.capture + base + k, hv[j]);
     if (a.x_copy) store_f32x8(a.x_copy + base + k, xv);

@@ -25,6 +25,7 @@ struct NormArgs {
   const bf16_t* w_pre;
   float* h_out;
   f16_t* x_out;
+  f16_t* x_lo;      // nullable: the fp16 remainder x - f16(x), so x_out + x_lo carries x to ~22 bits
   float* capture;
   float* x_copy;
   int rows, hidden;
@@ -91,7 +92,9 @@ enum GemvEpi { GEMV_STORE = 0, GEMV_SWIGLU = 1, GEMV_LOGITS = 2, GEMV_CONV = 3 }
 struct GemvArgs {
   QLinear w;
   const f16_t* x;   // [batch, ldx]
+  const f16_t* x_lo;  // nullable, [batch, ldx]: fp16 remainder of x (input carried as x + x_lo)
   int ldx;
+  int split_x;      // norm prologue: carry x as the fp16 pair x_hi + x_lo
   int batch;
   int epi;
   f16_t* y;
@@ -128,6 +131,7 @@ enum GemmEpi { GEMM_STORE = 0, GEMM_SWIGLU = 1 };
 struct GemmArgs {
   QLinear w;
   const f16_t* x;   // [M, ldx]
+  const f16_t* x_lo;  // nullable, [M, ldx]: fp16 remainder of x; Y = (x + x_lo) W as two K passes
   int ldx;
   int m;
   int epi;

@@ -152,7 +152,7 @@ bool check_config(const lfm3_config& c, std::string& err) {
 struct Layout {
   size_t cos_f, sin_f, cos_s, sin_s;
   size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
-  size_t h, h2, x, big, sbuf, mix, qrot, m, xf, part, keys, counters;
+  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, xf, part, keys, counters;
   size_t total;
   int max_rows, max_pages, ring_rows, max_splits, big_ld;
   size_t ring_layer, pool_layer, conv_slot;
@@ -190,6 +190,7 @@ Layout make_layout(const lfm3_config& c) {
   L.h = take(R * H * 4);
   L.h2 = take(R * H * 4);
   L.x = take(R * H * 2);
+  L.xlo = take(R * H * 2);
   L.big = take(R * L.big_ld * 4);
   L.sbuf = take(R * F * 2);
   L.mix = take(R * H * 2);
@@ -218,6 +219,7 @@ struct ProfRec {
   int kind;
   hipEvent_t a, b;
   double bytes, flops;
+  int64_t launches;
 };
 
 struct lfm3_ctx {
@@ -237,6 +239,7 @@ struct lfm3_ctx {
   std::string err;
   std::unordered_map<std::string, QLinear> lin_by_name;
   bool prof = false;
+  bool prof_open = false;    // the last record's run is still open (its end event not recorded)
   std::vector<ProfRec> prof_recs;
   std::vector<hipEvent_t> prof_pool;
   hipEvent_t ev() {
@@ -303,19 +306,36 @@ size_t blob_size_for(const lfm3_config& c) {
   return off;
 }
 
-// Launch `fn` (returning hipError_t); when profiling, bracket it with events.
+// Launch `fn` (returning hipError_t); when profiling, bracket it with events. A run of
+// consecutive launches of one family shares one event pair: the start event goes in before the
+// first launch and the end event after the last one (when a launch of another family comes, or
+// when the API call ends), so no event sits between two kernels of a run. Every launch of a step
+// goes through here, so a run never spans a kernel of another family.
+hipError_t prof_close(lfm3_ctx* ctx) {
+  if (!ctx->prof || !ctx->prof_open) return hipSuccess;
+  ctx->prof_open = false;
+  return hipEventRecord(ctx->prof_recs.back().b, ctx->stream);
+}
+
 template <class F>
 hipError_t timed(lfm3_ctx* ctx, int kind, double bytes, double flops, F fn) {
   if (!ctx->prof) return fn();
-  ProfRec r{kind, ctx->ev(), ctx->ev(), bytes, flops};
+  if (ctx->prof_open && ctx->prof_recs.back().kind == kind) {
+    ProfRec& r = ctx->prof_recs.back();
+    hipError_t e = fn();
+    if (e != hipSuccess) return e;
+    r.bytes += bytes; r.flops += flops; ++r.launches;
+    return hipSuccess;
+  }
+  hipError_t e = prof_close(ctx);
+  if (e != hipSuccess) return e;
+  ProfRec r{kind, ctx->ev(), ctx->ev(), bytes, flops, 1};
   if (!r.a || !r.b) return fn();
-  hipError_t e = hipEventRecord(r.a, ctx->stream);
+  e = hipEventRecord(r.a, ctx->stream);
   if (e != hipSuccess) return e;
-  e = fn();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(r.b, ctx->stream);
   ctx->prof_recs.push_back(r);
-  return e;
+  ctx->prof_open = true;
+  return fn();
 }
 
 double lin_bytes(const QLinear& w) {
@@ -360,14 +380,18 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
   f16_t* qrot = ctx->at<f16_t>(L.qrot);
   float* m = ctx->at<float>(L.m);
   f16_t* xf = ctx->at<f16_t>(L.xf);
+  f16_t* xlo = ctx->at<f16_t>(L.xlo);
 
   // fp32 output (STORE) or fp16 SwiGLU output
-  auto linear = [&](const QLinear& w, const f16_t* in, int ldin, float* outf, f16_t* outb, int ldout, int epi) -> hipError_t {
+  // x_lo: the input is carried as the fp16 pair in + x_lo (two K passes; counted as such)
+  auto linear = [&](const QLinear& w, const f16_t* in, int ldin, float* outf, f16_t* outb, int ldout, int epi,
+                    const f16_t* x_lo = nullptr) -> hipError_t {
     const double out_bytes = epi == GEMM_SWIGLU ? (double)M * (w.n / 2) * 2.0 : (double)M * w.n * 4.0;
-    const double bytes = lin_bytes(w) + (double)M * w.k * 2.0 + out_bytes;
-    const double flops = 2.0 * M * (double)w.n * w.k;
+    const double passes = x_lo ? 2.0 : 1.0;
+    const double bytes = lin_bytes(w) + passes * M * w.k * 2.0 + out_bytes;
+    const double flops = passes * 2.0 * M * (double)w.n * w.k;
     GemmArgs g{};
-    g.w = w; g.x = in; g.ldx = ldin; g.m = M; g.epi = epi; g.y = outb; g.yf = outf; g.ldy = ldout;
+    g.w = w; g.x = in; g.x_lo = x_lo; g.ldx = ldin; g.m = M; g.epi = epi; g.y = outb; g.yf = outf; g.ldy = ldout;
     return timed(ctx, LFM3_PROF_GEMM, bytes, flops, [&] { return launch_gemm(s, g); });
   };
   const double norm_bytes = (double)M * H * (4 + 4 + 4 + 2);
@@ -380,13 +404,13 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
     const LayerW& lw = ctx->layers[i];
     // h += post_ffn_norm(m) of the previous layer (if any); x = operator_norm(h)
     NormArgs na{};
-    na.h_in = h; na.h_out = h; na.x_out = x; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
+    na.h_in = h; na.h_out = h; na.x_out = x; na.x_lo = xlo; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
     na.w_pre = lw.op_norm;
     if (i > 0) { na.m = m; na.w_post = ctx->layers[i - 1].post_ffn; na.capture = cap(i - 1); }
     LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, na); }));
 
     if (lw.type == LFM3_LAYER_CONV) {
-      LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE));
+      LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE, xlo));
       ConvArgs ca{};
       ca.bcx = big; ca.ld = L.big_ld; ca.kernel = lw.conv_kernel;
       ca.state = ctx->at<f16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
@@ -395,7 +419,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
       LFM3_TRY(timed(ctx, LFM3_PROF_CONV, (double)M * H * (12 + 2) + 2.0 * H * 2 * (c.conv_taps - 1), 0,
                      [&] { return launch_conv(s, ca); }));
     } else {
-      LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE));
+      LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE, xlo));
       const bool full = lw.type == LFM3_LAYER_FULL;
       QkRopeArgs qa{};
       qa.qkvg = big; qa.ld = L.big_ld; qa.q_norm = lw.q_norm; qa.k_norm = lw.k_norm;
@@ -457,6 +481,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
   f16_t* mix = ctx->at<f16_t>(L.mix);
   float* m = ctx->at<float>(L.m);
   f16_t* xf = ctx->at<f16_t>(L.xf);
+  f16_t* xlo = ctx->at<f16_t>(L.xlo);
   const bool fuse = M <= 2;
   auto cap = [&](int layer) -> float* {
     if (!ctx->capture || layer < 0) return nullptr;
@@ -468,23 +493,26 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
                  [&] { return launch_gemv(s, g); });
   };
   // GEMV whose input is rmsnorm(cur [+ rmsnorm(m) * w_post]) * w_pre
+  // split: the normed input is carried as the fp16 pair x + x_lo (the operator-norm output, which
+  // feeds in_proj and qkvg); a fused split prologue handles one row
   auto normed_gemv = [&](GemvArgs& g, const bf16_t* w_post, const bf16_t* w_pre, float* capture, float* x_copy,
-                         double out_bytes) -> hipError_t {
+                         double out_bytes, bool split = false) -> hipError_t {
     g.batch = M;
-    if (fuse) {
+    if (fuse && (!split || M == 1)) {
       g.h_src = cur; g.m = w_post ? m : nullptr; g.w_post = w_post; g.w_pre = w_pre; g.eps = c.norm_eps;
-      g.h_dst = oth; g.capture = capture; g.capture_ld = H; g.x_copy = x_copy;
-      hipError_t e = gemv(g, out_bytes);
+      g.h_dst = oth; g.capture = capture; g.capture_ld = H; g.x_copy = x_copy; g.split_x = split;
+      hipError_t e = gemv(g, out_bytes + (split ? (double)M * H * 2 : 0.0));
       if (w_post) std::swap(cur, oth);
       return e;
     }
     NormArgs na{};
     na.h_in = cur; na.h_out = cur; na.m = w_post ? m : nullptr; na.w_post = w_post; na.w_pre = w_pre;
-    na.x_out = x; na.capture = capture; na.x_copy = x_copy; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
+    na.x_out = x; na.x_lo = split ? xlo : nullptr;
+    na.capture = capture; na.x_copy = x_copy; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
     hipError_t e = timed(ctx, LFM3_PROF_NORM, (double)M * H * 14, 0, [&] { return launch_resid_norm(s, na); });
     if (e != hipSuccess) return e;
-    g.x = x; g.ldx = H;
-    return gemv(g, out_bytes);
+    g.x = x; g.x_lo = na.x_lo; g.ldx = H;
+    return gemv(g, out_bytes + (split ? (double)M * H * 2 : 0.0));
   };
 
   for (int i = 0; i < c.n_layers; ++i) {
@@ -498,11 +526,11 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
       g.conv_slot_stride = (int64_t)L.conv_slot;
       g.conv_taps = c.conv_taps;
       for (int b = 0; b < M; ++b) g.conv_slot[b] = rows.slot[b];
-      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * H * (2 + 4 * (c.conv_taps - 1))));
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * H * (2 + 4 * (c.conv_taps - 1)), true));
     } else {
       GemvArgs g{};
       g.w = lw.mix_in; g.epi = GEMV_STORE; g.yf = big; g.ldy = L.big_ld;
-      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4));
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4, true));
       const bool full = lw.type == LFM3_LAYER_FULL;
       AttnDecodeArgs aa{};
       aa.qkvg = big; aa.ld = L.big_ld; aa.gate_col = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
@@ -545,7 +573,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     g.w = ctx->emb; g.epi = GEMV_LOGITS; g.logits = logits; g.ld_logits = c.vocab;
     g.keys = ctx->at<uint64_t>(L.keys);
     LFM3_TRY(normed_gemv(g, last_post, ctx->emb_norm, cap(c.n_layers - 1), hidden_out, logits ? (double)M * c.vocab * 4 : 0.0));
-    LFM3_TRY(launch_argmax_finalize(s, g.keys, ids, M));
+    LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, 12.0 * M, 0, [&] { return launch_argmax_finalize(s, g.keys, ids, M); }));
   } else {
     NormArgs nf{};
     nf.h_in = cur; nf.h_out = cur; nf.x_out = xf; nf.rows = M; nf.hidden = H; nf.eps = c.norm_eps;
@@ -564,7 +592,7 @@ lfm3_status head(lfm3_ctx* ctx, const f16_t* xrows, int n, float* logits, int32_
   g.logits = logits; g.ld_logits = ctx->cfg.vocab; g.keys = ctx->at<uint64_t>(ctx->L.keys);
   const double bytes = lin_bytes(g.w) + (double)n * g.w.k * 2 + (logits ? (double)n * g.w.n * 4 : 0.0);
   LFM3_TRY(timed(ctx, LFM3_PROF_GEMV, bytes, 2.0 * n * g.w.n * g.w.k, [&] { return launch_gemv(ctx->stream, g); }));
-  LFM3_TRY(launch_argmax_finalize(ctx->stream, g.keys, ids, n));
+  LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, 12.0 * n, 0, [&] { return launch_argmax_finalize(ctx->stream, g.keys, ids, n); }));
   return LFM3_OK;
 }
 
@@ -590,8 +618,8 @@ lfm3_status commit_pages(lfm3_ctx* ctx, int slot, int new_len) {
     ctx->free_pages.pop_back();
   }
   if ((int)pg.size() > first) {
-    LFM3_TRY(launch_set_pages(ctx->stream, ctx->at<int32_t>(ctx->L.page_table), slot * ctx->L.max_pages + first,
-                              (int)pg.size() - first, pg.data() + first));
+    LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, 8.0 * (need - first), 0, [&] { return launch_set_pages(ctx->stream, ctx->at<int32_t>(ctx->L.page_table), slot * ctx->L.max_pages + first,
+                              (int)pg.size() - first, pg.data() + first); }));
   }
   return LFM3_OK;
 }
@@ -757,7 +785,8 @@ lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
     Rows rows{};
     rows.n = M; rows.mode = 0; rows.slot0 = slot; rows.pos0 = ctx->len[slot];
     if (tokens_dev) {
-      LFM3_TRY(launch_embed(ctx->stream, ctx->emb, tokens_dev + r0, M, h));
+      LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, (double)M * (lin_bytes(ctx->emb) / ctx->emb.n + 4.0 * c.hidden), 0,
+                     [&] { return launch_embed(ctx->stream, ctx->emb, tokens_dev + r0, M, h); }));
     } else {
       LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev + (size_t)r0 * H, M, H, h));
     }
@@ -769,6 +798,7 @@ lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
       if (st != LFM3_OK) return st;
     }
   }
+  LFM3_TRY(prof_close(ctx));
   return LFM3_OK;
 }
 
@@ -803,13 +833,15 @@ lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_hos
   }
   float* h = ctx->at<float>(ctx->L.h);
   if (tokens_dev) {
-    LFM3_TRY(launch_embed(ctx->stream, ctx->emb, tokens_dev, n, h));
+    LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, (double)n * (lin_bytes(ctx->emb) / ctx->emb.n + 4.0 * c.hidden), 0,
+                   [&] { return launch_embed(ctx->stream, ctx->emb, tokens_dev, n, h); }));
   } else {
     LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev, n, c.hidden, h));
   }
   lfm3_status st = run_decode(ctx, rows, hidden_out_dev, logits_dev, argmax_dev);
   if (st != LFM3_OK) return st;
   for (int b = 0; b < n; ++b) ctx->len[slots_host[b]] += 1;
+  LFM3_TRY(prof_close(ctx));
   return LFM3_OK;
 }
 
@@ -887,6 +919,7 @@ lfm3_status lfm3_profile(lfm3_ctx* ctx, int32_t enable) {
   if (hipStreamSynchronize(ctx->stream) != hipSuccess) return ctx->fail(LFM3_ERR_DEVICE, "stream sync failed");
   for (auto& r : ctx->prof_recs) { ctx->prof_pool.push_back(r.a); ctx->prof_pool.push_back(r.b); }
   ctx->prof_recs.clear();
+  ctx->prof_open = false;
   ctx->prof = enable != 0;
   return LFM3_OK;
 }
@@ -901,7 +934,7 @@ lfm3_status lfm3_profile_read(lfm3_ctx* ctx, int32_t kind, double* total_ms, int
     if (r.kind != kind) continue;
     float t = 0;
     if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return ctx->fail(LFM3_ERR_DEVICE, "event timing failed");
-    ms += t; by += r.bytes; fl += r.flops; ++n;
+    ms += t; by += r.bytes; fl += r.flops; n += r.launches;
   }
   if (total_ms) *total_ms = ms;
   if (launches) *launches = n;

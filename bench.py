@@ -40,7 +40,7 @@ def main():
     ap.add_argument("--decode", type=int, default=256)
     ap.add_argument("--no-extras", action="store_true", help="skip the 8-stream decode and 8k prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=48, help="oracle decode steps timed for cpu_baseline")
+    ap.add_argument("--cpu-steps", type=int, default=192, help="oracle decode steps timed for cpu_baseline")
     ap.add_argument("--profile-only", action="store_true", help="one short step for rocprofv3 runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --profile-only: also run three 256 MiB device copies (the reference kernel that "
@@ -193,9 +193,8 @@ def gemv_traffic():
     return rec["traffic_bytes_per_launch"]
 
 
-def run_extras(eng, synth, torch, dev):
-    out = {}
-    # 8 concurrent streams: prompts U[300, 2960] (untimed prefill), then 128 greedy steps at B = 8
+def decode_8stream(eng, synth, torch, dev):
+    """8 concurrent streams: prompts U[300, 2960] (untimed prefill), then 128 greedy steps at B = 8."""
     lens = synth.stream_prompt_lengths(4, 8)
     prompts = synth.stream_prompts(4, lens)
     for i in range(8):
@@ -214,10 +213,11 @@ def run_extras(eng, synth, torch, dev):
     e1.record(eng.stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    out["decode_8stream_tok_s"] = round(8 * (n_steps - 1) / (ms / 1e3), 1)
-    out["decode_8stream_prompt_lengths"] = [int(x) for x in lens]
-    log(f"8-stream decode {out['decode_8stream_tok_s']} tok/s")
-    # 8192-token prefill in four 2048-row passes (weights resident; median of 3)
+    return round(8 * (n_steps - 1) / (ms / 1e3), 1), [int(x) for x in lens]
+
+
+def prefill_8k(eng, synth, torch, dev):
+    """8192-token prefill in four 2048-row passes (weights resident; median of 3): (tok/s, ms)."""
     toks = torch.from_numpy(synth.prompt_tokens(5, 8192)).to(dev)
     times = []
     for r in range(4):
@@ -231,7 +231,15 @@ def run_extras(eng, synth, torch, dev):
         if r > 0:
             times.append(a.elapsed_time(b))
     ms = float(np.median(times))
-    out["prefill_8k_tok_s"] = round(8192 / (ms / 1e3), 1)
+    return round(8192 / (ms / 1e3), 1), ms, toks
+
+
+def run_extras(eng, synth, torch, dev, schemes=True):
+    from attention_decoder_amd.lfm3 import Engine
+    out = {}
+    out["decode_8stream_tok_s"], out["decode_8stream_prompt_lengths"] = decode_8stream(eng, synth, torch, dev)
+    log(f"8-stream decode {out['decode_8stream_tok_s']} tok/s")
+    out["prefill_8k_tok_s"], ms, toks = prefill_8k(eng, synth, torch, dev)
     out["prefill_8k_ms"] = round(ms, 3)
     # MFMA fraction of the prefill GEMM on the same workload
     eng.reset(0)
@@ -249,6 +257,18 @@ def run_extras(eng, synth, torch, dev):
     total_flops = sum(v["flops"] for v in prof.values()) + 2.0 * 128000 * 2048
     out["prefill_8k_frac_of_f16_peak"] = round(total_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
     log(f"8k prefill {out['prefill_8k_tok_s']} tok/s ({ms:.2f} ms); {out['prefill_8k_breakdown_ms']}")
+    if schemes:
+        # the same two workloads at the 8-bit (8 streams) and 6-bit (8k prefill) schemes
+        for bits, key in [(8, "q8"), (6, "q6")]:
+            cfg = synth.full_config(bits=bits, group=64, max_slots=8, max_ctx=8704, max_chunk=2048)
+            e2 = Engine(cfg, synth.cached_blob(cfg, seed=0))
+            if bits == 8:
+                out["q8_decode_8stream_tok_s"], _ = decode_8stream(e2, synth, torch, dev)
+                log(f"q8 8-stream decode {out['q8_decode_8stream_tok_s']} tok/s")
+            else:
+                out["q6_prefill_8k_tok_s"], ms6, _ = prefill_8k(e2, synth, torch, dev)
+                log(f"q6 8k prefill {out['q6_prefill_8k_tok_s']} tok/s ({ms6:.2f} ms)")
+            e2.close()
     return out
 
 

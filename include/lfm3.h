@@ -162,12 +162,14 @@ lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uin
 
 /*
  * Kernel-family timing for roofline figures. lfm3_profile(ctx, 1) starts recording: every later
- * launch of a family is bracketed by HIP events on the context's stream and tagged with the
- * algorithmic bytes and flops it implies (weights + activations read and written; 2*M*N*K for a
- * linear; 4*128*heads per visible key for attention). lfm3_profile(ctx, 0) stops; either call
- * drops earlier records. lfm3_profile_read synchronises the stream and returns, for one family,
- * the summed event time (ms), the launch count and the summed bytes and flops. Any output may be
- * NULL. The events cost a little time, so throughput is measured with recording off.
+ * launch is tagged with its family and the algorithmic bytes and flops it implies (weights +
+ * activations read and written; 2*M*N*K for a linear; 4*128*heads per visible key for
+ * attention), and each run of consecutive launches of one family is bracketed by one pair of HIP
+ * events on the context's stream (so the time is back-to-back kernel execution, with no event
+ * between two kernels of a run). lfm3_profile(ctx, 0) stops; either call drops earlier records.
+ * lfm3_profile_read synchronises the stream and returns, for one family, the summed event time
+ * (ms), the launch count and the summed bytes and flops. Any output may be NULL. Recording adds
+ * an event pair per run, so throughput is measured with recording off.
  */
 enum {
   LFM3_PROF_GEMV = 0,          /* decode dequant-GEMV (linears and the tied head)   */
@@ -176,7 +178,7 @@ enum {
   LFM3_PROF_ATTN_PREFILL = 3,  /* flash prefill attention                           */
   LFM3_PROF_CONV = 4,          /* gated short conv                                  */
   LFM3_PROF_NORM = 5,          /* residual + RMSNorm                                */
-  LFM3_PROF_OTHER = 6,         /* q/k norm + RoPE + KV store                        */
+  LFM3_PROF_OTHER = 6,         /* q/k norm + RoPE + KV store, embedding, argmax, page table */
   LFM3_PROF_KINDS = 7
 };
 lfm3_status lfm3_profile(lfm3_ctx* ctx, int32_t enable);

@@ -273,10 +273,18 @@ class Oracle:
 
     def _r(self, x):
         """Storage diagnostic mode (off by default; parity is judged against plain float64): round
-        to fp16 where the GPU stores fp16 -- every matmul input (the normed rows, the conv's z and
+        to fp16 where the GPU stores fp16 -- the matmul inputs (the ffn-norm rows, the conv's z and
         C*y, the gated attention output, the SwiGLU product), the cached k and v, and the conv
         state. Linear outputs and the residual stream stay wide."""
         return f16_round(x) if self.storage else x
+
+    def _r2(self, x):
+        """Storage diagnostic for a value the GPU carries as an fp16 pair (the operator-norm output
+        feeding in_proj and qkvg): the high part and the rounded remainder."""
+        if not self.storage:
+            return x
+        hi = f16_round(x)
+        return hi + f16_round(x - hi)
 
     # layers ---------------------------------------------------------------------------------
     def _conv_mixer(self, i, st, u):
@@ -355,7 +363,7 @@ class Oracle:
         pos = np.arange(st.length, st.length + m)
         layers = []
         for i, lt in enumerate(c["layer_type"]):
-            u = self._r(rmsnorm(h, self.blob.bf16(f"layers.{i}.operator_norm"), eps))
+            u = self._r2(rmsnorm(h, self.blob.bf16(f"layers.{i}.operator_norm"), eps))
             if lt == LT_CONV:
                 mo = self._conv_mixer(i, st, u)
             else:
