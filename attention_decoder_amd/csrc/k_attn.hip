@@ -194,19 +194,28 @@ hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// decode: block (split of 64 keys, kv head, row). The prologue normalises and rotates the block's 4
-// query heads from the raw qkvg row; the block whose split holds the current position also forms
-// its key and value (per-head k RMSNorm + RoPE) and stores them in the cache. Scores: 16 lanes per
-// key row (8 dims each, coalesced), 4 keys per wave step; softmax per head over the split; P V
-// with one V row per wave step. Partials (max, sum, o) go to scratch; the last block of a (row,
-// kv head) to finish merges them, applies the sigmoid gate and stores fp16 -- one launch.
+// decode: block (split, kv head, row); a split is split_keys consecutive visible keys (a multiple
+// of 64), walked in 64-key tiles with an online softmax, the next tile's K/V loads (and the page
+// ids of the one after) in flight while a tile is computed. The prologue normalises and rotates
+// the block's 4 query heads from the raw qkvg row; the block whose split holds the current
+// position also forms its key and value (per-head k RMSNorm + RoPE) and stores them in the cache.
+// Scores: 4 lanes per key (32 dims each, summed by DPP); wave w is query head 4 kvh + w for the
+// softmax and P V (lane = 2 dims). One split: the block writes the gated output. Several: partials
+// (max, sum, o) go to the workspace and the last block of a (row, kv head) to finish merges them,
+// with every partial load issued at once.
 // ---------------------------------------------------------------------------------------------
 
-constexpr int SPLIT = 64;
+constexpr int TILE = 64;
 constexpr int KVS = kHeadDim + 8;   // LDS row stride of the K and V tiles (elements)
-int attn_decode_split_keys() { return SPLIT; }
+constexpr int kMaxMergeSplits = 512;
+constexpr int kFullSplitKeys = 128;  // keys per split on full layers (2 tiles)
 
-constexpr int kMaxMergeSplits = 512;   // 512 x 64 keys: contexts up to 32768
+// Sliding layers (<= window keys) split into single tiles, so all four 64-key tiles of a 256-key
+// window run in parallel blocks; full layers use 2-tile splits (fewer partials to merge).
+int attn_decode_split_keys(bool sliding, int window) {
+  (void)window;
+  return sliding ? TILE : kFullSplitKeys;
+}
 
 template <bool PAGED>
 LFM3_DEV size_t kv_off(const KvRef& kv, int slot, int pos, int page, int kvh, int n_kv) {
@@ -216,144 +225,168 @@ LFM3_DEV size_t kv_off(const KvRef& kv, int slot, int pos, int page, int kvh, in
 
 template <bool PAGED>
 __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) f16_t kt[(SPLIT + 1) * KVS];
-  __shared__ __attribute__((aligned(16))) f16_t vt[(SPLIT + 1) * KVS];
+  __shared__ __attribute__((aligned(16))) f16_t kt[(TILE + 1) * KVS];   // row TILE: spare (unused keys)
+  __shared__ __attribute__((aligned(16))) f16_t vt[(TILE + 1) * KVS];
   __shared__ float qs[kQPerKv][kHeadDim];
-  __shared__ float sc[kQPerKv][SPLIT];
+  __shared__ float sc[kQPerKv][TILE];
+  __shared__ __attribute__((aligned(16))) f16_t knew[kHeadDim], vnew[kHeadDim];
   __shared__ int is_last;
   const int split = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int slot = a.rows.slot[r], pos = a.rows.pos[r];
   const int nq = a.n_q_heads, nkv = a.n_kv_heads;
+  const int SK = a.split_keys;
   const int k_lo = a.window > 0 ? max(0, pos - (a.window - 1)) : 0;
-  const int ns = (pos - k_lo) / SPLIT + 1;
+  const int ns = (pos - k_lo) / SK + 1;
   if (split >= ns) return;
-  const int j0 = k_lo + split * SPLIT;
-  const int nk = min(SPLIT, pos - j0 + 1);
+  const int j0 = k_lo + split * SK;
+  const int j_end = min(pos, j0 + SK - 1);          // last key of the split
+  const int n_tiles = (j_end - j0) / TILE + 1;
   const bool has_new = split == ns - 1;   // the current position is this split's last key
   const int32_t* pt = PAGED ? a.kv.page_table + (size_t)slot * a.kv.max_pages : nullptr;
 
-  // 1. K/V tile loads, branch-free: thread t loads 16-byte chunks t + 256 q (q < 4) of the
-  //    64 key x 16 chunk tile for K and V; keys past the split load the split's last key (not
-  //    stored), the current position's row is replaced by the freshly formed key and value.
-  int jq[4], pg[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    jq[q] = j0 + min(((tid + 256 * q) >> 4), nk - 1);
-    pg[q] = PAGED ? pt[jq[q] / kPageTokens] : 0;
-  }
+  // tile loads, branch-free: thread t moves 16-byte chunks t + 256 q (q < 4) of the 64 key x 16
+  // chunk tile; keys past the split read the split's last key (not used)
+  auto key_of = [&](int tile, int q) { return min(j0 + tile * TILE + ((tid + 256 * q) >> 4), j_end); };
+  int pg[4], pgn[4];
   u32x4_v kr[4], vr[4];
 #pragma unroll
+  for (int q = 0; q < 4; ++q) pg[q] = PAGED ? pt[key_of(0, q) / kPageTokens] : 0;
+  // the step's own query row (issued with the page ids: independent loads)
+  const float* row = a.qkvg + (size_t)r * a.ld;
+  const int hq = kvh * kQPerKv + wave;
+  const float c = a.cos_t[(size_t)pos * kHalfDim + lane];
+  const float sn = a.sin_t[(size_t)pos * kHalfDim + lane];
+  const float x0 = row[(size_t)hq * kHeadDim + lane], x1 = row[(size_t)hq * kHeadDim + lane + kHalfDim];
+  const float qn0 = bf2f(a.q_norm[lane]), qn1 = bf2f(a.q_norm[lane + kHalfDim]);
+  // new key (wave 0) / value (wave 1) inputs
+  const float* nrow = row + (size_t)(wave == 0 ? nq + kvh : nq + nkv + kvh) * kHeadDim;
+  const float y0 = nrow[lane], y1 = nrow[lane + kHalfDim];
+  const float kn0 = bf2f(a.k_norm[lane]), kn1 = bf2f(a.k_norm[lane + kHalfDim]);
+  const float graw = row[a.gate_col + hq];
+#pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const size_t o = kv_off<PAGED>(a.kv, slot, jq[q], pg[q], kvh, nkv) + 8 * ((tid + 256 * q) & 15);
+    const size_t o = kv_off<PAGED>(a.kv, slot, key_of(0, q), pg[q], kvh, nkv) + 8 * ((tid + 256 * q) & 15);
     kr[q] = *(const u32x4_v*)(a.kv.k + o);
     vr[q] = *(const u32x4_v*)(a.kv.v + o);
   }
-  // 2. query heads 4 kvh + w (wave w), and the step's own key and value (per-head k RMSNorm +
-  //    RoPE, "LFM3-1.7B port": partial RoPE on the full layers); lane holds dims lane, lane + 64
-  const float* row = a.qkvg + (size_t)r * a.ld;
-  const float c = a.cos_t[(size_t)pos * kHalfDim + lane];
-  const float sn = a.sin_t[(size_t)pos * kHalfDim + lane];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pgn[q] = PAGED ? pt[key_of(1, q) / kPageTokens] : 0;
+
+  // q heads 4 kvh + w (wave w): per-head RMSNorm + RoPE ("LFM3-1.7B port": partial RoPE on the
+  // full layers); lane holds dims lane, lane + 64; q rounded to fp16 as the prefill path stores it
   {
-    const int h = kvh * kQPerKv + wave;
-    const float x0 = row[(size_t)h * kHeadDim + lane], x1 = row[(size_t)h * kHeadDim + lane + kHalfDim];
     const float rr = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)kHeadDim + a.eps);
-    const float n0 = x0 * rr * bf2f(a.q_norm[lane]), n1 = x1 * rr * bf2f(a.q_norm[lane + kHalfDim]);
-    // q is rounded to fp16 as the prefill path stores it
+    const float n0 = x0 * rr * qn0, n1 = x1 * rr * qn1;
     qs[wave][lane] = h2f(f2h(n0 * c - n1 * sn));
     qs[wave][lane + kHalfDim] = h2f(f2h(n1 * c + n0 * sn));
   }
   if (has_new && wave < 2) {
     float o0, o1;
     if (wave == 0) {
-      const float* kp = row + (size_t)(nq + kvh) * kHeadDim;
-      const float x0 = kp[lane], x1 = kp[lane + kHalfDim];
-      const float rr = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)kHeadDim + a.eps);
-      const float n0 = x0 * rr * bf2f(a.k_norm[lane]), n1 = x1 * rr * bf2f(a.k_norm[lane + kHalfDim]);
+      const float rr = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)kHeadDim + a.eps);
+      const float n0 = y0 * rr * kn0, n1 = y1 * rr * kn1;
       o0 = n0 * c - n1 * sn;
       o1 = n1 * c + n0 * sn;
     } else {
-      const float* vp = row + (size_t)(nq + nkv + kvh) * kHeadDim;
-      o0 = vp[lane];
-      o1 = vp[lane + kHalfDim];
+      o0 = y0;
+      o1 = y1;
     }
     const int page = PAGED ? pt[pos / kPageTokens] : 0;
     f16_t* dst = (wave == 0 ? a.kv.k : a.kv.v) + kv_off<PAGED>(a.kv, slot, pos, page, kvh, nkv);
     const f16_t h0 = f2h(o0), h1 = f2h(o1);
     dst[lane] = h0;
     dst[lane + kHalfDim] = h1;
-    f16_t* t = (wave == 0 ? kt : vt) + (nk - 1) * KVS;
+    f16_t* t = wave == 0 ? knew : vnew;
     t[lane] = h0;
     t[lane + kHalfDim] = h1;
   }
-  // 3. tiles to LDS (the current position's row came from step 2); keys past the split and the
-  //    current position go to the spare row SPLIT, so the stores are unconditional
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int idx = tid + 256 * q, key = idx >> 4, c8 = idx & 15;
-    const int row_l = (key < nk && j0 + key != pos) ? key : SPLIT;
-    *(u32x4_v*)(kt + row_l * KVS + 8 * c8) = kr[q];
-    *(u32x4_v*)(vt + row_l * KVS + 8 * c8) = vr[q];
-  }
-  __syncthreads();
-  // 4. scores: thread -> key t / 4, dims [32 (t % 4), + 32) for the 4 heads; sum over 4 lanes
+
   const float scale = 0.08838834764831845f;
-  {
-    const int key = tid >> 2, qd = tid & 3;
-    float d[kQPerKv] = {0.f, 0.f, 0.f, 0.f};
-    const f16_t* kp = kt + key * KVS + 32 * qd;
-#pragma unroll
-    for (int e8 = 0; e8 < 4; ++e8) {
-      const uint4 v = *(const uint4*)(kp + 8 * e8);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kf = h2f((f16_t)((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu)));
-#pragma unroll
-        for (int hh = 0; hh < kQPerKv; ++hh) d[hh] = fmaf(qs[hh][32 * qd + 8 * e8 + e], kf, d[hh]);
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < kQPerKv; ++hh) {
-      d[hh] += dpp_mov<0xb1>(d[hh]);
-      d[hh] += dpp_mov<0x4e>(d[hh]);
-    }
-    if (qd == 0)
-#pragma unroll
-      for (int hh = 0; hh < kQPerKv; ++hh) sc[hh][key] = key < nk ? d[hh] * scale : -__builtin_huge_valf();
-  }
-  __syncthreads();
-  // 5. wave w = head 4 kvh + w: softmax over the split (lane = key), then P V over the tile with
-  //    lane holding dims 2 lane, 2 lane + 1
-  const float v_ = sc[wave][lane];
-  const float mx = warp_max(v_);
-  const float p = v_ == -__builtin_huge_valf() ? 0.f : __expf(v_ - mx);
-  const float l = wave_sum(p);
-  sc[wave][lane] = p;
-  __syncthreads();
-  float o0 = 0.f, o1 = 0.f;
-  for (int kk = 0; kk < nk; ++kk) {
-    const float pk = sc[wave][kk];
-    const uint32_t vv = *(const uint32_t*)(vt + kk * KVS + 2 * lane);
-    o0 = fmaf(pk, h2f((f16_t)(vv & 0xffffu)), o0);
-    o1 = fmaf(pk, h2f((f16_t)(vv >> 16)), o1);
-  }
-  const int h = kvh * kQPerKv + wave;
+  float m_run = -__builtin_huge_valf(), l_run = 0.f, o0 = 0.f, o1 = 0.f;
   const int d0 = 2 * lane;
-  const float gate = sigmoidf_(row[a.gate_col + h]);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int tj = j0 + tile * TILE;
+    const int nk = min(TILE, j_end - tj + 1);
+    // 1. the tile into LDS: keys past the split and the current position go to the spare row,
+    //    the current position's row comes from knew / vnew
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q, key = idx >> 4, c8 = idx & 15;
+      const int row_l = (key < nk && tj + key != pos) ? key : TILE;
+      *(u32x4_v*)(kt + row_l * KVS + 8 * c8) = kr[q];
+      *(u32x4_v*)(vt + row_l * KVS + 8 * c8) = vr[q];
+    }
+    if (has_new && pos >= tj && pos < tj + TILE && tid < 32) {
+      const int kk = pos - tj;
+      if (tid < 16) *(u32x4_v*)(kt + kk * KVS + 8 * tid) = *(const u32x4_v*)(knew + 8 * tid);
+      else *(u32x4_v*)(vt + kk * KVS + 8 * (tid - 16)) = *(const u32x4_v*)(vnew + 8 * (tid - 16));
+    }
+    __syncthreads();
+    // 2. the next tile's loads (clamped past the split: valid keys, unused), page ids one further
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const size_t o = kv_off<PAGED>(a.kv, slot, key_of(tile + 1, q), pgn[q], kvh, nkv) + 8 * ((tid + 256 * q) & 15);
+      kr[q] = *(const u32x4_v*)(a.kv.k + o);
+      vr[q] = *(const u32x4_v*)(a.kv.v + o);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pgn[q] = PAGED ? pt[key_of(tile + 2, q) / kPageTokens] : 0;
+    // 3. scores: thread -> key t / 4, dims [32 (t % 4), + 32) for the 4 heads; sum over 4 lanes
+    {
+      const int key = tid >> 2, qd = tid & 3;
+      float d[kQPerKv] = {0.f, 0.f, 0.f, 0.f};
+      const f16_t* kp = kt + key * KVS + 32 * qd;
+#pragma unroll
+      for (int e8 = 0; e8 < 4; ++e8) {
+        const u32x4_v v = *(const u32x4_v*)(kp + 8 * e8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kf = h2f((f16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu)));
+#pragma unroll
+          for (int hh = 0; hh < kQPerKv; ++hh) d[hh] = fmaf(qs[hh][32 * qd + 8 * e8 + e], kf, d[hh]);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < kQPerKv; ++hh) {
+        d[hh] += dpp_mov<0xb1>(d[hh]);
+        d[hh] += dpp_mov<0x4e>(d[hh]);
+      }
+      if (qd == 0)
+#pragma unroll
+        for (int hh = 0; hh < kQPerKv; ++hh) sc[hh][key] = key < nk ? d[hh] * scale : -__builtin_huge_valf();
+    }
+    __syncthreads();
+    // 4. online softmax for head `wave` over the tile (lane = key), then P V with lane = 2 dims
+    const float v_ = sc[wave][lane];
+    const float m_new = fmaxf(m_run, warp_max(v_));        // finite: every tile has a visible key
+    const float alpha = __expf(m_run - m_new);
+    const float p = v_ == -__builtin_huge_valf() ? 0.f : __expf(v_ - m_new);
+    l_run = l_run * alpha + wave_sum(p);
+    m_run = m_new;
+    sc[wave][lane] = p;   // each wave rewrites only its own head's row, read back by itself
+    o0 *= alpha;
+    o1 *= alpha;
+    for (int kk = 0; kk < nk; ++kk) {
+      const float pk = sc[wave][kk];
+      const uint32_t vv = *(const uint32_t*)(vt + kk * KVS + d0);
+      o0 = fmaf(pk, h2f((f16_t)(vv & 0xffffu)), o0);
+      o1 = fmaf(pk, h2f((f16_t)(vv >> 16)), o1);
+    }
+  }
+  const int h = hq;
+  const float gate = sigmoidf_(graw);
   f16_t* out = a.out + (size_t)r * nq * kHeadDim + (size_t)h * kHeadDim;
   if (ns == 1) {
-    const float inv = gate / l;
-    out[d0] = f2h(o0 * inv);
-    out[d0 + 1] = f2h(o1 * inv);
+    const float inv = gate / l_run;
+    *(uint32_t*)(out + d0) = pack_h2(o0 * inv, o1 * inv);
     return;
   }
-  // 6. partials; the last block of this (row, kv head) merges them
-  constexpr int PS = kHeadDim + 2;
-  float* part = a.part + (((size_t)r * nq + h) * a.max_splits + split) * PS;
-  if (lane == 0) { part[0] = mx; part[1] = l; }
-  part[2 + d0] = o0;
-  part[2 + d0 + 1] = o1;
+  // 5. partials [o (128) | max | sum | pad]; the last block of this (row, kv head) merges them
+  float* part = a.part + (((size_t)r * nq + h) * a.max_splits + split) * kPartStride;
+  if (lane == 0) { part[kHeadDim] = m_run; part[kHeadDim + 1] = l_run; }
+  *(float2*)(part + d0) = make_float2(o0, o1);
   __threadfence();
   __syncthreads();
   if (tid == 0) {
@@ -365,54 +398,59 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
   __syncthreads();
   if (!is_last) return;
   __threadfence();
-  // merge, wave = head: split statistics spread over lanes (branch-free clamped loads), the
-  // weights go through LDS (reusing the score buffer area), then the o sums over splits
-  float* wbuf = reinterpret_cast<float*>(kt) + wave * kMaxMergeSplits;   // 4 x 512 floats fit in kt
-  const float* ph = a.part + ((size_t)r * nq + h) * a.max_splits * PS;
-  float gmx = -__builtin_huge_valf();
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s2 = min(s0 + lane, ns - 1);
-    gmx = fmaxf(gmx, ph[(size_t)s2 * PS]);
-  }
-  gmx = warp_max(gmx);
-  float lt = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s2 = min(s0 + lane, ns - 1);
-    const float pm = ph[(size_t)s2 * PS];
-    const float pl = ph[(size_t)s2 * PS + 1];
-    const float w = (s0 + lane < ns && pm != -__builtin_huge_valf()) ? __expf(pm - gmx) : 0.f;
-    if (s0 + lane < ns) wbuf[s0 + lane] = w;
-    lt += w * pl;
-  }
-  lt = wave_sum(lt);
-  __syncthreads();
-  float a0 = 0.f, a1 = 0.f;
-  int s2 = 0;
-  for (; s2 + 8 <= ns; s2 += 8) {
-    float2 ov[8];
+  // merge, wave = head, in batches of 32 splits with every load of a batch issued at once:
+  // lanes 0-31 hold the statistics of split s0 + lane; for o, lanes 0-31 take the even splits of
+  // the batch and lanes 32-63 the odd ones, 4 dims each (lane % 32)
+  float* wbuf = reinterpret_cast<float*>(kt) + wave * 32;   // 4 x 32 floats in the K tile area
+  const float* ph = a.part + ((size_t)r * nq + h) * a.max_splits * kPartStride;
+  const int half = lane >> 5, dq = 4 * (lane & 31);
+  float gmx = -__builtin_huge_valf(), lt = 0.f;
+  float a4[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int CH = 16;   // splits per lane half per batch
+  for (int s0 = 0; s0 < ns; s0 += 2 * CH) {
+    const int sS = s0 + (lane & 31);
+    const float pm = ph[(size_t)min(sS, ns - 1) * kPartStride + kHeadDim];
+    const float pl = ph[(size_t)min(sS, ns - 1) * kPartStride + kHeadDim + 1];
+    float4 ov[CH];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) ov[u] = *(const float2*)(ph + (size_t)(s2 + u) * PS + 2 + d0);
+    for (int u = 0; u < CH; ++u) ov[u] = *(const float4*)(ph + (size_t)min(s0 + 2 * u + half, ns - 1) * kPartStride + dq);
+    const bool real = sS < ns;
+    const float bm = warp_max(real ? pm : -__builtin_huge_valf());
+    const float gnew = fmaxf(gmx, bm);
+    const float resc = __expf(gmx - gnew);
+    const float w = (real && lane < 32) ? __expf(pm - gnew) : 0.f;
+    if (lane < 32) wbuf[lane] = w;
+    lt = lt * resc + wave_sum(w * pl);
+    gmx = gnew;
+    // wbuf is written and read by this wave only; LDS operations of a wave stay in order
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float w = wbuf[s2 + u];
-      a0 = fmaf(w, ov[u].x, a0);
-      a1 = fmaf(w, ov[u].y, a1);
+    for (int e = 0; e < 4; ++e) a4[e] *= resc;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float wu = wbuf[2 * u + half];   // 0 for splits past ns
+      a4[0] = fmaf(wu, ov[u].x, a4[0]);
+      a4[1] = fmaf(wu, ov[u].y, a4[1]);
+      a4[2] = fmaf(wu, ov[u].z, a4[2]);
+      a4[3] = fmaf(wu, ov[u].w, a4[3]);
     }
+    __builtin_amdgcn_wave_barrier();
   }
-  for (; s2 < ns; ++s2) {
-    const float2 ov = *(const float2*)(ph + (size_t)s2 * PS + 2 + d0);
-    const float w = wbuf[s2];
-    a0 = fmaf(w, ov.x, a0);
-    a1 = fmaf(w, ov.y, a1);
+  // the two lane halves hold the even / odd splits of the same 4 dims
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a4[e]), __float_as_uint(a4[e]), false, false);
+    a4[e] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  const float inv = lt > 0.f ? gate / lt : 0.f;
-  out[d0] = f2h(a0 * inv);
-  out[d0 + 1] = f2h(a1 * inv);
+  if (lane < 32) {
+    const float inv = lt > 0.f ? gate / lt : 0.f;
+    *(uint2*)(out + dq) = make_uint2(pack_h2(a4[0] * inv, a4[1] * inv), pack_h2(a4[2] * inv, a4[3] * inv));
+  }
 }
 
 hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a) {
   if (a.rows.n <= 0) return hipSuccess;
-  if (a.max_splits > kMaxMergeSplits) return hipErrorInvalidValue;
+  if (a.max_splits > kMaxMergeSplits || a.split_keys % TILE || a.split_keys <= 0) return hipErrorInvalidValue;
   if (a.kv.ring == 0)
     hipLaunchKernelGGL(k_attn_decode<true>, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
   else

@@ -350,8 +350,12 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     prologue_compute<BITS, BT>(a, p, xp, xsum, red, split);
   } else {
+    // (a barrier without a wait: every wave of the block has its input loads queued before any
+    // wave queues weight loads behind them)
     PlainRegs<BT> p;
     plain_load<BT>(a, p, 0, split);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     fetch(wa, 0);
     __builtin_amdgcn_sched_barrier(0);

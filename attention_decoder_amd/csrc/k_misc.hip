@@ -224,14 +224,15 @@ hipError_t launch_qk_rope(hipStream_t s, const QkRopeArgs& a) {
 // row, each row a distinct slot.
 // ---------------------------------------------------------------------------------------------
 
-constexpr int kConvRowBlock = 64;
+constexpr int kConvRun = 8;   // prefill rows per thread
 
 __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= a.hidden) return;
   const int H = a.hidden, T = a.taps, S = T - 1;
   float ker[kMaxTaps];
-  for (int j = 0; j < T; ++j) ker[j] = bf2f(a.kernel[(size_t)c * T + j]);
+#pragma unroll
+  for (int j = 0; j < kMaxTaps; ++j) ker[j] = j < T ? bf2f(a.kernel[(size_t)c * T + j]) : 0.f;
   auto zrow = [&](int r) -> float {
     const float* p = a.bcx + (size_t)r * a.ld;
     return h2f(f2h_sep(p[c] * p[2 * H + c]));
@@ -250,25 +251,46 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
     st[(size_t)(S - 1) * H + c] = f2h(z);
     return;
   }
+  // prefill: a run of kConvRun rows of one channel per thread; every input of the run (z of the
+  // run and of the taps-1 rows before it, from bcx or, before row 0, the kept state; C of the run)
+  // is loaded up front (clamped addresses, branch-free), then the run is computed
   const int M = a.rows.n;
-  const int r0 = blockIdx.y * kConvRowBlock;
-  const int r1 = min(M, r0 + kConvRowBlock);
+  const int r0 = blockIdx.y * kConvRun;
   f16_t* st = a.state + (size_t)a.rows.slot0 * a.slot_stride;
-  for (int j = 0; j < S; ++j) {
-    const int t = r0 - S + j;
-    win[j] = t >= 0 ? zrow(t) : h2f(st[(size_t)(S + t) * H + c]);
+  constexpr int NZ = kConvRun + kMaxTaps - 1;
+  float bz[NZ], xz[NZ], sz[NZ], cz[kConvRun];
+#pragma unroll
+  for (int i = 0; i < NZ; ++i) {
+    const int t = r0 - S + i;
+    const int tt = min(max(t, 0), M - 1);
+    const float* p = a.bcx + (size_t)tt * a.ld;
+    bz[i] = p[c];
+    xz[i] = p[2 * H + c];
+    sz[i] = h2f(st[(size_t)min(max(S + t, 0), S - 1) * H + c]);
   }
-  for (int r = r0; r < r1; ++r) {
-    const float z = zrow(r);
-    float y = ker[S] * z;
-    for (int j = 0; j < S; ++j) y = fmaf(ker[j], win[j], y);
-    a.out[(size_t)r * H + c] = f2h_sep(crow(r) * y);
-    for (int j = 0; j + 1 < S; ++j) win[j] = win[j + 1];
-    win[S - 1] = z;
+#pragma unroll
+  for (int i = 0; i < kConvRun; ++i) cz[i] = a.bcx[(size_t)min(r0 + i, M - 1) * a.ld + H + c];
+  float z[NZ];
+#pragma unroll
+  for (int i = 0; i < NZ; ++i) z[i] = (r0 - S + i) < 0 ? sz[i] : h2f(f2h_sep(bz[i] * xz[i]));
+  // z[i + S] is row r0 + i; the taps before it are z[i] .. z[i + S - 1] (all indices constant
+  // after unrolling, selected by S)
+  const float kS = bf2f(a.kernel[(size_t)c * T + S]);
+#pragma unroll
+  for (int i = 0; i < kConvRun; ++i) {
+    const int r = r0 + i;
+    float zc = z[i + kMaxTaps - 1];
+#pragma unroll
+    for (int q = kMaxTaps - 2; q >= 0; --q) zc = (q + 1 == S) ? z[i + q + 1] : zc;   // z[i + S]
+    float y = kS * zc;
+#pragma unroll
+    for (int j = 0; j < kMaxTaps - 1; ++j)
+      if (j < S) y = fmaf(ker[j], z[i + j], y);
+    if (r < M) a.out[(size_t)r * H + c] = f2h_sep(cz[i] * y);
   }
   if (blockIdx.y == 0) {
     // new state: the last S entries of [state | z_0 .. z_{M-1}]; ascending j reads state[M + j]
-    // (M >= 1) before it is overwritten.
+    // (M >= 1) before it is overwritten, and no other block reads the state.
     for (int j = 0; j < S; ++j) {
       const int t = M - S + j;
       const float v = t >= 0 ? zrow(t) : h2f(st[(size_t)(S + t) * H + c]);
@@ -280,7 +302,8 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
 hipError_t launch_conv(hipStream_t s, const ConvArgs& a) {
   if (a.rows.n <= 0) return hipSuccess;
   const int cb = (a.hidden + 255) / 256;
-  const int rb = a.rows.mode == 1 ? a.rows.n : (a.rows.n + kConvRowBlock - 1) / kConvRowBlock;
+  if (a.taps > kMaxTaps || a.taps < 2 || a.hidden % 256) return hipErrorInvalidValue;
+  const int rb = a.rows.mode == 1 ? a.rows.n : (a.rows.n + kConvRun - 1) / kConvRun;
   hipLaunchKernelGGL(k_conv, dim3(cb, rb), dim3(256), 0, s, a);
   return hipGetLastError();
 }

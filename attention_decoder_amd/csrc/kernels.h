@@ -176,11 +176,13 @@ struct AttnDecodeArgs {
   int n_q_heads, n_kv_heads;
   float eps;
   f16_t* out;          // [rows, n_q_heads * 128]
-  float* part;         // [rows, n_q_heads, max_splits, 130]
+  float* part;         // [rows, n_q_heads, max_splits, kPartStride]
   int* counters;       // [rows, n_kv_heads]
   int max_splits;      // grid extent: the most splits any row needs
+  int split_keys;      // keys per split (a multiple of 64): attn_decode_split_keys
 };
+constexpr int kPartStride = kHeadDim + 4;   // split partial: o [128], max, sum, 2 pad (16-byte rows)
 hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a);
-int attn_decode_split_keys();
+int attn_decode_split_keys(bool sliding, int window);
 
 }  // namespace lfm3

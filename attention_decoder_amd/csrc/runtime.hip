@@ -172,7 +172,7 @@ Layout make_layout(const lfm3_config& c) {
   L.max_rows = std::max(c.max_chunk, c.max_slots);
   L.max_pages = (c.max_ctx + kPageTokens - 1) / kPageTokens;
   L.ring_rows = c.window + c.max_chunk;
-  L.max_splits = (c.max_ctx + attn_decode_split_keys() - 1) / attn_decode_split_keys() + 1;
+  L.max_splits = (c.max_ctx + 63) / 64 + 1;   // splits are >= 64 keys
   L.big_ld = std::max<int>(3 * c.hidden, qkvg_rows(c));
   L.big_ld = (L.big_ld + 7) / 8 * 8;
   const size_t tab = (size_t)c.max_ctx * kHalfDim * 4;
@@ -197,7 +197,7 @@ Layout make_layout(const lfm3_config& c) {
   L.qrot = take(R * c.n_q_heads * kHeadDim * 2);
   L.m = take(R * H * 4);
   L.xf = take(R * H * 2);
-  L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * (kHeadDim + 2) * 4);
+  L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
   L.keys = take((size_t)std::max(kMaxBatch, (int)R) * 8);
   L.counters = take((size_t)c.max_slots * c.n_kv_heads * 4);
   L.total = off;
@@ -543,9 +543,10 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
       aa.out = mix; aa.part = ctx->at<float>(L.part); aa.counters = ctx->at<int>(L.counters);
       int ms = 1;
       double kv_bytes = 0;
+      aa.split_keys = attn_decode_split_keys(!full, c.window);
       for (int r = 0; r < M; ++r) {
         const int lo = full ? 0 : std::max(0, rows.pos[r] - (c.window - 1));
-        ms = std::max(ms, (rows.pos[r] - lo) / attn_decode_split_keys() + 1);
+        ms = std::max(ms, (rows.pos[r] - lo) / aa.split_keys + 1);
         kv_bytes += (double)(rows.pos[r] - lo + 1) * c.n_kv_heads * kHeadDim * 2 * 2;
       }
       aa.max_splits = ms;
