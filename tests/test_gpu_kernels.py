@@ -16,7 +16,7 @@ SHAPES = ["layers.0.conv.in_proj", "layers.1.attn.qkvg_proj", "layers.2.ffn.w13"
 def eng(slice3):
     from attention_decoder_amd.lfm3 import Engine
     cfg, blob = slice3
-    e = Engine(dict(cfg, max_slots=8, max_chunk=512), blob)
+    e = Engine(dict(cfg, max_slots=8, max_chunk=2048), blob)
     yield e
     e.close()
 
@@ -59,6 +59,28 @@ def test_gemm_matches_float64(eng, weights, name):
         assert np.abs(y - want_f16w).max() / np.abs(want_f16w).max() < 2e-5, (name, rows)
         rel = np.linalg.norm(y - want_exact) / np.linalg.norm(want_exact)
         assert rel < 1e-3, (name, rows, rel)
+
+
+@pytest.mark.parametrize("name,path", [("layers.2.ffn.w13", 1), ("layers.2.ffn.w13", 3), ("layers.0.conv.in_proj", 1)])
+def test_gemm_prefill_chunk_sampled_rows(eng, weights, name, path):
+    """At a full prefill chunk (1800 rows: the 256 x 256 eight-wave tiles with a ragged last row
+    tile) every sampled output row matches the float64 product with the fp16-rounded weights."""
+    import torch
+    w = weights[name]
+    rows = 1800
+    x, xd = _x(torch, rows, w.shape[1], 7)
+    y = eng.linear(name, xd, path).float().cpu().numpy().astype(np.float64)
+    pick = np.r_[0:8, 250:262, 1790:1800, np.random.default_rng(3).integers(0, rows, 24)]
+    xs = x[pick].astype(np.float64)
+    if path == 1:
+        want = xs @ ref.f16_round(w).T
+        assert np.abs(y[pick] - want).max() / np.abs(want).max() < 2e-5, name
+    else:
+        F = w.shape[0] // 2
+        ab = xs @ ref.f16_round(w).T
+        g, u = ab[:, :F], ab[:, F:]
+        want = g / (1 + np.exp(-g)) * u
+        assert np.abs(y[pick] - want).max() / np.abs(want).max() < 2e-3, name
 
 
 @pytest.mark.parametrize("name,path", [(n, 0) for n in SHAPES] + [("layers.2.ffn.w13", 2)])
