@@ -269,6 +269,54 @@ def run_extras(eng, synth, torch, dev, schemes=True):
                 out["q6_prefill_8k_tok_s"], ms6, _ = prefill_8k(e2, synth, torch, dev)
                 log(f"q6 8k prefill {out['q6_prefill_8k_tok_s']} tok/s ({ms6:.2f} ms)")
             e2.close()
+        out.update(cfg5_extras(synth, torch, dev))
+    return out
+
+
+def cfg5_extras(synth, torch, dev):
+    """4-bit g32 linears with an 8-bit g64 embedding / head: a 32768-token prefill (one stream, 2048-row
+    chunks), then 32 streams at contexts uniform in [1024, 32768] decoding 64 greedy tokens each at
+    batch 32."""
+    from attention_decoder_amd.lfm3 import Engine
+    out = {}
+    cfg = synth.full_config(bits=4, group=32, embed_bits=8, embed_group=64, max_slots=32, max_ctx=32768 + 128,
+                            max_chunk=2048)
+    eng = Engine(cfg, synth.cached_blob(cfg, seed=0))
+    toks = torch.from_numpy(synth.prompt_tokens(10, 32768)).to(dev)
+    times = []
+    for r in range(2):
+        eng.reset(0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(eng.stream)
+        eng.prefill(0, tokens=toks, logits=True, argmax=True)
+        b.record(eng.stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    out["cfg5_prefill_32k_ms"] = round(times[-1], 2)
+    out["cfg5_prefill_32k_tok_s"] = round(32768 / (times[-1] / 1e3), 1)
+    lens = synth.stream_prompt_lengths(11, 32, lo=1024, hi=32768)
+    for i in range(32):
+        eng.reset(i)
+        eng.prefill(i, tokens=torch.from_numpy(synth.prompt_tokens(1000 + i, int(lens[i]))).to(dev), logits=False,
+                    argmax=False)
+    n_steps = 64
+    ids = torch.empty((n_steps + 1, 32), dtype=torch.int32, device=dev)
+    ids[0] = torch.from_numpy(synth.prompt_tokens(12, 32)).to(dev)
+    slots = list(range(32))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(eng.stream)
+    for t in range(n_steps):
+        eng.decode(slots, tokens=ids[t], logits=False, argmax=True, out={"argmax": ids[t + 1]})
+    e1.record(eng.stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    out["cfg5_decode_32stream_tok_s"] = round(32 * n_steps / (ms / 1e3), 1)
+    out["cfg5_decode_32stream_mean_context"] = int(np.mean(lens))
+    log(f"g32 + 8-bit head: 32k prefill {out['cfg5_prefill_32k_tok_s']} tok/s, 32-stream decode "
+        f"{out['cfg5_decode_32stream_tok_s']} tok/s")
+    eng.close()
     return out
 
 

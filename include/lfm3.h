@@ -62,7 +62,8 @@ enum { LFM3_MAX_LAYERS = 64, LFM3_MAX_BATCH = 64 };
  *   runtime:   max_slots streams, max_ctx positions per slot, page_tokens positions per KV page
  *              (16), max_chunk rows per prefill pass, n_pages pages in the full-attention pool
  * This build runs head_dim 128, n_q_heads = 4 * n_kv_heads, conv_taps <= 8, page_tokens 16,
- * hidden and ffn multiples of 512; anything else is refused with LFM3_ERR_CONFIG.
+ * hidden (<= 4096) and ffn multiples of 512, max_ctx <= 65536; anything else is refused with
+ * LFM3_ERR_CONFIG.
  */
 typedef struct lfm3_config {
   int32_t n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, vocab, conv_taps, window;
