@@ -208,7 +208,10 @@ hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
 constexpr int TILE = 64;
 constexpr int KVS = kHeadDim + 8;   // LDS row stride of the K and V tiles (elements)
 constexpr int kMaxMergeSplits = 512;
-constexpr int kFullSplitKeys = 128;  // keys per split on full layers (2 tiles)
+#ifndef LFM3_FULL_SPLIT_KEYS
+#define LFM3_FULL_SPLIT_KEYS 128
+#endif
+constexpr int kFullSplitKeys = LFM3_FULL_SPLIT_KEYS;  // keys per split on full layers (2 tiles)
 
 // Sliding layers (<= window keys) split into single tiles, so all four 64-key tiles of a 256-key
 // window run in parallel blocks; full layers use 2-tile splits (fewer partials to merge).

@@ -339,12 +339,31 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     }
   };
 
+  // conv epilogue inputs of this wave's first group (taps and kept state of its two channels),
+  // loaded with the prologue so that the epilogue has no load of its own for that group
+  float cker[EPI == GEMV_CONV ? kMaxTaps : 1], cwin[EPI == GEMV_CONV ? BT : 1][EPI == GEMV_CONV ? kMaxTaps : 1];
+  auto conv_prefetch = [&]() {
+    if constexpr (EPI == GEMV_CONV) {
+      const int H = N / 3, T = a.conv_taps, S = T - 1;
+      const int ch = min(2 * min(g0, n_groups - 1) + ((lane >> 3) & 1), H - 1);
+#pragma unroll
+      for (int q = 0; q < kMaxTaps; ++q) cker[q] = bf2f(a.conv_kernel[(size_t)ch * T + min(q, T - 1)]);
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        const f16_t* st = a.conv_state + (size_t)a.conv_slot[min(b, a.batch - 1)] * a.conv_slot_stride;
+#pragma unroll
+        for (int q = 0; q < kMaxTaps - 1; ++q) cwin[b][q] = h2f(st[(size_t)min(q, S - 1) * H + ch]);
+      }
+    }
+  };
+
   WRegs wa, wb;
   if constexpr (PRO) {
     // prologue loads first, then the weight prefetch, then the prologue arithmetic: the in-order
     // load counter lets the weights stay in flight through the prologue
     PrologueRegs<BT> p;
     prologue_load<BT>(a, p);
+    conv_prefetch();
     __builtin_amdgcn_sched_barrier(0);
     fetch(wa, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -354,6 +373,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     // wave queues weight loads behind them)
     PlainRegs<BT> p;
     plain_load<BT>(a, p, 0, split);
+    conv_prefetch();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -471,18 +491,28 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
       if ((lane & 7) == 0 && r < 2) {
         const int H = N / 3, T = a.conv_taps, S = T - 1;
         const int ch = 2 * g + r;
+        const bool pre = gi == 0;   // the first group's taps and state were loaded up front
         float ker[kMaxTaps];
-        for (int q = 0; q < T; ++q) ker[q] = bf2f(a.conv_kernel[(size_t)ch * T + q]);
+#pragma unroll
+        for (int q = 0; q < kMaxTaps; ++q) ker[q] = pre ? cker[q] : (q < T ? bf2f(a.conv_kernel[(size_t)ch * T + q]) : 0.f);
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
           if (b >= a.batch) continue;
           f16_t* st = a.conv_state + (size_t)a.conv_slot[b] * a.conv_slot_stride;
           const float z = h2f(f2h_sep(t[b] * xg[b]));
           float win[kMaxTaps];
-          for (int q = 0; q < S; ++q) win[q] = h2f(st[(size_t)q * H + ch]);
-          float y = ker[S] * z;
-          for (int q = 0; q < S; ++q) y = fmaf(ker[q], win[q], y);
-          for (int q = 0; q + 1 < S; ++q) st[(size_t)q * H + ch] = f2h(win[q + 1]);
+#pragma unroll
+          for (int q = 0; q < kMaxTaps - 1; ++q) win[q] = pre ? cwin[b][q] : (q < S ? h2f(st[(size_t)q * H + ch]) : 0.f);
+          float kS = ker[kMaxTaps - 1];
+#pragma unroll
+          for (int q = kMaxTaps - 2; q >= 0; --q) kS = (q == S) ? ker[q] : kS;   // ker[S]
+          float y = kS * z;
+#pragma unroll
+          for (int q = 0; q < kMaxTaps - 1; ++q)
+            if (q < S) y = fmaf(ker[q], win[q], y);
+#pragma unroll
+          for (int q = 0; q < kMaxTaps - 2; ++q)
+            if (q + 1 < S) st[(size_t)q * H + ch] = f2h(win[q + 1]);
           st[(size_t)(S - 1) * H + ch] = f2h(z);
           a.y[(size_t)b * a.ldy + ch] = f2h_sep(cg[b] * y);
         }
@@ -522,7 +552,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
 }
 
 #ifndef LFM3_GEMV_MAX_BLOCKS
-#define LFM3_GEMV_MAX_BLOCKS 512
+#define LFM3_GEMV_MAX_BLOCKS 256
 #endif
 
 template <int BITS, int BT, int PRO, int KW>
