@@ -42,6 +42,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=192, help="oracle decode steps timed for cpu_baseline")
     ap.add_argument("--profile-only", action="store_true", help="one short step for rocprofv3 runs")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="one 8192-token prefill in 2048-row passes, for rocprofv3 runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --profile-only: also run three 256 MiB device copies (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -81,6 +83,14 @@ def main():
         e2.record(stream)
         if timing is not None:
             timing.append((e0, e1, e2))
+
+    if args.profile_prefill:
+        toks = torch.from_numpy(synth.prompt_tokens(5, 8192)).to(dev)
+        eng.reset(0)
+        eng.prefill(0, tokens=toks, logits=True, argmax=True)
+        torch.cuda.synchronize()
+        log("profile-prefill step done")
+        return
 
     if args.profile_only:
         args.decode = min(args.decode, 32)
