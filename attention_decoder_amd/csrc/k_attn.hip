@@ -22,19 +22,35 @@ LFM3_DEV float sigmoidf_(float g) { return 1.f / (1.f + __expf(-g)); }
 
 // ---------------------------------------------------------------------------------------------
 // prefill: one block per (32 query rows, kv head); wave w is query head 4 * kvh + w.
+// Keys are walked in 64-key tiles staged in LDS: the K and V rows of a tile are loaded into
+// registers two tiles ahead (branch-free; keys outside [k_lo, p_last] read a clamped valid key,
+// masked in the softmax) and stored into one of two LDS buffers one tile ahead. The page ids of the
+// block's key range are staged in LDS once, so no global load result feeds an address in the loop.
+// LDS rows are 256 bytes (128 dims) with the 16-byte chunk c of row r stored at chunk c ^ (r & 15),
+// which keeps the K reads, the V transpose reads and the stores free of bank conflicts.
 // S^T = K Q^T on v_mfma_f32_32x32x16_f16 (keys as rows, queries as columns), so each lane owns one
-// query: its softmax statistics need one exchange with lane ^ 32. Key slot r of the S^T tile reads
-// key pi(r) (bits 2 and 3 of r swapped) so that a lane's accumulators for P V are 8 consecutive keys
-// and feed the B operand of O^T += V^T P^T without moving data.
+// query: its softmax statistics need one exchange with lane ^ 32. Key slot r of an S^T sub-tile
+// reads key pi(r) (bits 2 and 3 of r swapped) so that a lane's accumulators for P V are 8
+// consecutive keys and feed the B operand of O^T += V^T P^T without moving data. The V^T operand
+// comes from the row-major V tile through the gfx950 LDS transpose read (ds_read_b64_tr_b16): in
+// each 16-lane group, slot j of lane i receives element i % 4 of the 8 bytes addressed by lane
+// 4j + i / 4, so lanes addressing 4 consecutive keys x 4 dims deliver 4 keys of one dim per lane.
 // ---------------------------------------------------------------------------------------------
 
-constexpr int KT = 32;             // keys per block
-constexpr int KS = kHeadDim + 8;   // K tile row stride (elements)
-constexpr int VS = KT + 8;         // V^T tile row stride (elements)
+constexpr int PKT = 64;                      // keys per staged tile
+constexpr int PTILE = PKT * kHeadDim;        // elements of one K or V tile
+constexpr int kAttnPrefillLds = 4 * PTILE * 2;   // two K and two V buffers (bytes)
 
-__global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) f16_t Ks[KT * KS];
-  __shared__ __attribute__((aligned(16))) f16_t Vt[kHeadDim * VS];
+LFM3_DEV int swz(int r, int c) { return r * kHeadDim + 8 * (c ^ (r & 15)); }   // element offset
+
+typedef short s16x4_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
+
+__global__ void __launch_bounds__(256, 1) k_attn_prefill(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) f16_t attn_smem[];
+  f16_t* Ks = attn_smem;                  // [2][PTILE]
+  f16_t* Vs = attn_smem + 2 * PTILE;      // [2][PTILE]
+  int* pids = (int*)(attn_smem + 4 * PTILE);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int kvh = blockIdx.y;
   const int h = kvh * kQPerKv + wave;
@@ -60,30 +76,41 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
   }
   int k_lo = 0;
   if (a.window > 0) k_lo = max(0, p_first - (a.window - 1));
-  const int kb0 = k_lo / KT * KT;
+  const int kb0 = k_lo / 32 * 32;
+  const int ntiles = (p_last - kb0) / PKT + 1;
 
-  // K/V tile loads, branch-free and one tile ahead: thread t moves 16-byte chunks t and t + 256 of
-  // the 32 key x 16 chunk tile; keys outside [k_lo, p_last] read a clamped valid key (masked in the
-  // softmax). Page ids of full layers are loaded one tile further ahead.
-  const int32_t* pt = a.kv.page_table + (size_t)slot * a.kv.max_pages;
-  auto key_of = [&](int kb, int i) { return min(max(kb + ((tid + 256 * i) >> 4), k_lo), p_last); };
-  auto page_of = [&](int kb, int i) { return paged ? pt[key_of(kb, i) / kPageTokens] : 0; };
-  auto kv_at = [&](int j, int page) -> size_t {
-    return paged ? (((size_t)page * nkv + kvh) * kPageTokens + (j % kPageTokens)) * kHeadDim
-                 : (((size_t)slot * nkv + kvh) * a.kv.ring + (j % a.kv.ring)) * kHeadDim;
-  };
-  int pg[2], pg_next[2];
-  u32x4_v kr[2], vr[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) pg[i] = page_of(kb0, i);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const size_t o = kv_at(key_of(kb0, i), pg[i]) + 8 * ((tid + 256 * i) & 15);
-    kr[i] = *(const u32x4_v*)(a.kv.k + o);
-    vr[i] = *(const u32x4_v*)(a.kv.v + o);
+  // page ids of the keys [kb0, p_last]
+  const int pg0 = kb0 / kPageTokens;
+  if (paged) {
+    const int32_t* pt = a.kv.page_table + (size_t)slot * a.kv.max_pages;
+    for (int i = tid; i <= p_last / kPageTokens - pg0; i += 256) pids[i] = pt[pg0 + i];
+    __syncthreads();
   }
+  auto row_of = [&](int key) -> size_t {
+    return paged ? (((size_t)pids[key / kPageTokens - pg0] * nkv + kvh) * kPageTokens + (key % kPageTokens)) * kHeadDim
+                 : (((size_t)slot * nkv + kvh) * a.kv.ring + (key % a.kv.ring)) * kHeadDim;
+  };
+  // thread t moves chunks u = t + 256 i (i < 4) of the tile's 64 rows x 16 chunks
+  auto gload = [&](int t, u32x4_v (&kr)[4], u32x4_v (&vr)[4]) {
+    const int kb = kb0 + t * PKT;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) pg_next[i] = page_of(kb0 + KT, i);
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      const int key = min(max(kb + (u >> 4), k_lo), p_last);
+      const size_t o = row_of(key) + 8 * (u & 15);
+      kr[i] = *(const u32x4_v*)(a.kv.k + o);
+      vr[i] = *(const u32x4_v*)(a.kv.v + o);
+    }
+  };
+  auto sstore = [&](int buf, const u32x4_v (&kr)[4], const u32x4_v (&vr)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      const int e = swz(u >> 4, u & 15);
+      *(u32x4_v*)(Ks + buf * PTILE + e) = kr[i];
+      *(u32x4_v*)(Vs + buf * PTILE + e) = vr[i];
+    }
+  };
 
   f32x16_v o[4];
 #pragma unroll
@@ -94,66 +121,56 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
   const float scale = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   const int ks_r = lane & 31;
   const int kslot = (ks_r & ~12) | ((ks_r & 4) << 1) | ((ks_r & 8) >> 1);
+  // transpose-read lane roles: group g = lane / 16, key j = (lane % 16) / 4, dims 4q .. 4q + 3
+  const int tg = lane >> 4, tj = (lane & 15) >> 2, tq = lane & 3;
 
-  for (int kb = kb0; kb <= p_last; kb += KT) {
-    // the tile's K rows and V^T columns into LDS
-    __syncthreads();
+  auto compute = [&](int t) {
+    const f16_t* Kt = Ks + (t & 1) * PTILE;
+    const f16_t* Vt = Vs + (t & 1) * PTILE;
+    const int kb = kb0 + t * PKT;
+    f32x16_v st[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
-      const int key = idx >> 4, c8 = idx & 15;
-      *(u32x4_v*)(Ks + key * KS + 8 * c8) = kr[i];
+    for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(8 * c8 + 2 * e) * VS + key] = (f16_t)(vr[i][e] & 0xffffu);
-        Vt[(8 * c8 + 2 * e + 1) * VS + key] = (f16_t)(vr[i][e] >> 16);
+      for (int v = 0; v < 16; ++v) st[sub][v] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8_v kvv = *(const f16x8_v*)(Kt + swz(32 * sub + kslot, 2 * s + (lane >> 5)));
+        st[sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kvv, qv[s], st[sub], 0, 0, 0);
       }
     }
-    __syncthreads();
-    // next tile's loads (clamped: past the last tile they re-read valid keys, unused)
-    {
-      const int kn = kb + KT;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const size_t off = kv_at(key_of(kn, i), pg_next[i]) + 8 * ((tid + 256 * i) & 15);
-        kr[i] = *(const u32x4_v*)(a.kv.k + off);
-        vr[i] = *(const u32x4_v*)(a.kv.v + off);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) pg_next[i] = page_of(kn + KT, i);
-    }
-
-    // S^T tile: rows = key slots, cols = queries
-    f32x16_v st;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) st[v] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8_v kvv = *(const f16x8_v*)(Ks + kslot * KS + 16 * s + 8 * (lane >> 5));
-      st = __builtin_amdgcn_mfma_f32_32x32x16_f16(kvv, qv[s], st, 0, 0, 0);
-    }
-    // acc v of this lane is key kb + 16(v/8) + 8(lane/32) + v%8 (after the slot permutation)
-    float sv[16];
+    // acc v of sub-tile sub is key kb + 32 sub + 16(v/8) + 8(lane/32) + v%8
+    const bool interior = kb >= k_lo && kb + PKT - 1 <= p_first && (a.window == 0 || p_last - kb < a.window);
+    float sv[2][16];
     float mloc = -__builtin_huge_valf();
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int j = kb + 16 * (v >> 3) + 8 * (lane >> 5) + (v & 7);
-      bool vis = j >= k_lo && j <= qpos;
-      if (a.window > 0) vis = vis && (qpos - j) < a.window;
-      sv[v] = vis ? st[v] * scale : -__builtin_huge_valf();
-      mloc = fmaxf(mloc, sv[v]);
-    }
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x = st[sub][v] * scale;
+        if (!interior) {
+          const int j = kb + 32 * sub + 16 * (v >> 3) + 8 * (lane >> 5) + (v & 7);
+          bool vis = j >= k_lo && j <= qpos;
+          if (a.window > 0) vis = vis && (qpos - j) < a.window;
+          x = vis ? x : -__builtin_huge_valf();
+        }
+        sv[sub][v] = x;
+        mloc = fmaxf(mloc, x);
+      }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     const float m_new = fmaxf(m_run, mloc);
-    const float alpha = m_new == -__builtin_huge_valf() ? 1.f : exp2f(m_run - m_new);
+    const bool none = m_new == -__builtin_huge_valf();
+    const float alpha = none ? 1.f : exp2f(m_run - m_new);
     float lsum = 0.f;
-    f16x8_v pv[2];
+    f16x8_v pv[2][2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = m_new == -__builtin_huge_valf() ? 0.f : exp2f(sv[v] - m_new);
-      lsum += p;
-      pv[v >> 3][v & 7] = (_Float16)p;
-    }
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pr = none ? 0.f : exp2f(sv[sub][v] - m_new);
+        lsum += pr;
+        pv[sub][v >> 3][v & 7] = (_Float16)pr;
+      }
     lsum += __shfl_xor(lsum, 32, 64);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
@@ -163,13 +180,40 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
       for (int v = 0; v < 16; ++v) o[d][v] *= alpha;
     // O^T[dim][query] += V^T[dim][keys] P^T[keys][query]
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f16x8_v vt = *(const f16x8_v*)(Vt + (32 * d + (lane & 31)) * VS + 16 * t + 8 * (lane >> 5));
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt, pv[t], o[d], 0, 0, 0);
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int kr = 32 * sub + 16 * t2 + 8 * (tg >> 1) + tj;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int c = 4 * d + 2 * (tg & 1) + (tq >> 1);
+          const int half = 4 * (tq & 1);
+          const s16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + swz(kr, c) + half));
+          const s16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + swz(kr + 4, c) + half));
+          const f16x8_v vt = __builtin_bit_cast(f16x8_v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt, pv[sub][t2], o[d], 0, 0, 0);
+        }
       }
-    }
+  };
+
+  // tile t + 1 is stored while tile t is computed; tile t + 3 is loaded into the registers the
+  // store freed (register sets A and B alternate, so nothing is copied across the loop edge)
+  u32x4_v kA[4], vA[4], kB[4], vB[4];
+  gload(0, kA, vA);
+  sstore(0, kA, vA);
+  gload(1, kA, vA);
+  gload(2, kB, vB);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    sstore(1, kA, vA);          // tile t + 1
+    gload(t + 3, kA, vA);
+    compute(t);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    sstore(0, kB, vB);          // tile t + 2
+    gload(t + 4, kB, vB);
+    compute(t + 1);
+    __syncthreads();
   }
 
   if (!qvalid) return;
@@ -189,7 +233,16 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnArgs a) {
 
 hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
   if (a.rows.n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_attn_prefill, dim3((a.rows.n + 31) / 32, a.n_kv_heads), dim3(256), 0, s, a);
+  // two K and two V tiles, then the page ids of up to the whole page table row
+  const size_t lds = kAttnPrefillLds + (a.kv.ring == 0 ? (size_t)a.kv.max_pages * sizeof(int) : 0);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  static size_t lds_set = 0;
+  if (lds > lds_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_attn_prefill, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_set = lds;
+  }
+  hipLaunchKernelGGL(k_attn_prefill, dim3((a.rows.n + 31) / 32, a.n_kv_heads), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

@@ -1,38 +1,42 @@
-// Dequant-to-LDS fp16 MFMA GEMM for prompt prefill on gfx950.
+// Dequant fp16 MFMA GEMM for prompt prefill on gfx950.
 //
 // Y[m, n] = sum_k X[m, k] * f16(q[n, k] * s + bias) with MLX affine weights (TensorFold issue
-// #1491, "Checkpoint handling"). The dequantised weight is rounded once to fp16 as it is staged in
-// LDS; X is the fp16 activation; products accumulate in fp32 on v_mfma_f32_32x32x16_f16.
+// #1491, "Checkpoint handling"). The dequantised weight is rounded once to fp16; X is the fp16
+// activation; products accumulate in fp32 on v_mfma_f32_32x32x16_f16.
 //
-// Block tile BM = 128 rows of X by BN = 256 (or 128) weight rows by BK = 64, four waves as 2 x 2,
-// each wave 64 x BN/2 (2 x BN/64 MFMA tiles of 32 x 32). One LDS buffer per operand; the next K
-// tile's global loads are issued before the current tile's MFMAs (register prefetch), and two
-// blocks share a CU so that one block's staging overlaps the other's MFMAs.
+// Block tile BM (128 or 64) rows of X by 256 weight rows by BK = 64, four waves side by side in N:
+// wave w owns weight rows [64w, 64w + 64) of the tile and every row of X, as BM/32 x 2 MFMA tiles.
+// Only X goes through LDS (double-buffered, one barrier per K tile). The weights never touch LDS:
+// each lane loads the codes its MFMA B operand needs (row n = lane % 32 of a 32-row tile, the 32
+// consecutive k of its lane half) and dequantises them straight into operand registers, so the
+// LDS traffic per MFMA is one 16-byte A read per lane.
+//
+// K order inside an MFMA: for k sub-step t the lane half h supplies k = 32h + 8t .. 32h + 8t + 7 of
+// the K tile (the 8 codes of one 32-bit word at 4-bit). The unpacked codes come out as fp16 pairs
+// in a fixed order inside each group of 8 k ((0,4)(1,5)(2,6)(3,7) at 4-bit, (0,2)(1,3)(4,6)(5,7) at
+// 8-bit, natural at 6-bit); X is staged in LDS with the same order, which leaves every dot product
+// unchanged.
 //
 // Dequant in packed fp16: a code pair becomes (1024 + q0, 1024 + q1) with one and-or (the fp16
 // bit pattern 0x6400 | q), 1024 is subtracted exactly, and one packed fp16 FMA forms q * s + b
-// with a single rounding. The pairs come out in a fixed order within each 8-code group; X is
-// staged in LDS with the same order, which leaves every dot product unchanged.
+// with a single rounding.
 //
 // Loads are branch-free (rows past M or N read a clamped valid row whose results are not stored).
-// SwiGLU tiles interleave 32 gate rows and the 32 matching up rows, so a lane holds both halves of
-// an output column.
+// SwiGLU: a lane's two weight rows are the gate row and the matching up row of one output column.
 #include "kernels.h"
 
 namespace lfm3 {
 
-constexpr int BM = 128, BK = 64;
-constexpr int LDSK = BK + 8;  // padded row stride (elements): 144-byte rows keep ds_read_b128 conflict-free
+constexpr int BK = 64;
+constexpr int LDSK = BK + 8;  // padded X row stride (elements): 144-byte rows keep ds_read_b128 conflict-free
+constexpr int BN = 256;       // weight rows per block tile
 
-// Order of 8 consecutive k inside the staged tiles (per 16-byte group), matching the pair order of
-// the dequant: 4-bit (0,4)(1,5)(2,6)(3,7); 8-bit (0,2)(1,3)(4,6)(5,7); 6-bit natural.
+// Order of 8 consecutive k inside the staged X tile (per 16-byte group), matching the pair order of
+// the dequant: 4-bit (0,2)(4,6)(1,3)(5,7); 8-bit and 6-bit natural.
 template <int BITS> LFM3_DEV u32x4_v perm8(u32x4_v h) {
   if constexpr (BITS == 4) {
-    return u32x4_v{__builtin_amdgcn_perm(h[2], h[0], 0x05040100u), __builtin_amdgcn_perm(h[2], h[0], 0x07060302u),
-                   __builtin_amdgcn_perm(h[3], h[1], 0x05040100u), __builtin_amdgcn_perm(h[3], h[1], 0x07060302u)};
-  } else if constexpr (BITS == 8) {
-    return u32x4_v{__builtin_amdgcn_perm(h[1], h[0], 0x05040100u), __builtin_amdgcn_perm(h[1], h[0], 0x07060302u),
-                   __builtin_amdgcn_perm(h[3], h[2], 0x05040100u), __builtin_amdgcn_perm(h[3], h[2], 0x07060302u)};
+    return u32x4_v{__builtin_amdgcn_perm(h[1], h[0], 0x05040100u), __builtin_amdgcn_perm(h[3], h[2], 0x05040100u),
+                   __builtin_amdgcn_perm(h[1], h[0], 0x07060302u), __builtin_amdgcn_perm(h[3], h[2], 0x07060302u)};
   } else {
     return h;
   }
@@ -45,66 +49,71 @@ LFM3_DEV uint32_t deq2(uint32_t magic_pair, f16x2_v s2, f16x2_v b2) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
 }
 
-// Codes of one thread's run: CPT codes (64 or 32) of one weight row.
-template <int BITS, int CPT> struct Codes {
-  static constexpr int BYTES = CPT * BITS / 8;
-  static constexpr int NV = BYTES / 16;  // 16-byte loads (q6 with 32 codes: 24 bytes, see load)
-  uint32_t w[BYTES / 4];
+// The 32 codes of one lane's run (one weight row, 32 consecutive k): 16, 24 or 32 bytes.
+template <int BITS> struct Run {
+  static constexpr int NW = BITS;  // 32 codes * BITS bits / 32
+  uint32_t w[NW];
 };
 
-template <int BITS, int CPT>
-LFM3_DEV void load_codes(const uint8_t* src, Codes<BITS, CPT>& c) {
-  constexpr int NW = Codes<BITS, CPT>::BYTES / 4;
-  if constexpr (NW % 4 == 0) {
+// Raw buffer loads: the lane's byte offset in a VGPR, the K-tile offset in an SGPR, so the loop
+// carries no per-lane address arithmetic.
+LFM3_DEV __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int BITS> LFM3_DEV void load_run(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, Run<BITS>& r) {
+  if constexpr (BITS == 6) {
 #pragma unroll
-    for (int v = 0; v < NW / 4; ++v) {
-      const u32x4_v t = *(const u32x4_v*)(src + 16 * v);
-      c.w[4 * v] = t[0]; c.w[4 * v + 1] = t[1]; c.w[4 * v + 2] = t[2]; c.w[4 * v + 3] = t[3];
+    for (int v = 0; v < 3; ++v) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 8 * v, soff, 0);
+      r.w[2 * v] = t[0]; r.w[2 * v + 1] = t[1];
     }
   } else {
 #pragma unroll
-    for (int v = 0; v < NW / 2; ++v) {
-      const uint2 t = *(const uint2*)(src + 8 * v);
-      c.w[2 * v] = t.x; c.w[2 * v + 1] = t.y;
+    for (int v = 0; v < BITS / 4; ++v) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * v, soff, 0);
+      r.w[4 * v] = t[0]; r.w[4 * v + 1] = t[1]; r.w[4 * v + 2] = t[2]; r.w[4 * v + 3] = t[3];
     }
   }
 }
 
-// Dequantise the run into CPT fp16 (CPT / 2 words) in the tile order. `sel` picks the scale pair
-// of codes at offsets >= group (two groups in a 64-code run at group 32).
-template <int BITS, int CPT>
-LFM3_DEV void dequant_run(const Codes<BITS, CPT>& c, const f16x2_v (&s2)[2], const f16x2_v (&b2)[2], int group,
-                          uint32_t (&out)[CPT / 2]) {
+// Byte selectors of v_perm_b32(0x64646464, t): [t.b0, 0x64, t.b1, 0x64] and [t.b2, 0x64, t.b3, 0x64],
+// i.e. the fp16 pairs (1024 + t.b0, 1024 + t.b1) and (1024 + t.b2, 1024 + t.b3) for bytes < 1024.
+constexpr uint32_t kSelLo = 0x04010400u, kSelHi = 0x04030402u;
+constexpr uint32_t kBytes64 = 0x64646464u;
+
+// Codes 8T .. 8T+7 of a run as the fp16 MFMA operand (4 pairs in the tile order).
+template <int BITS, int T> LFM3_DEV f16x8_v deq8(const Run<BITS>& r, f16x2_v s2, f16x2_v b2) {
+  uint32_t p[4];
   if constexpr (BITS == 4) {
-#pragma unroll
-    for (int d = 0; d < CPT / 8; ++d) {
-      const int g = (8 * d >= group) ? 1 : 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) out[4 * d + j] = deq2(((c.w[d] >> (4 * j)) & 0x000F000Fu) | kMagic2, s2[g], b2[g]);
-    }
+    // nibbles 0, 2, 4, 6 and 1, 3, 5, 7 of the word as bytes
+    const uint32_t t0 = r.w[T] & 0x0F0F0F0Fu, t1 = (r.w[T] >> 4) & 0x0F0F0F0Fu;
+    p[0] = deq2(__builtin_amdgcn_perm(kBytes64, t0, kSelLo), s2, b2);
+    p[1] = deq2(__builtin_amdgcn_perm(kBytes64, t0, kSelHi), s2, b2);
+    p[2] = deq2(__builtin_amdgcn_perm(kBytes64, t1, kSelLo), s2, b2);
+    p[3] = deq2(__builtin_amdgcn_perm(kBytes64, t1, kSelHi), s2, b2);
   } else if constexpr (BITS == 8) {
 #pragma unroll
-    for (int d = 0; d < CPT / 4; ++d) {
-      const int g = (4 * d >= group) ? 1 : 0;
-      out[2 * d] = deq2((c.w[d] & 0x00FF00FFu) | kMagic2, s2[g], b2[g]);
-      out[2 * d + 1] = deq2(((c.w[d] >> 8) & 0x00FF00FFu) | kMagic2, s2[g], b2[g]);
+    for (int d = 0; d < 2; ++d) {
+      p[2 * d] = deq2(__builtin_amdgcn_perm(kBytes64, r.w[2 * T + d], kSelLo), s2, b2);
+      p[2 * d + 1] = deq2(__builtin_amdgcn_perm(kBytes64, r.w[2 * T + d], kSelHi), s2, b2);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < CPT / 2; ++i) {
-      const int g = (2 * i >= group) ? 1 : 0;
+    for (int i = 0; i < 4; ++i) {
       uint32_t q2[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int bit = 6 * (2 * i + h);
+        const int bit = 6 * (8 * T + 2 * i + h);
         const int d = bit >> 5, sh = bit & 31;
-        uint32_t v = c.w[d] >> sh;
-        if (sh > 26) v |= c.w[d + 1] << (32 - sh);
+        uint32_t v = r.w[d] >> sh;
+        if (sh > 26) v |= r.w[d + 1] << (32 - sh);
         q2[h] = v & 63u;
       }
-      out[i] = deq2((q2[0] | (q2[1] << 16)) | kMagic2, s2[g], b2[g]);
+      p[i] = deq2((q2[0] | (q2[1] << 16)) | kMagic2, s2, b2);
     }
   }
+  return __builtin_bit_cast(f16x8_v, u32x4_v{p[0], p[1], p[2], p[3]});
 }
 
 LFM3_DEV f16x2_v bf16_pair(bf16_t b) {
@@ -112,135 +121,156 @@ LFM3_DEV f16x2_v bf16_pair(bf16_t b) {
   return f16x2_v{h, h};
 }
 
-template <int BITS, int EPI, int BN>
+template <int BITS, int EPI, int BM>
 __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
-  constexpr int NJ = BN / 64;          // 32-wide MFMA column tiles per wave
-  constexpr int CPT = BN == 256 ? 64 : 32;  // codes per thread per K tile
-  __shared__ __attribute__((aligned(16))) f16_t As[BM * LDSK];
-  __shared__ __attribute__((aligned(16))) f16_t Bs[BN * LDSK];
+  constexpr int MT = BM / 32;                  // 32-row MFMA tiles per wave
+  constexpr int AV = BM * BK / 8 / 256;        // 16-byte X pieces per thread per K tile
+  __shared__ __attribute__((aligned(16))) f16_t As[2][BM * LDSK];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int hf = lane >> 5, c32 = lane & 31;
   const int m0 = blockIdx.x * BM;
   const int K = a.w.k, N = a.w.n, M = a.m;
-  const int half = N / 2;
 
-  // weight row of this thread's run: tile row brow, codes [kofs, kofs + CPT) of the K tile
-  const int brow = BN == 256 ? tid : tid >> 1;
-  const int kofs = BN == 256 ? 0 : 32 * (tid & 1);
-  int wrow;
+  // the lane's two weight rows (MFMA column c32 of the wave's two 32-row tiles)
+  int wrow[2];
   if constexpr (EPI == GEMM_SWIGLU) {
-    const int wpart = brow / (BN / 2), j = (brow % (BN / 2)) / 32, r = brow & 31;
-    const int outc = blockIdx.y * (BN / 2) + wpart * (BN / 4) + (j >> 1) * 32 + r;
-    wrow = (j & 1 ? half : 0) + outc;
+    const int outc = blockIdx.y * (BN / 2) + 32 * wave + c32;
+    wrow[0] = outc;
+    wrow[1] = N / 2 + outc;
   } else {
-    wrow = min((int)blockIdx.y * BN + brow, N - 1);
+    wrow[0] = min((int)blockIdx.y * BN + 64 * wave + c32, N - 1);
+    wrow[1] = min((int)blockIdx.y * BN + 64 * wave + 32 + c32, N - 1);
   }
-  const size_t row_bytes = (size_t)K * BITS / 8;
-  const uint8_t* wsrc = a.w.q + (size_t)wrow * row_bytes;
+  const uint32_t row_bytes = (uint32_t)K * BITS / 8;
   const int ngr = K / a.w.group;
-  const int group = a.w.group;
-
-  u32x4_v areg[4];
-  Codes<BITS, CPT> creg;
-  bf16_t sraw[2], braw[2];
+  const int gshift = a.w.group == 32 ? 5 : 6;
 
   // K tiles 0 .. nk-1 read x; with a remainder input, tiles nk .. 2nk-1 read x_lo against the same
   // weight tiles (Y = x W + x_lo W)
   const int nk = K / BK;
-  auto gload = [&](int kt) {
+  const int nkt = a.x_lo ? 2 * nk : nk;
+
+  const uint32_t xbytes = (uint32_t)((size_t)(M - 1) * a.ldx + K) * 2u;
+  const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.x, xbytes);
+  const __amdgpu_buffer_rsrc_t rxl = rsrc_of(a.x_lo ? a.x_lo : a.x, xbytes);
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.w.q, (uint32_t)N * row_bytes);
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.w.scales, (uint32_t)N * ngr * 2u);
+  const __amdgpu_buffer_rsrc_t rb = rsrc_of(a.w.biases, (uint32_t)N * ngr * 2u);
+
+  // per-lane byte offsets, fixed over the K loop
+  uint32_t xoff[AV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i) {
+    const int idx = tid + 256 * i;
+    const int r = idx >> 3, c8 = idx & 7;
+    xoff[i] = ((uint32_t)min(m0 + r, M - 1) * (uint32_t)a.ldx + 8u * c8) * 2u;
+  }
+  uint32_t qoff[2], soff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    qoff[j] = (uint32_t)wrow[j] * row_bytes + 32u * hf * BITS / 8;
+    soff[j] = ((uint32_t)wrow[j] * ngr + ((32 * hf) >> gshift)) * 2u;
+  }
+
+  u32x4_v areg[AV];
+  auto load_x = [&](int kt) {
     const bool second = kt >= nk;
-    const int k0 = (second ? kt - nk : kt) * BK;
-    const f16_t* xs = second ? a.x_lo : a.x;
+    const uint32_t k0 = (uint32_t)(second ? kt - nk : kt) * BK;
+    const __amdgpu_buffer_rsrc_t r = second ? rxl : rx;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int r = idx >> 3, c8 = idx & 7;
-      const int m = min(m0 + r, M - 1);
-      areg[i] = *(const u32x4_v*)(xs + (size_t)m * a.ldx + k0 + 8 * c8);
-    }
-    const int kc = k0 + kofs;
-    load_codes<BITS, CPT>(wsrc + (size_t)kc * BITS / 8, creg);
-    const int g0 = kc / group, g1 = (kc + CPT - 1) / group;
-    sraw[0] = a.w.scales[(size_t)wrow * ngr + g0];
-    braw[0] = a.w.biases[(size_t)wrow * ngr + g0];
-    sraw[1] = a.w.scales[(size_t)wrow * ngr + g1];
-    braw[1] = a.w.biases[(size_t)wrow * ngr + g1];
+    for (int i = 0; i < AV; ++i) areg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, xoff[i], 2u * k0, 0);
   };
-  auto sstore = [&]() {
+  auto store_x = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < AV; ++i) {
       const int idx = tid + 256 * i;
       const int r = idx >> 3, c8 = idx & 7;
-      *(u32x4_v*)(As + r * LDSK + 8 * c8) = perm8<BITS>(areg[i]);
+      *(u32x4_v*)(&As[buf][r * LDSK + 8 * c8]) = perm8<BITS>(areg[i]);
     }
-    const f16x2_v s2[2] = {bf16_pair(sraw[0]), bf16_pair(sraw[1])};
-    const f16x2_v b2[2] = {bf16_pair(braw[0]), bf16_pair(braw[1])};
-    uint32_t pk[CPT / 2];
-    dequant_run<BITS, CPT>(creg, s2, b2, group, pk);
-    u32x4_v* dst = (u32x4_v*)(Bs + brow * LDSK + kofs);
+  };
+  // weight registers in two sets (even / odd K tiles), so that no value has to be copied across
+  // the loop edge (a copy would make every iteration wait for the loads it just issued)
+  struct WSet {
+    Run<BITS> run[2];
+    uint32_t s[2], b[2];   // raw bf16 bits
+  };
+  auto load_w = [&](int kt, WSet& w) {
+    const uint32_t k0 = (uint32_t)(kt >= nk ? kt - nk : kt) * BK;
+    const uint32_t sg = (k0 >> gshift) * 2u;
 #pragma unroll
-    for (int q = 0; q < CPT / 8; ++q) dst[q] = u32x4_v{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
+    for (int j = 0; j < 2; ++j) {
+      load_run<BITS>(rq, qoff[j], k0 * BITS / 8, w.run[j]);
+      w.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[j], sg, 0);
+      w.b[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, soff[j], sg, 0);
+    }
   };
 
-  f32x16_v acc[2][NJ];
+  f32x16_v acc[MT][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nkt = a.x_lo ? 2 * nk : nk;
-  gload(0);
-  sstore();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) gload(kt + 1);
+  // one K tile: its weights (in `cur`) into operand registers, the next tile's weight loads into
+  // `nxt`, the next tile's X (loaded one tile ago) into the other LDS buffer, the X loads of the
+  // tile after that, then the MFMAs
+  auto step = [&](int kt, const WSet& cur, WSet& nxt) {
+    f16x8_v bop[2][4];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      f16x8_v av[2], bv[NJ];
+    for (int j = 0; j < 2; ++j) {
+      const f16x2_v s2 = bf16_pair((bf16_t)cur.s[j]), b2 = bf16_pair((bf16_t)cur.b[j]);
+      bop[j][0] = deq8<BITS, 0>(cur.run[j], s2, b2);
+      bop[j][1] = deq8<BITS, 1>(cur.run[j], s2, b2);
+      bop[j][2] = deq8<BITS, 2>(cur.run[j], s2, b2);
+      bop[j][3] = deq8<BITS, 3>(cur.run[j], s2, b2);
+    }
+    // unconditional (past the end they re-read the last tile, unused): a branch here would make
+    // the compiler's wait counting assume the other path's loads are still in flight
+    load_w(min(kt + 1, nkt - 1), nxt);
+    store_x((kt + 1) & 1);
+    load_x(min(kt + 2, nkt - 1));
+    const f16_t* at = As[kt & 1];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 64 * wm + 32 * i + (lane & 31);
-        av[i] = *(const f16x8_v*)(As + r * LDSK + 16 * ks + 8 * (lane >> 5));
-      }
+    for (int t = 0; t < 4; ++t) {
+      f16x8_v av[MT];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int r = (BN / 2) * wn + 32 * j + (lane & 31);
-        bv[j] = *(const f16x8_v*)(Bs + r * LDSK + 16 * ks + 8 * (lane >> 5));
-      }
+      for (int i = 0; i < MT; ++i) av[i] = *(const f16x8_v*)(at + (32 * i + c32) * LDSK + 32 * hf + 8 * t);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bop[j][t], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
-    if (kt + 1 < nkt) {
-      sstore();
-      __syncthreads();
-    }
+  };
+
+  WSet w0, w1;
+  load_x(0);
+  load_w(0, w0);
+  store_x(0);
+  load_x(1);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {   // nkt is even (K % 128 == 0)
+    step(kt, w0, w1);
+    step(kt + 1, w1, w0);
   }
 
-  // epilogue: acc[i][j][v] is row 64wm + 32i + 8(v/4) + 4(lane/32) + v%4, tile column
-  // (BN/2) wn + 32 j + lane%32
+  // epilogue: acc[i][j][v] is X row m0 + 32i + 8(v/4) + 4(lane/32) + v%4 against weight row wrow[j]
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * hf + (v & 3);
       if (row >= M) continue;
       if constexpr (EPI == GEMM_SWIGLU) {
-#pragma unroll
-        for (int jj = 0; jj < NJ / 2; ++jj) {
-          const int col = blockIdx.y * (BN / 2) + wn * (BN / 4) + 32 * jj + (lane & 31);
-          const float g = acc[i][2 * jj][v], u = acc[i][2 * jj + 1][v];
-          a.y[(size_t)row * a.ldy + col] = f2h_sep(g / (1.f + __expf(-g)) * u);
-        }
+        const float g = acc[i][0][v], u = acc[i][1][v];
+        a.y[(size_t)row * a.ldy + wrow[0]] = f2h_sep(g / (1.f + __expf(-g)) * u);
       } else {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int col = blockIdx.y * BN + (BN / 2) * wn + 32 * j + (lane & 31);
+        for (int j = 0; j < 2; ++j) {
+          const int col = blockIdx.y * BN + 64 * wave + 32 * j + c32;
           if (col < N) a.yf[(size_t)row * a.ldy + col] = acc[i][j][v];
         }
       }
@@ -248,30 +278,30 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   }
 }
 
-template <int BITS, int BN>
-static void launch_bn(hipStream_t s, const GemmArgs& a) {
-  const int gm = (a.m + BM - 1) / BM;
+template <int BITS, int BMT>
+static void launch_bm(hipStream_t s, const GemmArgs& a) {
+  const int gm = (a.m + BMT - 1) / BMT;
   if (a.epi == GEMM_SWIGLU) {
-    hipLaunchKernelGGL((k_gemm<BITS, GEMM_SWIGLU, BN>), dim3(gm, a.w.n / BN), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<BITS, GEMM_SWIGLU, BMT>), dim3(gm, a.w.n / BN), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_gemm<BITS, GEMM_STORE, BN>), dim3(gm, (a.w.n + BN - 1) / BN), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<BITS, GEMM_STORE, BMT>), dim3(gm, (a.w.n + BN - 1) / BN), dim3(256), 0, s, a);
   }
 }
 
 template <int BITS>
 static hipError_t launch_bits(hipStream_t s, const GemmArgs& a) {
-  // wide tiles for wide weights (less re-reading of X); 128-wide for the 2048-row ones, which
-  // would otherwise leave half the chip idle
-  const bool wide = a.epi == GEMM_SWIGLU ? (a.w.n % 256 == 0 && a.w.n >= 4096) : a.w.n >= 4096;
-  if (wide) launch_bn<BITS, 256>(s, a);
-  else launch_bn<BITS, 128>(s, a);
+  // 128-row tiles for wide weights (each weight code is loaded once per 128 rows of X); 64-row
+  // tiles for the narrow ones, which would otherwise leave half the chip idle
+  if (a.w.n >= 4096) launch_bm<BITS, 128>(s, a);
+  else launch_bm<BITS, 64>(s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
   if (a.m <= 0) return hipSuccess;
-  // 16-byte rows of X, whole K tiles, whole code runs
-  if (a.w.k % BK || a.ldx % 8 || (uintptr_t)a.x % 16 || (uintptr_t)a.x_lo % 16 || (a.epi == GEMM_SWIGLU && a.w.n % 128))
+  // 16-byte rows of X, an even number of K tiles, 32-code runs inside one group, whole SwiGLU tiles
+  if (a.w.k % (2 * BK) || a.w.group % 32 || a.ldx % 8 || (uintptr_t)a.x % 16 || (uintptr_t)a.x_lo % 16 ||
+      (a.epi == GEMM_SWIGLU && a.w.n % BN))
     return hipErrorInvalidValue;
   switch (a.w.bits) {
     case 4: return launch_bits<4>(s, a);

@@ -1,4 +1,4 @@
-"""Kernel-level GPU parity: the decode dequant-GEMV and the prefill dequant-to-LDS MFMA GEMM on
+"""Kernel-level GPU parity: the decode dequant-GEMV and the prefill dequant MFMA GEMM on
 real layer shapes of the seeded three-layer slice, against the float64 oracle's dequantised
 weights times the same fp16 rows (MLX affine: w = q * scale + bias per group of 64)."""
 import numpy as np
@@ -63,8 +63,8 @@ def test_gemm_matches_float64(eng, weights, name):
 
 @pytest.mark.parametrize("name,path", [("layers.2.ffn.w13", 1), ("layers.2.ffn.w13", 3), ("layers.0.conv.in_proj", 1)])
 def test_gemm_prefill_chunk_sampled_rows(eng, weights, name, path):
-    """At a full prefill chunk (1800 rows: the 256 x 256 eight-wave tiles with a ragged last row
-    tile) every sampled output row matches the float64 product with the fp16-rounded weights."""
+    """At a full prefill chunk (1800 rows: 128- or 64-row tiles with a ragged last row tile) every
+    sampled output row matches the float64 product with the fp16-rounded weights."""
     import torch
     w = weights[name]
     rows = 1800
