@@ -21,7 +21,8 @@ LFM3_DEV const f16_t* kv_src(const KvRef& kv, const f16_t* base, int slot, int p
 LFM3_DEV float sigmoidf_(float g) { return 1.f / (1.f + __expf(-g)); }
 
 // ---------------------------------------------------------------------------------------------
-// prefill: one block per (32 query rows, kv head); wave w is query head 4 * kvh + w.
+// prefill: one block per (32 query rows, kv head), 8 waves: wave w is query head 4 * kvh + w % 4 over
+// the even (w < 4) or odd (w >= 4) key tiles; the two halves' softmax states are merged at the end.
 // Keys are walked in 64-key tiles staged in LDS: the K and V rows of a tile are loaded into
 // registers two tiles ahead (branch-free; keys outside [k_lo, p_last] read a clamped valid key,
 // masked in the softmax) and stored into one of two LDS buffers one tile ahead. The page ids of the
@@ -39,21 +40,24 @@ LFM3_DEV float sigmoidf_(float g) { return 1.f / (1.f + __expf(-g)); }
 
 constexpr int PKT = 64;                      // keys per staged tile
 constexpr int PTILE = PKT * kHeadDim;        // elements of one K or V tile
-constexpr int kAttnPrefillLds = 4 * PTILE * 2;   // two K and two V buffers (bytes)
+constexpr int kAttnPrefillLds = 8 * PTILE * 2;   // per key half: two K and two V buffers (bytes)
 
 LFM3_DEV int swz(int r, int c) { return r * kHeadDim + 8 * (c ^ (r & 15)); }   // element offset
 
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
 
-__global__ void __launch_bounds__(256, 1) k_attn_prefill(AttnArgs a) {
+template <bool PAGED>
+__global__ void __launch_bounds__(512, 1) k_attn_prefill(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) f16_t attn_smem[];
-  f16_t* Ks = attn_smem;                  // [2][PTILE]
-  f16_t* Vs = attn_smem + 2 * PTILE;      // [2][PTILE]
-  int* pids = (int*)(attn_smem + 4 * PTILE);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kh = wave >> 2;               // key half: even or odd tiles
+  const int tid = threadIdx.x & 255;      // thread within the half
+  f16_t* Ks = attn_smem + kh * 4 * PTILE;              // [2][PTILE]
+  f16_t* Vs = attn_smem + kh * 4 * PTILE + 2 * PTILE;  // [2][PTILE]
+  int* pids = (int*)(attn_smem + 8 * PTILE);
   const int kvh = blockIdx.y;
-  const int h = kvh * kQPerKv + wave;
+  const int h = kvh * kQPerKv + (wave & 3);
   const int M = a.rows.n;
   // the causal work grows with the query block: the longest blocks are dispatched first
   const int r0 = (gridDim.x - 1 - blockIdx.x) * 32;
@@ -62,7 +66,6 @@ __global__ void __launch_bounds__(256, 1) k_attn_prefill(AttnArgs a) {
   const int r_last = min(M - 1, r0 + 31);
   const int p_last = a.rows.pos0 + r_last;
   const int nq = a.n_q_heads, nkv = a.n_kv_heads;
-  const bool paged = a.kv.ring == 0;
 
   // this lane's query (column) and its position; rows past M read row M - 1 and are not stored
   const int qr = r0 + (lane & 31);
@@ -81,18 +84,18 @@ __global__ void __launch_bounds__(256, 1) k_attn_prefill(AttnArgs a) {
 
   // page ids of the keys [kb0, p_last]
   const int pg0 = kb0 / kPageTokens;
-  if (paged) {
+  if constexpr (PAGED) {
     const int32_t* pt = a.kv.page_table + (size_t)slot * a.kv.max_pages;
-    for (int i = tid; i <= p_last / kPageTokens - pg0; i += 256) pids[i] = pt[pg0 + i];
+    for (int i = threadIdx.x; i <= p_last / kPageTokens - pg0; i += 512) pids[i] = pt[pg0 + i];
     __syncthreads();
   }
   auto row_of = [&](int key) -> size_t {
-    return paged ? (((size_t)pids[key / kPageTokens - pg0] * nkv + kvh) * kPageTokens + (key % kPageTokens)) * kHeadDim
-                 : (((size_t)slot * nkv + kvh) * a.kv.ring + (key % a.kv.ring)) * kHeadDim;
+    if constexpr (PAGED) return (((size_t)pids[key / kPageTokens - pg0] * nkv + kvh) * kPageTokens + (key % kPageTokens)) * kHeadDim;
+    else return (((size_t)slot * nkv + kvh) * a.kv.ring + (key % a.kv.ring)) * kHeadDim;
   };
   // thread t moves chunks u = t + 256 i (i < 4) of the tile's 64 rows x 16 chunks
-  auto gload = [&](int t, u32x4_v (&kr)[4], u32x4_v (&vr)[4]) {
-    const int kb = kb0 + t * PKT;
+  auto gload = [&](int i_loc, u32x4_v (&kr)[4], u32x4_v (&vr)[4]) {
+    const int kb = kb0 + (2 * i_loc + kh) * PKT;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = tid + 256 * i;
@@ -124,10 +127,10 @@ __global__ void __launch_bounds__(256, 1) k_attn_prefill(AttnArgs a) {
   // transpose-read lane roles: group g = lane / 16, key j = (lane % 16) / 4, dims 4q .. 4q + 3
   const int tg = lane >> 4, tj = (lane & 15) >> 2, tq = lane & 3;
 
-  auto compute = [&](int t) {
-    const f16_t* Kt = Ks + (t & 1) * PTILE;
-    const f16_t* Vt = Vs + (t & 1) * PTILE;
-    const int kb = kb0 + t * PKT;
+  auto compute = [&](int i_loc) {
+    const f16_t* Kt = Ks + (i_loc & 1) * PTILE;
+    const f16_t* Vt = Vs + (i_loc & 1) * PTILE;
+    const int kb = kb0 + (2 * i_loc + kh) * PKT;
     f32x16_v st[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -196,24 +199,52 @@ __global__ void __launch_bounds__(256, 1) k_attn_prefill(AttnArgs a) {
       }
   };
 
-  // tile t + 1 is stored while tile t is computed; tile t + 3 is loaded into the registers the
-  // store freed (register sets A and B alternate, so nothing is copied across the loop edge)
+  // local tile i + 1 is stored while local tile i is computed; local tile i + 3 is loaded into the
+  // registers the store freed (register sets A and B alternate, so nothing is copied across the
+  // loop edge). Both halves run the same number of iterations (a past-the-end tile of the odd half
+  // is not computed) so that they meet at every barrier.
+  const int nloc = (ntiles + 1) / 2;
   u32x4_v kA[4], vA[4], kB[4], vB[4];
   gload(0, kA, vA);
   sstore(0, kA, vA);
   gload(1, kA, vA);
   gload(2, kB, vB);
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    sstore(1, kA, vA);          // tile t + 1
-    gload(t + 3, kA, vA);
-    compute(t);
+  for (int i = 0; i < nloc; i += 2) {
+    sstore(1, kA, vA);
+    gload(i + 3, kA, vA);
+    if (2 * i + kh < ntiles) compute(i);
     __syncthreads();
-    if (t + 1 >= ntiles) break;
-    sstore(0, kB, vB);          // tile t + 2
-    gload(t + 4, kB, vB);
-    compute(t + 1);
+    if (i + 1 >= nloc) break;
+    sstore(0, kB, vB);
+    gload(i + 4, kB, vB);
+    if (2 * (i + 1) + kh < ntiles) compute(i + 1);
     __syncthreads();
+  }
+
+  // merge the odd half's state into the even half's (the tile buffers are free now)
+  float* mb = (float*)attn_smem;   // [4 heads][66][64 lanes]: m, l, o
+  float* mine = mb + (size_t)(wave & 3) * 66 * 64 + lane;
+  if (kh == 1) {
+    mine[0] = m_run;
+    mine[64] = l_run;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mine[64 * (2 + 16 * d + v)] = o[d][v];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float m1 = mine[0], l1 = mine[64];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -__builtin_huge_valf() ? 0.f : exp2f(m_run - m);
+    const float a1 = m1 == -__builtin_huge_valf() ? 0.f : exp2f(m1 - m);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[d][v] = o[d][v] * a0 + mine[64 * (2 + 16 * d + v)] * a1;
   }
 
   if (!qvalid) return;
@@ -233,16 +264,20 @@ __global__ void __launch_bounds__(256, 1) k_attn_prefill(AttnArgs a) {
 
 hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
   if (a.rows.n <= 0) return hipSuccess;
-  // two K and two V tiles, then the page ids of up to the whole page table row
+  // per key half two K and two V tiles, then the page ids of up to the whole page table row
   const size_t lds = kAttnPrefillLds + (a.kv.ring == 0 ? (size_t)a.kv.max_pages * sizeof(int) : 0);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static size_t lds_set = 0;
-  if (lds > lds_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_attn_prefill, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static size_t lds_set[2] = {0, 0};
+  const bool paged = a.kv.ring == 0;
+  const void* fn = paged ? (const void*)k_attn_prefill<true> : (const void*)k_attn_prefill<false>;
+  if (lds > lds_set[paged]) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    lds_set = lds;
+    lds_set[paged] = lds;
   }
-  hipLaunchKernelGGL(k_attn_prefill, dim3((a.rows.n + 31) / 32, a.n_kv_heads), dim3(256), lds, s, a);
+  const dim3 grid((a.rows.n + 31) / 32, a.n_kv_heads);
+  if (paged) hipLaunchKernelGGL(k_attn_prefill<true>, grid, dim3(512), lds, s, a);
+  else hipLaunchKernelGGL(k_attn_prefill<false>, grid, dim3(512), lds, s, a);
   return hipGetLastError();
 }
 
