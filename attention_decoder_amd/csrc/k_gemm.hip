@@ -9,17 +9,17 @@
 // Only X goes through LDS (double-buffered, one barrier per K tile). The weights never touch LDS:
 // each lane loads the codes its MFMA B operand needs (row n = lane % 32 of a 32-row tile, the 32
 // consecutive k of its lane half) and dequantises them straight into operand registers, so the
-// LDS traffic per MFMA is one 16-byte A read per lane.
+// LDS traffic per MFMA is one 16-byte A read per lane. The weights are read from a re-tiled copy
+// (GemmW, built once by k_repack) in which every load instruction of a wave reads whole
+// contiguous 1 KB (or 512 B) runs, and the scale and bias of a lane's group come as one fp16 pair.
 //
 // K order inside an MFMA: for k sub-step t the lane half h supplies k = 32h + 8t .. 32h + 8t + 7 of
-// the K tile (the 8 codes of one 32-bit word at 4-bit). The unpacked codes come out as fp16 pairs
-// in a fixed order inside each group of 8 k ((0,4)(1,5)(2,6)(3,7) at 4-bit, (0,2)(1,3)(4,6)(5,7) at
-// 8-bit, natural at 6-bit); X is staged in LDS with the same order, which leaves every dot product
-// unchanged.
+// the K tile, in order (the re-tiled 4-bit words hold their codes at the nibble order the
+// byte-permute unpack needs), so X is staged in LDS as it is.
 //
-// Dequant in packed fp16: a code pair becomes (1024 + q0, 1024 + q1) with one and-or (the fp16
-// bit pattern 0x6400 | q), 1024 is subtracted exactly, and one packed fp16 FMA forms q * s + b
-// with a single rounding.
+// Dequant in packed fp16: a code pair becomes (1024 + q0, 1024 + q1) with one byte permute (the
+// fp16 bit pattern 0x6400 | q), 1024 is subtracted exactly, and one packed fp16 FMA forms
+// q * s + b with a single rounding.
 //
 // Loads are branch-free (rows past M or N read a clamped valid row whose results are not stored).
 // SwiGLU: a lane's two weight rows are the gate row and the matching up row of one output column.
@@ -30,17 +30,6 @@ namespace lfm3 {
 constexpr int BK = 64;
 constexpr int LDSK = BK + 8;  // padded X row stride (elements): 144-byte rows keep ds_read_b128 conflict-free
 constexpr int BN = 256;       // weight rows per block tile
-
-// Order of 8 consecutive k inside the staged X tile (per 16-byte group), matching the pair order of
-// the dequant: 4-bit (0,2)(4,6)(1,3)(5,7); 8-bit and 6-bit natural.
-template <int BITS> LFM3_DEV u32x4_v perm8(u32x4_v h) {
-  if constexpr (BITS == 4) {
-    return u32x4_v{__builtin_amdgcn_perm(h[1], h[0], 0x05040100u), __builtin_amdgcn_perm(h[3], h[2], 0x05040100u),
-                   __builtin_amdgcn_perm(h[1], h[0], 0x07060302u), __builtin_amdgcn_perm(h[3], h[2], 0x07060302u)};
-  } else {
-    return h;
-  }
-}
 
 constexpr uint32_t kMagic2 = 0x64006400u;  // fp16 (1024, 1024); 0x6400 | q == 1024 + q
 
@@ -61,17 +50,24 @@ LFM3_DEV __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Plane layout of a lane's 32 codes in the re-tiled copy: bytes per lane per plane, planes.
+template <int BITS> struct Planes {
+  static constexpr int PB = BITS == 6 ? 8 : 16;
+  static constexpr int NP = 4 * BITS / PB;
+};
+
 template <int BITS> LFM3_DEV void load_run(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, Run<BITS>& r) {
+  constexpr int PB = Planes<BITS>::PB;
   if constexpr (BITS == 6) {
 #pragma unroll
     for (int v = 0; v < 3; ++v) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 8 * v, soff, 0);
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 64 * PB * v, soff, 0);
       r.w[2 * v] = t[0]; r.w[2 * v + 1] = t[1];
     }
   } else {
 #pragma unroll
     for (int v = 0; v < BITS / 4; ++v) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * v, soff, 0);
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 64 * PB * v, soff, 0);
       r.w[4 * v] = t[0]; r.w[4 * v + 1] = t[1]; r.w[4 * v + 2] = t[2]; r.w[4 * v + 3] = t[3];
     }
   }
@@ -86,7 +82,7 @@ constexpr uint32_t kBytes64 = 0x64646464u;
 template <int BITS, int T> LFM3_DEV f16x8_v deq8(const Run<BITS>& r, f16x2_v s2, f16x2_v b2) {
   uint32_t p[4];
   if constexpr (BITS == 4) {
-    // nibbles 0, 2, 4, 6 and 1, 3, 5, 7 of the word as bytes
+    // nibbles 0, 2, 4, 6 (codes 0 .. 3 after the re-tiling) and 1, 3, 5, 7 (codes 4 .. 7) as bytes
     const uint32_t t0 = r.w[T] & 0x0F0F0F0Fu, t1 = (r.w[T] >> 4) & 0x0F0F0F0Fu;
     p[0] = deq2(__builtin_amdgcn_perm(kBytes64, t0, kSelLo), s2, b2);
     p[1] = deq2(__builtin_amdgcn_perm(kBytes64, t0, kSelHi), s2, b2);
@@ -116,11 +112,6 @@ template <int BITS, int T> LFM3_DEV f16x8_v deq8(const Run<BITS>& r, f16x2_v s2,
   return __builtin_bit_cast(f16x8_v, u32x4_v{p[0], p[1], p[2], p[3]});
 }
 
-LFM3_DEV f16x2_v bf16_pair(bf16_t b) {
-  const _Float16 h = (_Float16)bf2f(b);
-  return f16x2_v{h, h};
-}
-
 template <int BITS, int EPI, int BM>
 __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   constexpr int MT = BM / 32;                  // 32-row MFMA tiles per wave
@@ -132,19 +123,19 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   const int m0 = blockIdx.x * BM;
   const int K = a.w.k, N = a.w.n, M = a.m;
 
-  // the lane's two weight rows (MFMA column c32 of the wave's two 32-row tiles)
-  int wrow[2];
+  // the lane's two weight rows (MFMA column c32 of the wave's two 32-row tiles): their tiles in the
+  // re-tiled copy (past N: the last tile, whose results are not stored)
+  int wtile[2], wrow0;
   if constexpr (EPI == GEMM_SWIGLU) {
-    const int outc = blockIdx.y * (BN / 2) + 32 * wave + c32;
-    wrow[0] = outc;
-    wrow[1] = N / 2 + outc;
+    wtile[0] = blockIdx.y * (BN / 64) + wave;
+    wtile[1] = (N / 2) / 32 + wtile[0];
+    wrow0 = 32 * wtile[0] + c32;   // output column
   } else {
-    wrow[0] = min((int)blockIdx.y * BN + 64 * wave + c32, N - 1);
-    wrow[1] = min((int)blockIdx.y * BN + 64 * wave + 32 + c32, N - 1);
+    wtile[0] = min((int)blockIdx.y * (BN / 32) + 2 * wave, a.w.ntile - 1);
+    wtile[1] = min((int)blockIdx.y * (BN / 32) + 2 * wave + 1, a.w.ntile - 1);
+    wrow0 = 0;
   }
-  const uint32_t row_bytes = (uint32_t)K * BITS / 8;
-  const int ngr = K / a.w.group;
-  const int gshift = a.w.group == 32 ? 5 : 6;
+  constexpr uint32_t kTileBytes = 256u * BITS;    // one (32-row, 64-k) tile of codes
 
   // K tiles 0 .. nk-1 read x; with a remainder input, tiles nk .. 2nk-1 read x_lo against the same
   // weight tiles (Y = x W + x_lo W)
@@ -154,9 +145,8 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   const uint32_t xbytes = (uint32_t)((size_t)(M - 1) * a.ldx + K) * 2u;
   const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.x, xbytes);
   const __amdgpu_buffer_rsrc_t rxl = rsrc_of(a.x_lo ? a.x_lo : a.x, xbytes);
-  const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.w.q, (uint32_t)N * row_bytes);
-  const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.w.scales, (uint32_t)N * ngr * 2u);
-  const __amdgpu_buffer_rsrc_t rb = rsrc_of(a.w.biases, (uint32_t)N * ngr * 2u);
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.w.codes, (uint32_t)a.w.ntile * nk * kTileBytes);
+  const __amdgpu_buffer_rsrc_t rsb = rsrc_of(a.w.sb, (uint32_t)a.w.ntile * nk * 256u);
 
   // per-lane byte offsets, fixed over the K loop
   uint32_t xoff[AV];
@@ -166,11 +156,11 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
     const int r = idx >> 3, c8 = idx & 7;
     xoff[i] = ((uint32_t)min(m0 + r, M - 1) * (uint32_t)a.ldx + 8u * c8) * 2u;
   }
-  uint32_t qoff[2], soff[2];
+  uint32_t qoff[2], sboff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    qoff[j] = (uint32_t)wrow[j] * row_bytes + 32u * hf * BITS / 8;
-    soff[j] = ((uint32_t)wrow[j] * ngr + ((32 * hf) >> gshift)) * 2u;
+    qoff[j] = (uint32_t)wtile[j] * nk * kTileBytes + (uint32_t)lane * Planes<BITS>::PB;
+    sboff[j] = ((uint32_t)wtile[j] * nk * 64u + lane) * 4u;
   }
 
   u32x4_v areg[AV];
@@ -186,23 +176,21 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
     for (int i = 0; i < AV; ++i) {
       const int idx = tid + 256 * i;
       const int r = idx >> 3, c8 = idx & 7;
-      *(u32x4_v*)(&As[buf][r * LDSK + 8 * c8]) = perm8<BITS>(areg[i]);
+      *(u32x4_v*)(&As[buf][r * LDSK + 8 * c8]) = areg[i];
     }
   };
   // weight registers in two sets (even / odd K tiles), so that no value has to be copied across
   // the loop edge (a copy would make every iteration wait for the loads it just issued)
   struct WSet {
     Run<BITS> run[2];
-    uint32_t s[2], b[2];   // raw bf16 bits
+    uint32_t sb[2];   // fp16 (scale, bias)
   };
   auto load_w = [&](int kt, WSet& w) {
-    const uint32_t k0 = (uint32_t)(kt >= nk ? kt - nk : kt) * BK;
-    const uint32_t sg = (k0 >> gshift) * 2u;
+    const uint32_t kk = (uint32_t)(kt >= nk ? kt - nk : kt);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      load_run<BITS>(rq, qoff[j], k0 * BITS / 8, w.run[j]);
-      w.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[j], sg, 0);
-      w.b[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, soff[j], sg, 0);
+      load_run<BITS>(rq, qoff[j], kk * kTileBytes, w.run[j]);
+      w.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, sboff[j], kk * 256u, 0);
     }
   };
 
@@ -221,7 +209,8 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
     f16x8_v bop[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const f16x2_v s2 = bf16_pair((bf16_t)cur.s[j]), b2 = bf16_pair((bf16_t)cur.b[j]);
+      const f16x2_v sbv = __builtin_bit_cast(f16x2_v, cur.sb[j]);
+      const f16x2_v s2 = __builtin_shufflevector(sbv, sbv, 0, 0), b2 = __builtin_shufflevector(sbv, sbv, 1, 1);
       bop[j][0] = deq8<BITS, 0>(cur.run[j], s2, b2);
       bop[j][1] = deq8<BITS, 1>(cur.run[j], s2, b2);
       bop[j][2] = deq8<BITS, 2>(cur.run[j], s2, b2);
@@ -257,7 +246,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
     step(kt + 1, w1, w0);
   }
 
-  // epilogue: acc[i][j][v] is X row m0 + 32i + 8(v/4) + 4(lane/32) + v%4 against weight row wrow[j]
+  // epilogue: acc[i][j][v] is X row m0 + 32i + 8(v/4) + 4(lane/32) + v%4 against row c32 of tile wtile[j]
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -266,7 +255,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
       if (row >= M) continue;
       if constexpr (EPI == GEMM_SWIGLU) {
         const float g = acc[i][0][v], u = acc[i][1][v];
-        a.y[(size_t)row * a.ldy + wrow[0]] = f2h_sep(g / (1.f + __expf(-g)) * u);
+        a.y[(size_t)row * a.ldy + wrow0] = f2h_sep(g / (1.f + __expf(-g)) * u);
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -276,6 +265,55 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
       }
     }
   }
+}
+
+size_t gemm_codes_bytes(int n, int k, int bits) { return (size_t)((n + 31) / 32) * (k / BK) * 256u * bits; }
+size_t gemm_sb_bytes(int n, int k) { return (size_t)((n + 31) / 32) * (k / BK) * 256u; }
+
+// One block of 64 threads per (32-row, 64-k) tile; thread l writes lane l's codes and (scale,
+// bias) pair of the re-tiled copy (the layout is described with GemmW).
+template <int BITS>
+__global__ void __launch_bounds__(64) k_repack(QLinear w, uint8_t* codes, uint32_t* sb, int nk) {
+  constexpr int PB = Planes<BITS>::PB, NP = Planes<BITS>::NP;
+  const int blk = blockIdx.x, lane = threadIdx.x;
+  const int nt = blk / nk, kt = blk - nt * nk;
+  const int row = min(nt * 32 + (lane & 31), w.n - 1);
+  const int k0 = kt * BK + 32 * (lane >> 5);
+  const uint32_t* src = (const uint32_t*)(w.q + (size_t)row * ((size_t)w.k * BITS / 8) + (size_t)k0 * BITS / 8);
+  uint32_t v[BITS];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) v[i] = src[i];
+  if constexpr (BITS == 4) {
+    // code j of each word to nibble 0, 2, 4, 6, 1, 3, 5, 7
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t o = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o |= ((v[i] >> (4 * j)) & 0xFu) << (4 * (j < 4 ? 2 * j : 2 * (j - 4) + 1));
+      v[i] = o;
+    }
+  }
+  uint8_t* dst = codes + (size_t)blk * 256u * BITS + (size_t)lane * PB;
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int d = 0; d < PB / 4; ++d) ((uint32_t*)(dst + (size_t)p * 64 * PB))[d] = v[p * (PB / 4) + d];
+  const int ngr = w.k / w.group;
+  const int g = k0 / w.group;
+  const f16_t s16 = f2h(bf2f(w.scales[(size_t)row * ngr + g])), b16 = f2h(bf2f(w.biases[(size_t)row * ngr + g]));
+  sb[(size_t)blk * 64 + lane] = (uint32_t)s16 | ((uint32_t)b16 << 16);
+}
+
+hipError_t launch_repack_gemm(hipStream_t s, const QLinear& w, uint8_t* codes, uint32_t* sb) {
+  if (w.k % (2 * BK) || w.group % 32 || (uintptr_t)codes % 16 || (uintptr_t)sb % 4) return hipErrorInvalidValue;
+  const int nk = w.k / BK, nt = (w.n + 31) / 32;
+  switch (w.bits) {
+    case 4: hipLaunchKernelGGL(k_repack<4>, dim3(nt * nk), dim3(64), 0, s, w, codes, sb, nk); break;
+    case 6: hipLaunchKernelGGL(k_repack<6>, dim3(nt * nk), dim3(64), 0, s, w, codes, sb, nk); break;
+    case 8: hipLaunchKernelGGL(k_repack<8>, dim3(nt * nk), dim3(64), 0, s, w, codes, sb, nk); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int BITS, int BMT>
@@ -301,7 +339,7 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
   if (a.m <= 0) return hipSuccess;
   // 16-byte rows of X, an even number of K tiles, 32-code runs inside one group, whole SwiGLU tiles
   if (a.w.k % (2 * BK) || a.w.group % 32 || a.ldx % 8 || (uintptr_t)a.x % 16 || (uintptr_t)a.x_lo % 16 ||
-      (a.epi == GEMM_SWIGLU && a.w.n % BN))
+      a.w.ntile != (a.w.n + 31) / 32 || (a.epi == GEMM_SWIGLU && a.w.n % BN))
     return hipErrorInvalidValue;
   switch (a.w.bits) {
     case 4: return launch_bits<4>(s, a);

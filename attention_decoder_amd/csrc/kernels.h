@@ -126,10 +126,27 @@ hipError_t launch_gemv(hipStream_t s, const GemvArgs& a);
 // ---- k_gemm.hip --------------------------------------------------------------------------------
 
 enum GemmEpi { GEMM_STORE = 0, GEMM_SWIGLU = 1 };
+
+// A quantized linear re-tiled for the prefill GEMM (built once from the blob's linear by
+// launch_repack_gemm). Tile (t, kt) covers weight rows [32t, 32t + 32) (rows past N repeat row
+// N - 1) and k [64kt, 64kt + 64); lane l of a wave holds row 32t + l % 32, k 64kt + 32(l / 32) ..
+// + 31: its codes (16 B at 4-bit, 32 B at 8-bit as two 16-byte planes, 24 B at 6-bit as three
+// 8-byte planes; each plane is 64 lanes contiguous) and one dword of fp16 (scale, bias) for its
+// group. 4-bit codes are reordered inside each 32-bit word (code j of the word at nibble
+// 0, 2, 4, 6, 1, 3, 5, 7 for j = 0 .. 7) so that the byte-permute unpack yields k in order.
+struct GemmW {
+  const uint8_t* codes;
+  const uint32_t* sb;
+  int32_t n, k, bits, group, ntile;
+};
+size_t gemm_codes_bytes(int n, int k, int bits);
+size_t gemm_sb_bytes(int n, int k);
+hipError_t launch_repack_gemm(hipStream_t s, const QLinear& w, uint8_t* codes, uint32_t* sb);
+
 // Y[m, n] = sum_k X[m, k] * f16(q[n, k] * s + bias), MFMA fp16 with fp32 accumulation.
 // STORE writes fp32 yf; SWIGLU writes fp16 y.
 struct GemmArgs {
-  QLinear w;
+  GemmW w;
   const f16_t* x;   // [M, ldx]
   const f16_t* x_lo;  // nullable, [M, ldx]: fp16 remainder of x; Y = (x + x_lo) W as two K passes
   int ldx;

@@ -154,10 +154,35 @@ struct Layout {
   size_t cos_f, sin_f, cos_s, sin_s;
   size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
   size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, xf, part, keys, counters;
+  size_t gemm_w, gemm_w_bytes;   // re-tiled copies of every prefill GEMM weight
   size_t total;
   int max_rows, max_pages, ring_rows, max_splits, big_ld;
   size_t ring_layer, pool_layer, conv_slot;
 };
+
+// (N, K) of every prefill GEMM weight, in layer order: the mixer's input and output linears, then
+// w13 and w2.
+std::vector<std::pair<int, int>> gemm_shapes(const lfm3_config& c) {
+  std::vector<std::pair<int, int>> v;
+  for (int i = 0; i < c.n_layers; ++i) {
+    if (c.layer_type[i] == LFM3_LAYER_CONV) {
+      v.push_back({3 * c.hidden, c.hidden});
+      v.push_back({c.hidden, c.hidden});
+    } else {
+      v.push_back({qkvg_rows(c), c.hidden});
+      v.push_back({c.hidden, c.n_q_heads * c.head_dim});
+    }
+    v.push_back({2 * c.ffn, c.hidden});
+    v.push_back({c.hidden, c.ffn});
+  }
+  return v;
+}
+
+// codes then (scale, bias) pairs, each 256-byte aligned
+size_t gemm_w_bytes(int n, int k, int bits) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  return up(gemm_codes_bytes(n, k, bits)) + up(gemm_sb_bytes(n, k));
+}
 
 Layout make_layout(const lfm3_config& c) {
   Layout L{};
@@ -201,6 +226,9 @@ Layout make_layout(const lfm3_config& c) {
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
   L.keys = take((size_t)std::max(kMaxBatch, (int)R) * 8);
   L.counters = take((size_t)c.max_slots * c.n_kv_heads * 4);
+  L.gemm_w_bytes = 0;
+  for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits);
+  L.gemm_w = take(L.gemm_w_bytes);
   L.total = off;
   return L;
 }
@@ -210,6 +238,7 @@ struct LayerW {
   int sub;  // index among layers of the same type
   const bf16_t *op_norm, *post_op, *ffn_norm, *post_ffn, *conv_kernel, *q_norm, *k_norm;
   QLinear mix_in, mix_out, w13, w2;
+  GemmW g_in, g_out, g13, g2;   // their re-tiled copies for the prefill GEMM
 };
 
 }  // namespace
@@ -239,6 +268,7 @@ struct lfm3_ctx {
   int capture_rows = 0;
   std::string err;
   std::unordered_map<std::string, QLinear> lin_by_name;
+  std::unordered_map<std::string, GemmW> gemm_by_name;
   bool prof = false;
   bool prof_open = false;    // the last record's run is still open (its end event not recorded)
   std::vector<ProfRec> prof_recs;
@@ -342,6 +372,10 @@ hipError_t timed(lfm3_ctx* ctx, int kind, double bytes, double flops, F fn) {
 double lin_bytes(const QLinear& w) {
   return (double)w.n * ((double)w.k * w.bits / 8.0 + 4.0 * w.k / w.group);
 }
+// the same algorithmic bytes for the re-tiled copy (the quantized weight itself)
+double lin_bytes(const GemmW& w) {
+  return (double)w.n * ((double)w.k * w.bits / 8.0 + 4.0 * w.k / w.group);
+}
 
 #define LFM3_TRY(expr)                                                                      \
   do {                                                                                      \
@@ -385,7 +419,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
 
   // fp32 output (STORE) or fp16 SwiGLU output
   // x_lo: the input is carried as the fp16 pair in + x_lo (two K passes; counted as such)
-  auto linear = [&](const QLinear& w, const f16_t* in, int ldin, float* outf, f16_t* outb, int ldout, int epi,
+  auto linear = [&](const GemmW& w, const f16_t* in, int ldin, float* outf, f16_t* outb, int ldout, int epi,
                     const f16_t* x_lo = nullptr) -> hipError_t {
     const double out_bytes = epi == GEMM_SWIGLU ? (double)M * (w.n / 2) * 2.0 : (double)M * w.n * 4.0;
     const double passes = x_lo ? 2.0 : 1.0;
@@ -411,7 +445,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
     LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, na); }));
 
     if (lw.type == LFM3_LAYER_CONV) {
-      LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE, xlo));
+      LFM3_TRY(linear(lw.g_in, x, H, big, nullptr, L.big_ld, GEMM_STORE, xlo));
       ConvArgs ca{};
       ca.bcx = big; ca.ld = L.big_ld; ca.kernel = lw.conv_kernel;
       ca.state = ctx->at<f16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
@@ -420,7 +454,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
       LFM3_TRY(timed(ctx, LFM3_PROF_CONV, (double)M * H * (12 + 2) + 2.0 * H * 2 * (c.conv_taps - 1), 0,
                      [&] { return launch_conv(s, ca); }));
     } else {
-      LFM3_TRY(linear(lw.mix_in, x, H, big, nullptr, L.big_ld, GEMM_STORE, xlo));
+      LFM3_TRY(linear(lw.g_in, x, H, big, nullptr, L.big_ld, GEMM_STORE, xlo));
       const bool full = lw.type == LFM3_LAYER_FULL;
       QkRopeArgs qa{};
       qa.qkvg = big; qa.ld = L.big_ld; qa.q_norm = lw.q_norm; qa.k_norm = lw.k_norm;
@@ -446,14 +480,14 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
         LFM3_TRY(timed(ctx, LFM3_PROF_ATTN_PREFILL, 0, fl, [&] { return launch_attn_prefill(s, aa); }));
       }
     }
-    LFM3_TRY(linear(lw.mix_out, mix, H, m, nullptr, H, GEMM_STORE));
+    LFM3_TRY(linear(lw.g_out, mix, H, m, nullptr, H, GEMM_STORE));
     // h += post_operator_norm(m); x = ffn_norm(h)
     NormArgs nb{};
     nb.h_in = h; nb.h_out = h; nb.x_out = x; nb.rows = M; nb.hidden = H; nb.eps = c.norm_eps;
     nb.m = m; nb.w_post = lw.post_op; nb.w_pre = lw.ffn_norm;
     LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, nb); }));
-    LFM3_TRY(linear(lw.w13, x, H, nullptr, sb, c.ffn, GEMM_SWIGLU));
-    LFM3_TRY(linear(lw.w2, sb, c.ffn, m, nullptr, H, GEMM_STORE));
+    LFM3_TRY(linear(lw.g13, x, H, nullptr, sb, c.ffn, GEMM_SWIGLU));
+    LFM3_TRY(linear(lw.g2, sb, c.ffn, m, nullptr, H, GEMM_STORE));
   }
   NormArgs nf{};
   nf.h_in = h; nf.h_out = h; nf.x_out = xf; nf.rows = M; nf.hidden = H; nf.eps = c.norm_eps;
@@ -722,6 +756,36 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
   }
   if (c.has_embedding) ctx->emb = lin("embedding", c.vocab, c.hidden, c.embed_bits, c.embed_group);
   ctx->emb_norm = bf("embedding_norm");
+
+  // re-tiled copies of the prefill GEMM weights, in the order gemm_shapes lists them
+  {
+    size_t goff = L.gemm_w;
+    hipError_t e = hipSuccess;
+    auto retile = [&](const QLinear& q, const std::string& name) {
+      GemmW g{};
+      uint8_t* codes = ctx->at<uint8_t>(goff);
+      uint32_t* sbp = (uint32_t*)(codes + (gemm_codes_bytes(q.n, q.k, q.bits) + 255) / 256 * 256);
+      goff += gemm_w_bytes(q.n, q.k, q.bits);
+      g.codes = codes; g.sb = sbp; g.n = q.n; g.k = q.k; g.bits = q.bits; g.group = q.group; g.ntile = (q.n + 31) / 32;
+      if (e == hipSuccess) e = launch_repack_gemm(ctx->stream, q, codes, sbp);
+      ctx->gemm_by_name[name] = g;
+      return g;
+    };
+    for (int i = 0; i < c.n_layers; ++i) {
+      LayerW& lw = ctx->layers[i];
+      const std::string p = "layers." + std::to_string(i) + ".";
+      const bool conv = lw.type == LFM3_LAYER_CONV;
+      lw.g_in = retile(lw.mix_in, p + (conv ? "conv.in_proj" : "attn.qkvg_proj"));
+      lw.g_out = retile(lw.mix_out, p + (conv ? "conv.out_proj" : "attn.o_proj"));
+      lw.g13 = retile(lw.w13, p + "ffn.w13");
+      lw.g2 = retile(lw.w2, p + "ffn.w2");
+    }
+    if (e != hipSuccess || goff != L.gemm_w + L.gemm_w_bytes) {
+      delete ctx;
+      g_err = e != hipSuccess ? std::string("GEMM weight re-tiling failed: ") + hipGetErrorString(e) : "GEMM weight layout mismatch";
+      return LFM3_ERR_DEVICE;
+    }
+  }
   ctx->len.assign(c.max_slots, 0);
   ctx->pages.assign(c.max_slots, {});
   for (int p = c.n_pages - 1; p >= 0; --p) ctx->free_pages.push_back(p);
@@ -900,15 +964,14 @@ lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uin
     GemvArgs g{};
     g.w = w; g.x = x_dev; g.ldx = w.k; g.batch = rows; g.epi = GEMV_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2;
     LFM3_TRY(launch_gemv(ctx->stream, g));
-  } else if (path == 3) {
+  } else if (path == 1 || path == 3) {
     if (rows < 1) return ctx->fail(LFM3_ERR_ARG, "GEMM rows must be >= 1");
+    auto gt = ctx->gemm_by_name.find(name);
+    if (gt == ctx->gemm_by_name.end()) return ctx->fail(LFM3_ERR_ARG, std::string(name) + " has no GEMM copy (the head is decode-only)");
     GemmArgs g{};
-    g.w = w; g.x = x_dev; g.ldx = w.k; g.m = rows; g.epi = GEMM_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2;
-    LFM3_TRY(launch_gemm(ctx->stream, g));
-  } else if (path == 1) {
-    if (rows < 1) return ctx->fail(LFM3_ERR_ARG, "GEMM rows must be >= 1");
-    GemmArgs g{};
-    g.w = w; g.x = x_dev; g.ldx = w.k; g.m = rows; g.epi = GEMM_STORE; g.yf = y_dev; g.ldy = w.n;
+    g.w = gt->second; g.x = x_dev; g.ldx = w.k; g.m = rows;
+    if (path == 3) { g.epi = GEMM_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2; }
+    else { g.epi = GEMM_STORE; g.yf = y_dev; g.ldy = w.n; }
     LFM3_TRY(launch_gemm(ctx->stream, g));
   } else {
     return ctx->fail(LFM3_ERR_ARG, "path must be 0..3");

@@ -108,3 +108,35 @@ def test_swiglu_epilogues(eng, weights):
         want = ab[:, :F] / (1 + np.exp(-ab[:, :F])) * ab[:, F:]
         rel = np.linalg.norm(y - want) / np.linalg.norm(want)
         assert rel < 2e-3, (path, rel)
+
+
+@pytest.mark.parametrize("bits,group", [(8, 64), (6, 64), (4, 32)])
+def test_gemm_other_schemes(bits, group):
+    """The prefill GEMM (re-tiled weights) at 8-bit, 6-bit and 4-bit g32 on the slice's shapes, at a
+    ragged row count: the float64 product with the fp16-rounded dequantised weights (SwiGLU for
+    w13)."""
+    import torch
+    from attention_decoder_amd import synth
+    from attention_decoder_amd.lfm3 import Engine
+    cfg = synth.slice3_config(bits=bits, group=group, max_slots=1, max_chunk=512)
+    blob = synth.cached_blob(cfg, seed=0)
+    eng = Engine(cfg, blob)
+    b = ref.Blob(blob)
+    try:
+        for name, path in [("layers.0.conv.in_proj", 1), ("layers.0.ffn.w2", 1), ("layers.2.attn.qkvg_proj", 1),
+                           ("layers.1.ffn.w13", 3)]:
+            w = ref.load_linear(b, name, bits, group)
+            x, xd = _x(torch, 300, w.shape[1], bits + group)
+            y = eng.linear(name, xd, path).float().cpu().numpy().astype(np.float64)
+            ab = x.astype(np.float64) @ ref.f16_round(w).T
+            if path == 3:
+                F = w.shape[0] // 2
+                want = ab[:, :F] / (1 + np.exp(-ab[:, :F])) * ab[:, F:]
+                tol = 2e-3
+            else:
+                want, tol = ab, 2e-5
+            err = np.abs(y - want).max() / np.abs(want).max()
+            print(f"{bits}-bit g{group} {name}: max rel err {err:.2e}")
+            assert err < tol, (bits, group, name, err)
+    finally:
+        eng.close()
