@@ -78,7 +78,8 @@ typedef struct lfm3_config {
 typedef struct lfm3_ctx lfm3_ctx;
 
 /* Sizes the caller must allocate: the exact weight-blob size this config implies and the device
- * workspace (KV pool, sliding rings, conv states, RoPE tables, activation scratch). Host only. */
+ * workspace (KV pool, sliding rings, conv states, RoPE tables, activation scratch, and a re-tiled
+ * copy of every prefill GEMM weight: about the quantized size of the layers' linears). Host only. */
 lfm3_status lfm3_query_sizes(const lfm3_config* cfg, size_t* blob_bytes, size_t* workspace_bytes);
 
 /* Admission of a weight blob held in host memory: magic, version, every tensor's name, dtype,
@@ -89,7 +90,9 @@ lfm3_status lfm3_validate_blob(const lfm3_config* cfg, const void* blob_host, si
 
 /* Create a context. blob_dev holds the blob (validated by reading its header back); workspace_dev
  * holds at least workspace_bytes from lfm3_query_sizes. hip_stream is a hipStream_t (NULL = the
- * default stream). Zeroes every slot and uploads the RoPE tables (built in float64, stored fp32). */
+ * default stream). Zeroes every slot, uploads the RoPE tables (built in float64, stored fp32) and
+ * enqueues the re-tiling of the prefill GEMM weights from the blob on hip_stream (the blob must
+ * stay unchanged while the context lives). */
 lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blob_bytes,
                         void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                         lfm3_ctx** out);
