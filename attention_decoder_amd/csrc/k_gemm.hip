@@ -138,9 +138,11 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   constexpr uint32_t kTileBytes = 256u * BITS;    // one (32-row, 64-k) tile of codes
 
   // K tiles 0 .. nk-1 read x; with a remainder input, tiles nk .. 2nk-1 read x_lo against the same
-  // weight tiles (Y = x W + x_lo W)
+  // weight tiles (Y = x W + x_lo W). With a K split, block z runs tiles [z nk/2, (z + 1) nk/2).
   const int nk = K / BK;
-  const int nkt = a.x_lo ? 2 * nk : nk;
+  const int kt0 = blockIdx.z * (nk / 2);
+  const int nkt = a.yf2 ? kt0 + nk / 2 : (a.x_lo ? 2 * nk : nk);   // end of this block's tiles
+  float* const yout = blockIdx.z ? a.yf2 : a.yf;
 
   const uint32_t xbytes = (uint32_t)((size_t)(M - 1) * a.ldx + K) * 2u;
   const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.x, xbytes);
@@ -236,12 +238,12 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   };
 
   WSet w0, w1;
-  load_x(0);
-  load_w(0, w0);
+  load_x(kt0);
+  load_w(kt0, w0);
   store_x(0);
-  load_x(1);
+  load_x(kt0 + 1);
   __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {   // nkt is even (K % 128 == 0)
+  for (int kt = kt0; kt < nkt; kt += 2) {   // kt0 and nkt are even
     step(kt, w0, w1);
     step(kt + 1, w1, w0);
   }
@@ -260,7 +262,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = blockIdx.y * BN + 64 * wave + 32 * j + c32;
-          if (col < N) a.yf[(size_t)row * a.ldy + col] = acc[i][j][v];
+          if (col < N) yout[(size_t)row * a.ldy + col] = acc[i][j][v];
         }
       }
     }
@@ -322,7 +324,7 @@ static void launch_bm(hipStream_t s, const GemmArgs& a) {
   if (a.epi == GEMM_SWIGLU) {
     hipLaunchKernelGGL((k_gemm<BITS, GEMM_SWIGLU, BMT>), dim3(gm, a.w.n / BN), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_gemm<BITS, GEMM_STORE, BMT>), dim3(gm, (a.w.n + BN - 1) / BN), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<BITS, GEMM_STORE, BMT>), dim3(gm, (a.w.n + BN - 1) / BN, a.yf2 ? 2 : 1), dim3(256), 0, s, a);
   }
 }
 
@@ -341,6 +343,8 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
   if (a.w.k % (2 * BK) || a.w.group % 32 || a.ldx % 8 || (uintptr_t)a.x % 16 || (uintptr_t)a.x_lo % 16 ||
       a.w.ntile != (a.w.n + 31) / 32 || (a.epi == GEMM_SWIGLU && a.w.n % BN))
     return hipErrorInvalidValue;
+  // a K split: two halves of an even number of K tiles, plain STORE
+  if (a.yf2 && ((a.w.k / BK) % 4 || a.x_lo || a.epi != GEMM_STORE)) return hipErrorInvalidValue;
   switch (a.w.bits) {
     case 4: return launch_bits<4>(s, a);
     case 6: return launch_bits<6>(s, a);

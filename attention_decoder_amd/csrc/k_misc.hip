@@ -108,6 +108,16 @@ __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
     bf16x8_to_f32(load_u16x8(wpo_p + 8 * v), wpo[j]);
     bf16x8_to_f32(load_u16x8(a.w_pre + 8 * v), wpr[j]);
   }
+  if (a.m && a.m2) {
+#pragma unroll
+    for (int j = 0; j < kVecBlocks; ++j) {
+      const int v = min((int)threadIdx.x + 256 * j, nv - 1);
+      float m2v[8];
+      load_f32x8(a.m2 + base + 8 * v, m2v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mv[j][e] = mv[j][e] + m2v[e];
+    }
+  }
   bool ok[kVecBlocks];
 #pragma unroll
   for (int j = 0; j < kVecBlocks; ++j) ok[j] = (int)threadIdx.x + 256 * j < nv;

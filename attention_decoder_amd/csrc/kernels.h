@@ -21,6 +21,7 @@ hipError_t launch_bf16_to_f32(hipStream_t s, const bf16_t* in, int rows, int col
 struct NormArgs {
   const float* h_in;
   const float* m;
+  const float* m2;  // nullable: the mixer/FFN output is m + m2 (two K-half partials, added in that order)
   const bf16_t* w_post;
   const bf16_t* w_pre;
   float* h_out;
@@ -154,6 +155,8 @@ struct GemmArgs {
   int epi;
   f16_t* y;         // [M, ldy]
   float* yf;
+  float* yf2;       // nullable (STORE, no x_lo): K is split in two halves run by separate blocks; the
+                    // first half's sums go to yf, the second half's to yf2 (the consumer adds them)
   int ldy;
 };
 hipError_t launch_gemm(hipStream_t s, const GemmArgs& a);

@@ -153,7 +153,7 @@ bool check_config(const lfm3_config& c, std::string& err) {
 struct Layout {
   size_t cos_f, sin_f, cos_s, sin_s;
   size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
-  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, xf, part, keys, counters;
+  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, m2, xf, part, keys, counters;
   size_t gemm_w, gemm_w_bytes;   // re-tiled copies of every prefill GEMM weight
   size_t total;
   int max_rows, max_pages, ring_rows, max_splits, big_ld;
@@ -222,6 +222,7 @@ Layout make_layout(const lfm3_config& c) {
   L.mix = take(R * H * 2);
   L.qrot = take(R * c.n_q_heads * kHeadDim * 2);
   L.m = take(R * H * 4);
+  L.m2 = take(R * H * 4);
   L.xf = take(R * H * 2);
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
   L.keys = take((size_t)std::max(kMaxBatch, (int)R) * 8);
@@ -414,20 +415,25 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
   f16_t* mix = ctx->at<f16_t>(L.mix);
   f16_t* qrot = ctx->at<f16_t>(L.qrot);
   float* m = ctx->at<float>(L.m);
+  float* m2 = ctx->at<float>(L.m2);
   f16_t* xf = ctx->at<f16_t>(L.xf);
   f16_t* xlo = ctx->at<f16_t>(L.xlo);
 
   // fp32 output (STORE) or fp16 SwiGLU output
   // x_lo: the input is carried as the fp16 pair in + x_lo (two K passes; counted as such)
+  // outf2: the hidden-width outputs (mixer output projection, w2) run as two K halves, whose
+  // partial sums (outf, outf2) the next residual norm adds; the narrow N would otherwise give one
+  // block per CU
   auto linear = [&](const GemmW& w, const f16_t* in, int ldin, float* outf, f16_t* outb, int ldout, int epi,
-                    const f16_t* x_lo = nullptr) -> hipError_t {
+                    const f16_t* x_lo = nullptr, float* outf2 = nullptr) -> hipError_t {
     const double out_bytes = epi == GEMM_SWIGLU ? (double)M * (w.n / 2) * 2.0 : (double)M * w.n * 4.0;
     const double passes = x_lo ? 2.0 : 1.0;
     const double bytes = lin_bytes(w) + passes * M * w.k * 2.0 + out_bytes;
     const double flops = passes * 2.0 * M * (double)w.n * w.k;
     GemmArgs g{};
-    g.w = w; g.x = in; g.x_lo = x_lo; g.ldx = ldin; g.m = M; g.epi = epi; g.y = outb; g.yf = outf; g.ldy = ldout;
-    return timed(ctx, LFM3_PROF_GEMM, bytes, flops, [&] { return launch_gemm(s, g); });
+    g.w = w; g.x = in; g.x_lo = x_lo; g.ldx = ldin; g.m = M; g.epi = epi; g.y = outb; g.yf = outf; g.yf2 = outf2;
+    g.ldy = ldout;
+    return timed(ctx, LFM3_PROF_GEMM, bytes + (outf2 ? (double)M * w.n * 4.0 : 0.0), flops, [&] { return launch_gemm(s, g); });
   };
   const double norm_bytes = (double)M * H * (4 + 4 + 4 + 2);
   auto cap = [&](int layer) -> float* {
@@ -441,7 +447,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
     NormArgs na{};
     na.h_in = h; na.h_out = h; na.x_out = x; na.x_lo = xlo; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
     na.w_pre = lw.op_norm;
-    if (i > 0) { na.m = m; na.w_post = ctx->layers[i - 1].post_ffn; na.capture = cap(i - 1); }
+    if (i > 0) { na.m = m; na.m2 = m2; na.w_post = ctx->layers[i - 1].post_ffn; na.capture = cap(i - 1); }
     LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, na); }));
 
     if (lw.type == LFM3_LAYER_CONV) {
@@ -480,18 +486,18 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
         LFM3_TRY(timed(ctx, LFM3_PROF_ATTN_PREFILL, 0, fl, [&] { return launch_attn_prefill(s, aa); }));
       }
     }
-    LFM3_TRY(linear(lw.g_out, mix, H, m, nullptr, H, GEMM_STORE));
+    LFM3_TRY(linear(lw.g_out, mix, H, m, nullptr, H, GEMM_STORE, nullptr, m2));
     // h += post_operator_norm(m); x = ffn_norm(h)
     NormArgs nb{};
     nb.h_in = h; nb.h_out = h; nb.x_out = x; nb.rows = M; nb.hidden = H; nb.eps = c.norm_eps;
-    nb.m = m; nb.w_post = lw.post_op; nb.w_pre = lw.ffn_norm;
-    LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, nb); }));
+    nb.m = m; nb.m2 = m2; nb.w_post = lw.post_op; nb.w_pre = lw.ffn_norm;
+    LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes + (double)M * H * 4, 0, [&] { return launch_resid_norm(s, nb); }));
     LFM3_TRY(linear(lw.g13, x, H, nullptr, sb, c.ffn, GEMM_SWIGLU));
-    LFM3_TRY(linear(lw.g2, sb, c.ffn, m, nullptr, H, GEMM_STORE));
+    LFM3_TRY(linear(lw.g2, sb, c.ffn, m, nullptr, H, GEMM_STORE, nullptr, m2));
   }
   NormArgs nf{};
   nf.h_in = h; nf.h_out = h; nf.x_out = xf; nf.rows = M; nf.hidden = H; nf.eps = c.norm_eps;
-  nf.m = m; nf.w_post = ctx->layers[c.n_layers - 1].post_ffn; nf.w_pre = ctx->emb_norm;
+  nf.m = m; nf.m2 = m2; nf.w_post = ctx->layers[c.n_layers - 1].post_ffn; nf.w_pre = ctx->emb_norm;
   nf.capture = cap(c.n_layers - 1);
   nf.x_copy = hidden_out;
   LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, nf); }));
