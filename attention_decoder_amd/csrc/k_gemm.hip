@@ -204,10 +204,18 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // one K tile: its weights (in `cur`) into operand registers, the next tile's weight loads into
-  // `nxt`, the next tile's X (loaded one tile ago) into the other LDS buffer, the X loads of the
-  // tile after that, then the MFMAs
+  // one K tile: the next tile's X (loaded one tile ago) into the other LDS buffer, the X loads of
+  // the tile after that and the next tile's weight loads (into `nxt`) go out first, then this
+  // tile's weights (in `cur`) are dequantised into operand registers and the MFMAs run. All loads
+  // are unconditional (past the end they re-read the last tile, unused): a branch would make the
+  // compiler's wait counting assume the other path's loads are still in flight. The scheduling
+  // barrier keeps the compiler from sinking the loads behind the MFMAs, which would expose their
+  // latency at the next tile's store.
   auto step = [&](int kt, const WSet& cur, WSet& nxt) {
+    store_x((kt + 1) & 1);
+    load_x(min(kt + 2, nkt - 1));
+    load_w(min(kt + 1, nkt - 1), nxt);
+    __builtin_amdgcn_sched_barrier(0);
     f16x8_v bop[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -218,11 +226,6 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
       bop[j][2] = deq8<BITS, 2>(cur.run[j], s2, b2);
       bop[j][3] = deq8<BITS, 3>(cur.run[j], s2, b2);
     }
-    // unconditional (past the end they re-read the last tile, unused): a branch here would make
-    // the compiler's wait counting assume the other path's loads are still in flight
-    load_w(min(kt + 1, nkt - 1), nxt);
-    store_x((kt + 1) & 1);
-    load_x(min(kt + 2, nkt - 1));
     const f16_t* at = As[kt & 1];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
