@@ -282,8 +282,8 @@ hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// decode: block (split, kv head, row); a split is split_keys consecutive visible keys (a multiple
-// of 64), walked in 64-key tiles with an online softmax, the next tile's K/V loads (and the page
+// decode: block (split, kv head, row); a split is attn_decode_split_keys(row) consecutive visible
+// keys (a multiple of 64), walked in 64-key tiles with an online softmax, the next tile's K/V loads (and the page
 // ids of the one after) in flight while a tile is computed. The prologue normalises and rotates
 // the block's 4 query heads from the raw qkvg row; the block whose split holds the current
 // position also forms its key and value (per-head k RMSNorm + RoPE) and stores them in the cache.
@@ -296,18 +296,6 @@ hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
 constexpr int TILE = 64;
 constexpr int KVS = kHeadDim + 8;   // LDS row stride of the K and V tiles (elements)
 constexpr int kMaxMergeSplits = 512;
-#ifndef LFM3_FULL_SPLIT_KEYS
-#define LFM3_FULL_SPLIT_KEYS 128
-#endif
-constexpr int kFullSplitKeys = LFM3_FULL_SPLIT_KEYS;  // keys per split on full layers (2 tiles)
-
-// Sliding layers (<= window keys) split into single tiles, so all four 64-key tiles of a 256-key
-// window run in parallel blocks; full layers use 2-tile splits (fewer partials to merge).
-int attn_decode_split_keys(bool sliding, int window) {
-  (void)window;
-  return sliding ? TILE : kFullSplitKeys;
-}
-
 template <bool PAGED>
 LFM3_DEV size_t kv_off(const KvRef& kv, int slot, int pos, int page, int kvh, int n_kv) {
   if constexpr (PAGED) return (((size_t)page * n_kv + kvh) * kPageTokens + (pos % kPageTokens)) * kHeadDim;
@@ -326,8 +314,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int slot = a.rows.slot[r], pos = a.rows.pos[r];
   const int nq = a.n_q_heads, nkv = a.n_kv_heads;
-  const int SK = a.split_keys;
   const int k_lo = a.window > 0 ? max(0, pos - (a.window - 1)) : 0;
+  const int SK = attn_decode_split_keys(a.window > 0, pos - k_lo + 1);
   const int ns = (pos - k_lo) / SK + 1;
   if (split >= ns) return;
   const int j0 = k_lo + split * SK;
@@ -541,7 +529,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
 
 hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a) {
   if (a.rows.n <= 0) return hipSuccess;
-  if (a.max_splits > kMaxMergeSplits || a.split_keys % TILE || a.split_keys <= 0) return hipErrorInvalidValue;
+  if (a.max_splits > kMaxMergeSplits) return hipErrorInvalidValue;
   if (a.kv.ring == 0)
     hipLaunchKernelGGL(k_attn_decode<true>, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
   else

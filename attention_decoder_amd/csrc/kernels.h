@@ -180,8 +180,9 @@ struct AttnArgs {
 hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a);
 
 // Decode attention for one row per slot, fused with the q/k norm + RoPE of the step's own query
-// and key and the store of its key and value; split-K over 64-key splits with the merge done by
-// the last block of each (row, kv head) (counters start at zero and are left at zero).
+// and key and the store of its key and value; split-K (attn_decode_split_keys keys per split) with
+// the merge done by the last block of each (row, kv head) (counters start at zero and are left at
+// zero).
 struct AttnDecodeArgs {
   const float* qkvg;   // raw fp32 linear output [rows, ld]: q | k | v | g
   int ld;
@@ -199,10 +200,19 @@ struct AttnDecodeArgs {
   float* part;         // [rows, n_q_heads, max_splits, kPartStride]
   int* counters;       // [rows, n_kv_heads]
   int max_splits;      // grid extent: the most splits any row needs
-  int split_keys;      // keys per split (a multiple of 64): attn_decode_split_keys
 };
 constexpr int kPartStride = kHeadDim + 4;   // split partial: o [128], max, sum, 2 pad (16-byte rows)
 hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a);
-int attn_decode_split_keys(bool sliding, int window);
+
+// Keys per split of a decode row with `keys` visible keys (a multiple of the 64-key tile): single
+// tiles on sliding layers (the four tiles of a 256-key window run in parallel blocks); on full
+// layers two tiles while that gives at most 32 splits, beyond that the keys in 32 equal splits, so
+// a long row is at most 32 blocks per kv head and its merge reads at most 32 partials. It depends
+// on the row alone, which keeps a row's result independent of the batch it is decoded in.
+LFM3_HOST_DEV int attn_decode_split_keys(bool sliding, int keys) {
+  if (sliding) return 64;
+  const int s = ((keys + 31) / 32 + 63) / 64 * 64;
+  return s > 128 ? s : 128;
+}
 
 }  // namespace lfm3

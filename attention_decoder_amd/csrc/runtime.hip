@@ -198,7 +198,7 @@ Layout make_layout(const lfm3_config& c) {
   L.max_rows = std::max(c.max_chunk, c.max_slots);
   L.max_pages = (c.max_ctx + kPageTokens - 1) / kPageTokens;
   L.ring_rows = c.window + c.max_chunk;
-  L.max_splits = std::max((c.max_ctx + 127) / 128, c.window / 64) + 1;   // full: 128-key splits, sliding: 64
+  L.max_splits = std::max(32, c.window / 64) + 1;   // attn_decode_split_keys: <= 32 full splits, window / 64 sliding
   L.big_ld = std::max<int>(3 * c.hidden, qkvg_rows(c));
   L.big_ld = (L.big_ld + 7) / 8 * 8;
   const size_t tab = (size_t)c.max_ctx * kHalfDim * 4;
@@ -584,10 +584,9 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
       aa.out = mix; aa.part = ctx->at<float>(L.part); aa.counters = ctx->at<int>(L.counters);
       int ms = 1;
       double kv_bytes = 0;
-      aa.split_keys = attn_decode_split_keys(!full, c.window);
       for (int r = 0; r < M; ++r) {
         const int lo = full ? 0 : std::max(0, rows.pos[r] - (c.window - 1));
-        ms = std::max(ms, (rows.pos[r] - lo) / aa.split_keys + 1);
+        ms = std::max(ms, (rows.pos[r] - lo) / attn_decode_split_keys(!full, rows.pos[r] - lo + 1) + 1);
         kv_bytes += (double)(rows.pos[r] - lo + 1) * c.n_kv_heads * kHeadDim * 2 * 2;
       }
       aa.max_splits = ms;

@@ -223,7 +223,16 @@ def decode_8stream(eng, synth, torch, dev):
     e1.record(eng.stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    return round(8 * (n_steps - 1) / (ms / 1e3), 1), [int(x) for x in lens]
+    return round(8 * (n_steps - 1) / (ms / 1e3), 1), [int(x) for x in lens], step_breakdown(eng, slots, ids[n_steps])
+
+
+def step_breakdown(eng, slots, tokens):
+    """Kernel-family milliseconds of one more decode step (library event timing, untimed above)."""
+    eng.profile(True)
+    eng.decode(slots, tokens=tokens, logits=False, argmax=True)
+    prof = eng.profile_read()
+    eng.profile(False)
+    return {k: round(v["ms"], 4) for k, v in prof.items() if v["launches"]}
 
 
 def prefill_8k(eng, synth, torch, dev):
@@ -247,7 +256,8 @@ def prefill_8k(eng, synth, torch, dev):
 def run_extras(eng, synth, torch, dev, schemes=True):
     from attention_decoder_amd.lfm3 import Engine
     out = {}
-    out["decode_8stream_tok_s"], out["decode_8stream_prompt_lengths"] = decode_8stream(eng, synth, torch, dev)
+    out["decode_8stream_tok_s"], out["decode_8stream_prompt_lengths"], out["decode_8stream_step_breakdown_ms"] = \
+        decode_8stream(eng, synth, torch, dev)
     log(f"8-stream decode {out['decode_8stream_tok_s']} tok/s")
     out["prefill_8k_tok_s"], ms, toks = prefill_8k(eng, synth, torch, dev)
     out["prefill_8k_ms"] = round(ms, 3)
@@ -273,7 +283,7 @@ def run_extras(eng, synth, torch, dev, schemes=True):
             cfg = synth.full_config(bits=bits, group=64, max_slots=8, max_ctx=8704, max_chunk=2048)
             e2 = Engine(cfg, synth.cached_blob(cfg, seed=0))
             if bits == 8:
-                out["q8_decode_8stream_tok_s"], _ = decode_8stream(e2, synth, torch, dev)
+                out["q8_decode_8stream_tok_s"], _, out["q8_decode_8stream_step_breakdown_ms"] = decode_8stream(e2, synth, torch, dev)
                 log(f"q8 8-stream decode {out['q8_decode_8stream_tok_s']} tok/s")
             else:
                 out["q6_prefill_8k_tok_s"], ms6, _ = prefill_8k(e2, synth, torch, dev)
@@ -324,6 +334,7 @@ def cfg5_extras(synth, torch, dev):
     ms = e0.elapsed_time(e1)
     out["cfg5_decode_32stream_tok_s"] = round(32 * n_steps / (ms / 1e3), 1)
     out["cfg5_decode_32stream_mean_context"] = int(np.mean(lens))
+    out["cfg5_decode_step_breakdown_ms"] = step_breakdown(eng, slots, ids[n_steps])
     log(f"g32 + 8-bit head: 32k prefill {out['cfg5_prefill_32k_tok_s']} tok/s, 32-stream decode "
         f"{out['cfg5_decode_32stream_tok_s']} tok/s")
     eng.close()
