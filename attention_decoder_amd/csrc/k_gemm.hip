@@ -23,6 +23,8 @@
 //
 // Loads are branch-free (rows past M or N read a clamped valid row whose results are not stored).
 // SwiGLU: a lane's two weight rows are the gate row and the matching up row of one output column.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace lfm3 {
@@ -352,6 +354,216 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
     case 4: return launch_bits<4>(s, a);
     case 6: return launch_bits<6>(s, a);
     case 8: return launch_bits<8>(s, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode linears at 3 .. 32 rows ("skinny" MFMA GEMM). One block per 32-row weight tile (SwiGLU:
+// the gate tile and its up tile; the conv in_proj: the B, C and x tiles of 32 channels); the four
+// waves take every fourth K tile (with the loads of the next 2-4 of them in flight), each
+// accumulating MT x NT MFMA tiles over all input rows
+// (x rows, then the x_lo rows when the input is carried as a pair), with the weights dequantised
+// straight into operand registers from the re-tiled copy and the input rows read from L2. The
+// four partial tiles meet in LDS and are added in wave order; the epilogue (the GEMV's) runs one
+// thread per (row, column): the pair's two rows are added (x row first), then STORE, SwiGLU or the
+// gated short conv with the slot's kept state.
+// ---------------------------------------------------------------------------------------------
+
+template <int EPI> struct SgTiles { static constexpr int v = EPI == GEMV_SWIGLU ? 2 : EPI == GEMV_CONV ? 3 : 1; };
+
+template <int BITS, int EPI, int MT>
+__global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
+  constexpr int NT = SgTiles<EPI>::v;
+  constexpr int D = MT == 1 ? 4 : 2;   // K tiles in flight per wave
+  constexpr int TW = NT * 32, TR = MT * 32;
+  constexpr uint32_t kTileBytes = 256u * BITS;
+  extern __shared__ __attribute__((aligned(16))) float sg_smem[];   // [4 waves][TR][TW]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hf = lane >> 5, c32 = lane & 31;
+  const int R = g.batch;
+  const bool pair = g.x_lo != nullptr;
+  const int Meff = pair ? 2 * R : R;
+  const int N = w.n, K = w.k;
+  const int nk = K / BK;
+
+  int tile[NT];
+  if constexpr (EPI == GEMV_SWIGLU) {
+    tile[0] = blockIdx.x;
+    tile[1] = (N / 2) / 32 + blockIdx.x;
+  } else if constexpr (EPI == GEMV_CONV) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) tile[j] = j * ((N / 3) / 32) + blockIdx.x;
+  } else {
+    tile[0] = blockIdx.x;
+  }
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(w.codes, (uint32_t)w.ntile * nk * kTileBytes);
+  const __amdgpu_buffer_rsrc_t rsb = rsrc_of(w.sb, (uint32_t)w.ntile * nk * 256u);
+  uint32_t qoff[NT], sboff[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    qoff[j] = (uint32_t)tile[j] * nk * kTileBytes + (uint32_t)lane * Planes<BITS>::PB;
+    sboff[j] = ((uint32_t)tile[j] * nk * 64u + lane) * 4u;
+  }
+  // the lane's A rows: virtual row 32i + c32 (x rows, then x_lo rows; rows past Meff read row 0)
+  const f16_t* arow[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int vr = 32 * i + c32;
+    arow[i] = (vr < R ? g.x + (size_t)vr * g.ldx : vr < Meff ? g.x_lo + (size_t)(vr - R) * g.ldx : g.x) + 32 * hf;
+  }
+
+  struct WSet {
+    Run<BITS> run[NT];
+    uint32_t sb[NT];
+    u32x4_v av[MT][4];
+  };
+  const int ns = (nk - wave + 3) / 4;   // K tiles of this wave: wave, wave + 4, ...
+  auto load = [&](int s, WSet& ws) {
+    const int kt = wave + 4 * min(s, ns - 1);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      load_run<BITS>(rq, qoff[j], (uint32_t)kt * kTileBytes, ws.run[j]);
+      ws.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, sboff[j], (uint32_t)kt * 256u, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ws.av[i][t] = *(const u32x4_v*)(arow[i] + kt * BK + 8 * t);
+  };
+  f32x16_v acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto compute = [&](const WSet& ws) {
+    f16x2_v s2[NT], b2[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const f16x2_v sbv = __builtin_bit_cast(f16x2_v, ws.sb[j]);
+      s2[j] = __builtin_shufflevector(sbv, sbv, 0, 0);
+      b2[j] = __builtin_shufflevector(sbv, sbv, 1, 1);
+    }
+    auto sub = [&](auto tc) {
+      constexpr int T = decltype(tc)::value;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const f16x8_v b = deq8<BITS, T>(ws.run[j], s2[j], b2[j]);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_v, ws.av[i][T]), b, acc[i][j], 0, 0, 0);
+      }
+    };
+    sub(std::integral_constant<int, 0>{});
+    sub(std::integral_constant<int, 1>{});
+    sub(std::integral_constant<int, 2>{});
+    sub(std::integral_constant<int, 3>{});
+  };
+  // D register sets in a ring: the loads of the wave's next D K tiles are in flight while one is
+  // computed (the K loop of a decode linear is latency-bound: few tiles per wave, one block per
+  // CU). Branch-free: past the end the loads re-read the wave's last tile and are not computed.
+  WSet ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, ring[d]);
+  for (int s = 0; s < ns; s += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (s + d < ns) compute(ring[d]);
+      load(s + d + D, ring[d]);
+    }
+  }
+
+  // the partial tiles into LDS: acc[i][j][v] is virtual row 32i + 8(v/4) + 4(lane/32) + v%4,
+  // column 32j + lane%32 of the block's tile
+  float* mine = sg_smem + (size_t)wave * TR * TW;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mine[(32 * i + 8 * (v >> 2) + 4 * hf + (v & 3)) * TW + 32 * j + c32] = acc[i][j][v];
+  __syncthreads();
+  auto total = [&](int vr, int col) {
+    const int e = vr * TW + col;
+    return ((sg_smem[e] + sg_smem[TR * TW + e]) + sg_smem[2 * TR * TW + e]) + sg_smem[3 * TR * TW + e];
+  };
+  auto val = [&](int r, int col) {
+    float v = total(r, col);
+    if (pair) v = v + total(r + R, col);
+    return v;
+  };
+  for (int idx = tid; idx < R * 32; idx += 256) {
+    const int r = idx >> 5, c = idx & 31;
+    if constexpr (EPI == GEMV_STORE) {
+      const int n = 32 * tile[0] + c;
+      if (n < N) g.yf[(size_t)r * g.ldy + n] = val(r, c);
+    } else if constexpr (EPI == GEMV_SWIGLU) {
+      const float gt = val(r, c), up = val(r, 32 + c);
+      g.y[(size_t)r * g.ldy + 32 * blockIdx.x + c] = f2h_sep(gt / (1.f + __expf(-gt)) * up);
+    } else {
+      // gated short conv of channel ch ("LFM3-1.7B port" table row 1): z = f16(B * x),
+      // y = sum_j ker[ch, j] * [state | z]_j, out = f16(C * y), state <- the last taps-1 z
+      const int H = N / 3, T = g.conv_taps, S = T - 1;
+      const int ch = 32 * blockIdx.x + c;
+      f16_t* st = g.conv_state + (size_t)g.conv_slot[r] * g.conv_slot_stride;
+      const float z = h2f(f2h_sep(val(r, c) * val(r, 64 + c)));
+      float win[kMaxTaps];
+#pragma unroll
+      for (int q = 0; q < kMaxTaps - 1; ++q) win[q] = q < S ? h2f(st[(size_t)q * H + ch]) : 0.f;
+      float y = bf2f(g.conv_kernel[(size_t)ch * T + S]) * z;
+#pragma unroll
+      for (int q = 0; q < kMaxTaps - 1; ++q)
+        if (q < S) y = fmaf(bf2f(g.conv_kernel[(size_t)ch * T + q]), win[q], y);
+#pragma unroll
+      for (int q = 0; q < kMaxTaps - 2; ++q)
+        if (q + 1 < S) st[(size_t)q * H + ch] = f2h(win[q + 1]);
+      st[(size_t)(S - 1) * H + ch] = f2h(z);
+      g.y[(size_t)r * g.ldy + ch] = f2h_sep(val(r, 32 + c) * y);
+    }
+  }
+}
+
+template <int BITS, int EPI, int MT>
+static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks) {
+  const size_t lds = (size_t)4 * MT * 32 * SgTiles<EPI>::v * 32 * sizeof(float);
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_sgemm<BITS, EPI, MT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_sgemm<BITS, EPI, MT>), dim3(blocks), dim3(256), lds, s, w, g);
+  return hipGetLastError();
+}
+
+template <int BITS, int EPI>
+static hipError_t launch_sg_epi(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int meff) {
+  return meff <= 32 ? launch_sg<BITS, EPI, 1>(s, w, g, blocks) : launch_sg<BITS, EPI, 2>(s, w, g, blocks);
+}
+
+template <int BITS>
+static hipError_t launch_sg_bits(hipStream_t s, const GemmW& w, const GemvArgs& g, int meff) {
+  switch (g.epi) {
+    case GEMV_STORE: return launch_sg_epi<BITS, GEMV_STORE>(s, w, g, w.ntile, meff);
+    case GEMV_SWIGLU: return launch_sg_epi<BITS, GEMV_SWIGLU>(s, w, g, w.n / 64, meff);
+    case GEMV_CONV: return launch_sg_epi<BITS, GEMV_CONV>(s, w, g, (w.n / 3) / 32, meff);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_sgemm(hipStream_t s, const GemmW& w, const GemvArgs& g) {
+  const int meff = g.x_lo ? 2 * g.batch : g.batch;
+  if (g.batch < 1 || meff > 64 || w.k % (4 * BK) || w.group % 32 || g.ldx % 8 || (uintptr_t)g.x % 16 ||
+      (uintptr_t)g.x_lo % 16 || w.ntile != (w.n + 31) / 32 ||
+      (g.epi == GEMV_SWIGLU && w.n % 64) || (g.epi == GEMV_CONV && ((w.n / 3) % 32 || w.n % 3 || g.conv_taps < 2 ||
+                                                                  g.conv_taps > kMaxTaps)))
+    return hipErrorInvalidValue;
+  switch (w.bits) {
+    case 4: return launch_sg_bits<4>(s, w, g, meff);
+    case 6: return launch_sg_bits<6>(s, w, g, meff);
+    case 8: return launch_sg_bits<8>(s, w, g, meff);
     default: return hipErrorInvalidValue;
   }
 }

@@ -529,15 +529,20 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     return ctx->capture + (size_t)layer * ctx->capture_rows * H;
   };
   auto gemv_bytes = [&](const QLinear& w, double out_bytes) { return lin_bytes(w) + (double)M * w.k * 2.0 + out_bytes; };
-  auto gemv = [&](GemvArgs& g, double out_bytes) -> hipError_t {
-    return timed(ctx, LFM3_PROF_GEMV, gemv_bytes(g.w, out_bytes), 2.0 * M * (double)g.w.n * g.w.k,
-                 [&] { return launch_gemv(s, g); });
+  // batches of 3 rows and more run the layers' linears on MFMA from the re-tiled weights (one read
+  // of the weights for all rows); 1 and 2 rows keep the exact GEMV with its fused norm prologue
+  const bool mfma = M >= 3;
+  auto gemv = [&](GemvArgs& g, double out_bytes, const GemmW* gw = nullptr) -> hipError_t {
+    const double fl = 2.0 * M * (double)g.w.n * g.w.k;
+    if (mfma && gw && (g.x_lo ? 2 * M : M) <= 64)
+      return timed(ctx, LFM3_PROF_GEMV, gemv_bytes(g.w, out_bytes), fl, [&] { return launch_sgemm(s, *gw, g); });
+    return timed(ctx, LFM3_PROF_GEMV, gemv_bytes(g.w, out_bytes), fl, [&] { return launch_gemv(s, g); });
   };
   // GEMV whose input is rmsnorm(cur [+ rmsnorm(m) * w_post]) * w_pre
   // split: the normed input is carried as the fp16 pair x + x_lo (the operator-norm output, which
   // feeds in_proj and qkvg); a fused split prologue handles one row
   auto normed_gemv = [&](GemvArgs& g, const bf16_t* w_post, const bf16_t* w_pre, float* capture, float* x_copy,
-                         double out_bytes, bool split = false) -> hipError_t {
+                         double out_bytes, bool split = false, const GemmW* gw = nullptr) -> hipError_t {
     g.batch = M;
     if (fuse && (!split || M == 1)) {
       g.h_src = cur; g.m = w_post ? m : nullptr; g.w_post = w_post; g.w_pre = w_pre; g.eps = c.norm_eps;
@@ -553,7 +558,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     hipError_t e = timed(ctx, LFM3_PROF_NORM, (double)M * H * 14, 0, [&] { return launch_resid_norm(s, na); });
     if (e != hipSuccess) return e;
     g.x = x; g.x_lo = na.x_lo; g.ldx = H;
-    return gemv(g, out_bytes + (split ? (double)M * H * 2 : 0.0));
+    return gemv(g, out_bytes + (split ? (double)M * H * 2 : 0.0), gw);
   };
 
   for (int i = 0; i < c.n_layers; ++i) {
@@ -567,11 +572,11 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
       g.conv_slot_stride = (int64_t)L.conv_slot;
       g.conv_taps = c.conv_taps;
       for (int b = 0; b < M; ++b) g.conv_slot[b] = rows.slot[b];
-      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * H * (2 + 4 * (c.conv_taps - 1)), true));
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * H * (2 + 4 * (c.conv_taps - 1)), true, &lw.g_in));
     } else {
       GemvArgs g{};
       g.w = lw.mix_in; g.epi = GEMV_STORE; g.yf = big; g.ldy = L.big_ld;
-      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4, true));
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4, true, &lw.g_in));
       const bool full = lw.type == LFM3_LAYER_FULL;
       AttnDecodeArgs aa{};
       aa.qkvg = big; aa.ld = L.big_ld; aa.gate_col = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
@@ -595,17 +600,17 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     {
       GemvArgs g{};
       g.w = lw.mix_out; g.x = mix; g.ldx = H; g.batch = M; g.epi = GEMV_STORE; g.yf = m; g.ldy = H;
-      LFM3_TRY(gemv(g, (double)M * H * 4));
+      LFM3_TRY(gemv(g, (double)M * H * 4, &lw.g_out));
     }
     {
       GemvArgs g{};
       g.w = lw.w13; g.epi = GEMV_SWIGLU; g.y = sb; g.ldy = c.ffn;
-      LFM3_TRY(normed_gemv(g, lw.post_op, lw.ffn_norm, nullptr, nullptr, (double)M * c.ffn * 2));
+      LFM3_TRY(normed_gemv(g, lw.post_op, lw.ffn_norm, nullptr, nullptr, (double)M * c.ffn * 2, false, &lw.g13));
     }
     {
       GemvArgs g{};
       g.w = lw.w2; g.x = sb; g.ldx = c.ffn; g.batch = M; g.epi = GEMV_STORE; g.yf = m; g.ldy = H;
-      LFM3_TRY(gemv(g, (double)M * H * 4));
+      LFM3_TRY(gemv(g, (double)M * H * 4, &lw.g2));
     }
   }
   const bf16_t* last_post = ctx->layers[c.n_layers - 1].post_ffn;
@@ -978,8 +983,17 @@ lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uin
     if (path == 3) { g.epi = GEMM_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2; }
     else { g.epi = GEMM_STORE; g.yf = y_dev; g.ldy = w.n; }
     LFM3_TRY(launch_gemm(ctx->stream, g));
+  } else if (path == 4 || path == 5) {
+    if (rows < 1 || rows > 64) return ctx->fail(LFM3_ERR_ARG, "decode MFMA rows must be in [1, 64]");
+    auto gt = ctx->gemm_by_name.find(name);
+    if (gt == ctx->gemm_by_name.end()) return ctx->fail(LFM3_ERR_ARG, std::string(name) + " has no GEMM copy (the head is decode-only)");
+    GemvArgs g{};
+    g.w = w; g.x = x_dev; g.ldx = w.k; g.batch = rows;
+    if (path == 5) { g.epi = GEMV_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2; }
+    else { g.epi = GEMV_STORE; g.yf = y_dev; g.ldy = w.n; }
+    LFM3_TRY(launch_sgemm(ctx->stream, gt->second, g));
   } else {
-    return ctx->fail(LFM3_ERR_ARG, "path must be 0..3");
+    return ctx->fail(LFM3_ERR_ARG, "path must be 0..5");
   }
   return LFM3_OK;
 }

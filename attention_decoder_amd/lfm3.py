@@ -248,7 +248,9 @@ class Engine:
         lfm3_capture_layers(self.ctx, buf, max_rows)
 
     def linear(self, name, x_f16, path):
-        """y fp32 [rows, N] = x (torch fp16 [rows, K]) through the GEMV (path 0) or GEMM (path 1)."""
+        """y fp32 [rows, N] = x (torch fp16 [rows, K]) through the GEMV (path 0), the prefill GEMM
+        (path 1) or the decode MFMA GEMM (path 4); paths 2, 3, 5: the same with the SwiGLU epilogue
+        (fp16 [rows, N/2])."""
         n = None
         from .synth import tensor_plan
         for nm, kind, shape, bits, group in tensor_plan(self.cfg):
@@ -256,7 +258,7 @@ class Engine:
                 n = shape[0]
         if n is None:
             raise LFM3Error(1, f"no quantized linear named {name}")
-        if path in (2, 3):
+        if path in (2, 3, 5):
             y = self._empty((x_f16.shape[0], n // 2), self.torch.float16)
         else:
             y = self._empty((x_f16.shape[0], n), self.torch.float32)

@@ -156,10 +156,11 @@ lfm3_status lfm3_dequant_rows(lfm3_ctx* ctx, const char* name, int32_t row0, int
 /*
  * One stored linear (name without the .q/.scales/.biases suffix) applied to caller rows, for
  * kernel-level parity: y_dev fp32 [rows, N] = x_dev fp16 [rows, K] times the dequantised weight,
- * through the decode dequant-GEMV (path 0, rows in [1, 8], exact weights) or the prefill
- * dequant-to-LDS MFMA GEMM (path 1, weights rounded to fp16 in LDS). Paths 2 (GEMV) and 3 (GEMM)
- * apply the SwiGLU epilogue of a fused [gate | up] weight instead: y_dev then receives fp16
- * [rows, N/2] = silu(gate) * up.
+ * through the decode dequant-GEMV (path 0, rows in [1, 8], exact weights), the prefill MFMA GEMM
+ * (path 1, weights rounded to fp16) or the decode MFMA GEMM of 3+ rows (path 4, rows in [1, 64],
+ * weights rounded to fp16). Paths 2 (GEMV), 3 (GEMM) and 5 (decode MFMA) apply the SwiGLU epilogue
+ * of a fused [gate | up] weight instead: y_dev then receives fp16 [rows, N/2] = silu(gate) * up.
+ * The embedding (tied head) has only path 0.
  */
 lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uint16_t* x_dev,
                         int32_t rows, float* y_dev);

@@ -67,22 +67,32 @@ def test_q4_per_layer_residuals(q4):
     assert max(rels) <= REL_L2, rels
 
 
-def test_q4_batched_decode_equals_solo(q4):
-    """Eight streams decoded together give bitwise the logits of each stream decoded alone."""
+def test_q4_batched_decode(q4):
+    """Eight streams decoded together (the MFMA path of 3+ rows): equal, bitwise, to the same streams
+    decoded as two batches of four (a row's result does not depend on the rows beside it); two of
+    them against the float64 oracle."""
     torch, cfg, eng, orc = q4
     lens = [37, 300, 260, 5, 128, 257, 90, 400]
     prompts = [synth.prompt_tokens(100 + i, n) for i, n in enumerate(lens)]
-    for i in range(8):
-        eng.reset(i)
-        eng.prefill(i, tokens=dev_tokens(torch, prompts[i]), logits=False, argmax=False)
     step_tok = [int(t) for t in synth.prompt_tokens(200, 8)]
-    both = eng.decode(list(range(8)), tokens=dev_tokens(torch, step_tok), logits=True, argmax=True)
-    batched = both["logits"].clone()
-    solo = []
+
+    def run(groups):
+        for i in range(8):
+            eng.reset(i)
+            eng.prefill(i, tokens=dev_tokens(torch, prompts[i]), logits=False, argmax=False)
+        out = {}
+        for grp in groups:
+            o = eng.decode(list(grp), tokens=dev_tokens(torch, [step_tok[i] for i in grp]), logits=True, argmax=True)
+            for j, i in enumerate(grp):
+                out[i] = (o["logits"][j].clone(), int(o["argmax"][j].item()))
+        torch.cuda.synchronize()
+        return out
+
+    eight = run([range(8)])
+    halves = run([(4, 0, 6, 2), (1, 7, 3, 5)])
     for i in range(8):
-        eng.reset(i)
-        eng.prefill(i, tokens=dev_tokens(torch, prompts[i]), logits=False, argmax=False)
-        solo.append(eng.decode([i], tokens=dev_tokens(torch, [step_tok[i]]), logits=True)["logits"][0].clone())
-    torch.cuda.synchronize()
-    for i in range(8):
-        assert torch.equal(batched[i], solo[i]), i
+        assert torch.equal(eight[i][0], halves[i][0]), i
+    for i in (3, 0):
+        want = oracle_teacher_forced(orc, np.concatenate([prompts[i], [step_tok[i]]]), [])
+        got = eight[i][0].cpu().numpy().astype(np.float64)
+        compare_logits(got[None], [eight[i][1]], want, f"q4 batch-8 decode, stream {i}")

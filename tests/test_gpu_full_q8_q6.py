@@ -4,7 +4,7 @@
   each crossing the 256-token window seam, prefilled into their own slots, then greedy decode of
   all eight in one batch; every stream's logits against the float64 oracle run teacher-forced on
   that stream alone. At the full stream lengths (prompts uniform in [300, 2960]), where the oracle
-  would take minutes, batched decode is checked against solo decode bitwise.
+  would take minutes, a batch of eight is checked against batches of three and five, bitwise.
 - 6-bit g64, chunked prefill (the 8192-token structure): a prompt over several library chunks,
   whose last-position logits are checked against the oracle both when the library chunks it and
   when the caller does; at the full 8192 tokens in 2048-row chunks two different chunkings must
@@ -65,21 +65,29 @@ def test_q8_eight_streams_teacher_forced(q8):
         compare_logits(lg[:, s], [ids[t][s] for t in range(steps + 1)], ref, f"q8 stream {s} (prompt {lens[s]})")
 
 
-def test_q8_full_length_streams_batched_equals_solo(q8):
-    """Prompts at the full stream lengths (uniform in [300, 2960]); batched == solo bitwise."""
+def test_q8_full_length_streams_batch_composition(q8):
+    """Prompts at the full stream lengths (uniform in [300, 2960]): one step of the 8 streams decoded
+    together equals, bitwise, the same step decoded as batches of 3 and 5."""
     torch, cfg, eng, orc = q8
     lens = synth.stream_prompt_lengths(4, 8)
     prompts = synth.stream_prompts(4, lens)
-    for i in range(8):
-        eng.reset(i)
-        eng.prefill(i, tokens=dev_tokens(torch, prompts[i]), logits=False, argmax=False)
     step_tok = [int(t) for t in synth.prompt_tokens(300, 8)]
-    batched = eng.decode(list(range(8)), tokens=dev_tokens(torch, step_tok), logits=True)["logits"].clone()
+
+    def run(groups):
+        for i in range(8):
+            eng.reset(i)
+            eng.prefill(i, tokens=dev_tokens(torch, prompts[i]), logits=False, argmax=False)
+        out = {}
+        for grp in groups:
+            o = eng.decode(list(grp), tokens=dev_tokens(torch, [step_tok[i] for i in grp]), logits=True)["logits"]
+            for j, i in enumerate(grp):
+                out[i] = o[j].clone()
+        return out
+
+    eight = run([range(8)])
+    split = run([(5, 1, 7), (0, 6, 2, 4, 3)])
     for i in range(8):
-        eng.reset(i)
-        eng.prefill(i, tokens=dev_tokens(torch, prompts[i]), logits=False, argmax=False)
-        solo = eng.decode([i], tokens=dev_tokens(torch, [step_tok[i]]), logits=True)["logits"][0]
-        assert torch.equal(batched[i], solo), i
+        assert torch.equal(eight[i], split[i]), i
 
 
 @pytest.fixture(scope="module")

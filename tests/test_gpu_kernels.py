@@ -140,3 +140,27 @@ def test_gemm_other_schemes(bits, group):
             assert err < tol, (bits, group, name, err)
     finally:
         eng.close()
+
+
+@pytest.mark.parametrize("name", SHAPES)
+def test_decode_mfma_matches_float64(eng, weights, name):
+    """The decode MFMA GEMM (3+ rows) at 3, 8, 32 and 64 rows: the float64 product with the
+    fp16-rounded weights (SwiGLU for w13), and each row independent of the rows beside it."""
+    import torch
+    w = weights[name]
+    wf = ref.f16_round(w)
+    swiglu = name.endswith("w13")
+    x64, xd64 = _x(torch, 64, w.shape[1], 64)
+    for rows in (3, 8, 32, 64):
+        y = eng.linear(name, xd64[:rows].contiguous(), 5 if swiglu else 4).float().cpu().numpy().astype(np.float64)
+        ab = x64[:rows].astype(np.float64) @ wf.T
+        if swiglu:
+            F = w.shape[0] // 2
+            want, tol = ab[:, :F] / (1 + np.exp(-ab[:, :F])) * ab[:, F:], 2e-3
+        else:
+            want, tol = ab, 2e-5
+        err = np.abs(y - want).max() / np.abs(want).max()
+        assert err < tol, (name, rows, err)
+        if rows == 64:
+            y3 = eng.linear(name, xd64[61:64].contiguous(), 5 if swiglu else 4).float().cpu().numpy()
+            assert np.array_equal(y3, y[61:64].astype(np.float32)), name
