@@ -283,14 +283,16 @@ hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
 
 // ---------------------------------------------------------------------------------------------
 // decode: block (split, kv head, row); a split is attn_decode_split_keys(row) consecutive visible
-// keys (a multiple of 64), walked in 64-key tiles with an online softmax, the next tile's K/V loads (and the page
-// ids of the one after) in flight while a tile is computed. The prologue normalises and rotates
-// the block's 4 query heads from the raw qkvg row; the block whose split holds the current
-// position also forms its key and value (per-head k RMSNorm + RoPE) and stores them in the cache.
-// Scores: 4 lanes per key (32 dims each, summed by DPP); wave w is query head 4 kvh + w for the
-// softmax and P V (lane = 2 dims). One split: the block writes the gated output. Several: partials
-// (max, sum, o) go to the workspace and the last block of a (row, kv head) to finish merges them,
-// with every partial load issued at once.
+// keys (a multiple of 64), walked in 64-key tiles with an online softmax, the next tile's K/V loads
+// (and the page ids of the one after) in flight while a tile is computed. The prologue normalises
+// and rotates the block's 4 query heads from the raw qkvg row; the block whose split holds the
+// current position also forms its key and value (per-head k RMSNorm + RoPE) and stores them in the
+// cache. Scores: 4 lanes per key (32 dims each, summed by DPP); wave w is query head 4 kvh + w for
+// the softmax and P V (lane = 2 dims). One split: the block writes the gated output. Several:
+// partials (max, sum, o) go to the workspace and k_attn_merge, the next launch, combines them (the
+// kernel boundary orders the partials' stores before its loads; an in-kernel last-block merge
+// would need an agent-scope release and acquire per block, a write-back and an invalidate of the
+// L2, which measured slower than the extra launch).
 // ---------------------------------------------------------------------------------------------
 
 constexpr int TILE = 64;
@@ -309,7 +311,6 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
   __shared__ float qs[kQPerKv][kHeadDim];
   __shared__ float sc[kQPerKv][TILE];
   __shared__ __attribute__((aligned(16))) f16_t knew[kHeadDim], vnew[kHeadDim];
-  __shared__ int is_last;
   const int split = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int slot = a.rows.slot[r], pos = a.rows.pos[r];
@@ -462,25 +463,29 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
     *(uint32_t*)(out + d0) = pack_h2(o0 * inv, o1 * inv);
     return;
   }
-  // 5. partials [o (128) | max | sum | pad]; the last block of this (row, kv head) merges them
+  // 5. partials [o (128) | max | sum | pad], merged by k_attn_merge
   float* part = a.part + (((size_t)r * nq + h) * a.max_splits + split) * kPartStride;
   if (lane == 0) { part[kHeadDim] = m_run; part[kHeadDim + 1] = l_run; }
   *(float2*)(part + d0) = make_float2(o0, o1);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int* cnt = a.counters + (size_t)r * nkv + kvh;
-    const int old = atomicAdd(cnt, 1);
-    is_last = old == ns - 1;
-    if (is_last) *cnt = 0;   // ready for the next launch
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  // merge, wave = head, in batches of 32 splits with every load of a batch issued at once:
-  // lanes 0-31 hold the statistics of split s0 + lane; for o, lanes 0-31 take the even splits of
-  // the batch and lanes 32-63 the odd ones, 4 dims each (lane % 32)
-  float* wbuf = reinterpret_cast<float*>(kt) + wave * 32;   // 4 x 32 floats in the K tile area
+}
+
+// Merge of a row's split partials: block (kv head, row), wave w = query head 4 kvh + w, in batches
+// of 32 splits with every load of a batch issued at once: lanes 0-31 hold the statistics of split
+// s0 + lane; for o, lanes 0-31 take the even splits of the batch and lanes 32-63 the odd ones,
+// 4 dims each (lane % 32). Rows with one split were written by k_attn_decode.
+__global__ void __launch_bounds__(256) k_attn_merge(AttnDecodeArgs a) {
+  __shared__ float wb[kQPerKv][32];
+  const int kvh = blockIdx.x, r = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int pos = a.rows.pos[r];
+  const int nq = a.n_q_heads;
+  const int k_lo = a.window > 0 ? max(0, pos - (a.window - 1)) : 0;
+  const int ns = (pos - k_lo) / attn_decode_split_keys(a.window > 0, pos - k_lo + 1) + 1;
+  if (ns == 1) return;
+  const int h = kvh * kQPerKv + wave;
+  const float gate = sigmoidf_(a.qkvg[(size_t)r * a.ld + a.gate_col + h]);
+  f16_t* out = a.out + (size_t)r * nq * kHeadDim + (size_t)h * kHeadDim;
+  float* wbuf = wb[wave];
   const float* ph = a.part + ((size_t)r * nq + h) * a.max_splits * kPartStride;
   const int half = lane >> 5, dq = 4 * (lane & 31);
   float gmx = -__builtin_huge_valf(), lt = 0.f;
@@ -534,6 +539,7 @@ hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a) {
     hipLaunchKernelGGL(k_attn_decode<true>, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_attn_decode<false>, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
+  if (a.max_splits > 1) hipLaunchKernelGGL(k_attn_merge, dim3(a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -186,8 +186,7 @@ hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a);
 
 // Decode attention for one row per slot, fused with the q/k norm + RoPE of the step's own query
 // and key and the store of its key and value; split-K (attn_decode_split_keys keys per split) with
-// the merge done by the last block of each (row, kv head) (counters start at zero and are left at
-// zero).
+// the partials merged by a second launch.
 struct AttnDecodeArgs {
   const float* qkvg;   // raw fp32 linear output [rows, ld]: q | k | v | g
   int ld;
@@ -203,7 +202,6 @@ struct AttnDecodeArgs {
   float eps;
   f16_t* out;          // [rows, n_q_heads * 128]
   float* part;         // [rows, n_q_heads, max_splits, kPartStride]
-  int* counters;       // [rows, n_kv_heads]
   int max_splits;      // grid extent: the most splits any row needs
 };
 constexpr int kPartStride = kHeadDim + 4;   // split partial: o [128], max, sum, 2 pad (16-byte rows)

@@ -153,7 +153,7 @@ bool check_config(const lfm3_config& c, std::string& err) {
 struct Layout {
   size_t cos_f, sin_f, cos_s, sin_s;
   size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
-  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, m2, xf, part, keys, counters;
+  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, m2, xf, part, keys;
   size_t gemm_w, gemm_w_bytes;   // re-tiled copies of every prefill GEMM weight
   size_t total;
   int max_rows, max_pages, ring_rows, max_splits, big_ld;
@@ -226,7 +226,6 @@ Layout make_layout(const lfm3_config& c) {
   L.xf = take(R * H * 2);
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
   L.keys = take((size_t)std::max(kMaxBatch, (int)R) * 8);
-  L.counters = take((size_t)c.max_slots * c.n_kv_heads * 4);
   L.gemm_w_bytes = 0;
   for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits);
   L.gemm_w = take(L.gemm_w_bytes);
@@ -586,7 +585,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
       aa.kv = kv_for(ctx, lw); aa.rows = rows;
       aa.window = full ? 0 : c.window;
       aa.n_q_heads = c.n_q_heads; aa.n_kv_heads = c.n_kv_heads; aa.eps = c.norm_eps;
-      aa.out = mix; aa.part = ctx->at<float>(L.part); aa.counters = ctx->at<int>(L.counters);
+      aa.out = mix; aa.part = ctx->at<float>(L.part);
       int ms = 1;
       double kv_bytes = 0;
       for (int r = 0; r < M; ++r) {
@@ -825,8 +824,7 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
   // zero the conv states, page table and argmax keys
   if (launch_zero(ctx->stream, ctx->at<void>(L.conv_state), (size_t)c.max_slots * L.conv_slot * 2) != hipSuccess ||
       launch_zero(ctx->stream, ctx->at<void>(L.page_table), (size_t)c.max_slots * L.max_pages * 4) != hipSuccess ||
-      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)std::max(kMaxBatch, L.max_rows) * 8) != hipSuccess ||
-      launch_zero(ctx->stream, ctx->at<void>(L.counters), (size_t)c.max_slots * c.n_kv_heads * 4) != hipSuccess) {
+      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)std::max(kMaxBatch, L.max_rows) * 8) != hipSuccess) {
     delete ctx;
     g_err = "workspace clear failed";
     return LFM3_ERR_DEVICE;
