@@ -366,11 +366,12 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
 // (x rows, then the x_lo rows when the input is carried as a pair), with the weights dequantised
 // straight into operand registers from the re-tiled copy and the input rows read from L2. The
 // four partial tiles meet in LDS and are added in wave order; the epilogue (the GEMV's) runs one
-// thread per (row, column): the pair's two rows are added (x row first), then STORE, SwiGLU or the
-// gated short conv with the slot's kept state.
+// thread per (row, column): the pair's two rows are added (x row first), then STORE, SwiGLU, the
+// gated short conv with the slot's kept state, or the head's logits with each row's argmax key.
 // ---------------------------------------------------------------------------------------------
 
 template <int EPI> struct SgTiles { static constexpr int v = EPI == GEMV_SWIGLU ? 2 : EPI == GEMV_CONV ? 3 : 1; };
+constexpr int kHeadTiles = 16;   // 32-row tiles of the head per block
 
 template <int BITS, int EPI, int MT>
 __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
@@ -387,15 +388,22 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
   const int N = w.n, K = w.k;
   const int nk = K / BK;
 
+  // the head: each block takes kHeadTiles consecutive 32-row tiles and keeps every row's best key
+  // across them, so the rows' argmax keys take one atomicMax per block (not per tile)
+  constexpr int TPB = EPI == GEMV_LOGITS ? kHeadTiles : 1;
+  uint64_t best[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // per epilogue slot idx = tid + 256 k (rows < 64)
+  for (int tt = 0; tt < TPB; ++tt) {
+  const int tb = blockIdx.x * TPB + tt;
+  if (EPI == GEMV_LOGITS && tb >= w.ntile) break;
   int tile[NT];
   if constexpr (EPI == GEMV_SWIGLU) {
-    tile[0] = blockIdx.x;
-    tile[1] = (N / 2) / 32 + blockIdx.x;
+    tile[0] = tb;
+    tile[1] = (N / 2) / 32 + tb;
   } else if constexpr (EPI == GEMV_CONV) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) tile[j] = j * ((N / 3) / 32) + blockIdx.x;
+    for (int j = 0; j < NT; ++j) tile[j] = j * ((N / 3) / 32) + tb;
   } else {
-    tile[0] = blockIdx.x;
+    tile[0] = tb;
   }
   const __amdgpu_buffer_rsrc_t rq = rsrc_of(w.codes, (uint32_t)w.ntile * nk * kTileBytes);
   const __amdgpu_buffer_rsrc_t rsb = rsrc_of(w.sb, (uint32_t)w.ntile * nk * 256u);
@@ -496,17 +504,26 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
   };
   for (int idx = tid; idx < R * 32; idx += 256) {
     const int r = idx >> 5, c = idx & 31;
-    if constexpr (EPI == GEMV_STORE) {
+    if constexpr (EPI == GEMV_LOGITS) {
+      // logits, and the running argmax key of the row (order key, then the lower id)
+      const int n = 32 * tile[0] + c;
+      const float v = val(r, c);
+      if (n < N) {
+        if (g.logits) g.logits[(size_t)r * g.ld_logits + n] = v;
+        const uint64_t key = ((uint64_t)order_key(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)n);
+        best[idx >> 8] = key > best[idx >> 8] ? key : best[idx >> 8];
+      }
+    } else if constexpr (EPI == GEMV_STORE) {
       const int n = 32 * tile[0] + c;
       if (n < N) g.yf[(size_t)r * g.ldy + n] = val(r, c);
     } else if constexpr (EPI == GEMV_SWIGLU) {
       const float gt = val(r, c), up = val(r, 32 + c);
-      g.y[(size_t)r * g.ldy + 32 * blockIdx.x + c] = f2h_sep(gt / (1.f + __expf(-gt)) * up);
+      g.y[(size_t)r * g.ldy + 32 * tb + c] = f2h_sep(gt / (1.f + __expf(-gt)) * up);
     } else {
       // gated short conv of channel ch ("LFM3-1.7B port" table row 1): z = f16(B * x),
       // y = sum_j ker[ch, j] * [state | z]_j, out = f16(C * y), state <- the last taps-1 z
       const int H = N / 3, T = g.conv_taps, S = T - 1;
-      const int ch = 32 * blockIdx.x + c;
+      const int ch = 32 * tb + c;
       f16_t* st = g.conv_state + (size_t)g.conv_slot[r] * g.conv_slot_stride;
       const float z = h2f(f2h_sep(val(r, c) * val(r, 64 + c)));
       float win[kMaxTaps];
@@ -521,6 +538,22 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
         if (q + 1 < S) st[(size_t)q * H + ch] = f2h(win[q + 1]);
       st[(size_t)(S - 1) * H + ch] = f2h(z);
       g.y[(size_t)r * g.ldy + ch] = f2h_sep(val(r, 32 + c) * y);
+    }
+  }
+  __syncthreads();   // the LDS tiles are reused by the next tile
+  }
+  if constexpr (EPI == GEMV_LOGITS) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (tid + 256 * k >= R * 32) break;
+      uint64_t key = best[k];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)key, o, 64), hi = __shfl_xor((uint32_t)(key >> 32), o, 64);
+        const uint64_t other = ((uint64_t)hi << 32) | lo;
+        key = other > key ? other : key;
+      }
+      if ((tid & 31) == 0 && key) atomicMax((unsigned long long*)&g.keys[(tid + 256 * k) >> 5], (unsigned long long)key);
     }
   }
 }
@@ -549,6 +582,7 @@ static hipError_t launch_sg_bits(hipStream_t s, const GemmW& w, const GemvArgs& 
     case GEMV_STORE: return launch_sg_epi<BITS, GEMV_STORE>(s, w, g, w.ntile, meff);
     case GEMV_SWIGLU: return launch_sg_epi<BITS, GEMV_SWIGLU>(s, w, g, w.n / 64, meff);
     case GEMV_CONV: return launch_sg_epi<BITS, GEMV_CONV>(s, w, g, (w.n / 3) / 32, meff);
+    case GEMV_LOGITS: return launch_sg_epi<BITS, GEMV_LOGITS>(s, w, g, (w.ntile + kHeadTiles - 1) / kHeadTiles, meff);
     default: return hipErrorInvalidValue;
   }
 }

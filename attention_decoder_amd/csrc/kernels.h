@@ -144,9 +144,9 @@ size_t gemm_codes_bytes(int n, int k, int bits);
 size_t gemm_sb_bytes(int n, int k);
 hipError_t launch_repack_gemm(hipStream_t s, const QLinear& w, uint8_t* codes, uint32_t* sb);
 
-// Decode linears of 3 .. 32 rows on MFMA from the re-tiled weights: the GEMV's STORE, SWIGLU and
-// CONV epilogues with its argument block (x, x_lo, batch, outputs, conv state); the input rows
-// (x, and x_lo as extra rows when set) number at most 64.
+// Decode linears of 3 .. 32 rows on MFMA from the re-tiled weights: the GEMV's STORE, SWIGLU,
+// CONV and LOGITS epilogues with its argument block (x, x_lo, batch, outputs, conv state, argmax
+// keys); the input rows (x, and x_lo as extra rows when set) number at most 64.
 hipError_t launch_sgemm(hipStream_t s, const GemmW& w, const GemvArgs& g);
 
 // Y[m, n] = sum_k X[m, k] * f16(q[n, k] * s + bias), MFMA fp16 with fp32 accumulation.

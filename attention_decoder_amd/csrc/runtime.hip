@@ -228,6 +228,7 @@ Layout make_layout(const lfm3_config& c) {
   L.keys = take((size_t)std::max(kMaxBatch, (int)R) * 8);
   L.gemm_w_bytes = 0;
   for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits);
+  if (c.has_embedding) L.gemm_w_bytes += gemm_w_bytes(c.vocab, c.hidden, c.embed_bits);   // the tied head
   L.gemm_w = take(L.gemm_w_bytes);
   L.total = off;
   return L;
@@ -260,6 +261,7 @@ struct lfm3_ctx {
   uint8_t* ws;
   std::vector<LayerW> layers;
   QLinear emb{};
+  GemmW g_emb{};   // the head's re-tiled copy (decode batches of 3+ rows)
   const bf16_t* emb_norm = nullptr;
   std::vector<int> len;
   std::vector<std::vector<int32_t>> pages;
@@ -617,7 +619,8 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     GemvArgs g{};
     g.w = ctx->emb; g.epi = GEMV_LOGITS; g.logits = logits; g.ld_logits = c.vocab;
     g.keys = ctx->at<uint64_t>(L.keys);
-    LFM3_TRY(normed_gemv(g, last_post, ctx->emb_norm, cap(c.n_layers - 1), hidden_out, logits ? (double)M * c.vocab * 4 : 0.0));
+    LFM3_TRY(normed_gemv(g, last_post, ctx->emb_norm, cap(c.n_layers - 1), hidden_out, logits ? (double)M * c.vocab * 4 : 0.0,
+                         false, &ctx->g_emb));
     LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, 12.0 * M, 0, [&] { return launch_argmax_finalize(s, g.keys, ids, M); }));
   } else {
     NormArgs nf{};
@@ -788,6 +791,10 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
       lw.g_out = retile(lw.mix_out, p + (conv ? "conv.out_proj" : "attn.o_proj"));
       lw.g13 = retile(lw.w13, p + "ffn.w13");
       lw.g2 = retile(lw.w2, p + "ffn.w2");
+    }
+    if (c.has_embedding) {
+      ctx->g_emb = retile(ctx->emb, "embedding");
+      ctx->gemm_by_name.erase("embedding");   // the GEMM hook paths stay off the head
     }
     if (e != hipSuccess || goff != L.gemm_w + L.gemm_w_bytes) {
       delete ctx;
