@@ -389,7 +389,7 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
   const int nk = K / BK;
 
   // the head: each block takes kHeadTiles consecutive 32-row tiles and keeps every row's best key
-  // across them, so the rows' argmax keys take one atomicMax per block (not per tile)
+  // across them, so the rows' argmax keys take one partial store per block (not per tile)
   constexpr int TPB = EPI == GEMV_LOGITS ? kHeadTiles : 1;
   uint64_t best[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // per epilogue slot idx = tid + 256 k (rows < 64)
   for (int tt = 0; tt < TPB; ++tt) {
@@ -553,7 +553,7 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
         const uint64_t other = ((uint64_t)hi << 32) | lo;
         key = other > key ? other : key;
       }
-      if ((tid & 31) == 0 && key) atomicMax((unsigned long long*)&g.keys[(tid + 256 * k) >> 5], (unsigned long long)key);
+      if ((tid & 31) == 0) g.keys[(size_t)((tid + 256 * k) >> 5) * kArgmaxParts + blockIdx.x] = key;
     }
   }
 }
@@ -582,7 +582,9 @@ static hipError_t launch_sg_bits(hipStream_t s, const GemmW& w, const GemvArgs& 
     case GEMV_STORE: return launch_sg_epi<BITS, GEMV_STORE>(s, w, g, w.ntile, meff);
     case GEMV_SWIGLU: return launch_sg_epi<BITS, GEMV_SWIGLU>(s, w, g, w.n / 64, meff);
     case GEMV_CONV: return launch_sg_epi<BITS, GEMV_CONV>(s, w, g, (w.n / 3) / 32, meff);
-    case GEMV_LOGITS: return launch_sg_epi<BITS, GEMV_LOGITS>(s, w, g, (w.ntile + kHeadTiles - 1) / kHeadTiles, meff);
+    case GEMV_LOGITS:
+      if ((w.ntile + kHeadTiles - 1) / kHeadTiles > kArgmaxParts) return hipErrorInvalidValue;
+      return launch_sg_epi<BITS, GEMV_LOGITS>(s, w, g, (w.ntile + kHeadTiles - 1) / kHeadTiles, meff);
     default: return hipErrorInvalidValue;
   }
 }

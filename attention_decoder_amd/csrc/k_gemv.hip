@@ -4,8 +4,10 @@
 // issue #1491, "Checkpoint handling"). The weights are never rounded: per lane chunk of one group,
 //   sum_k x_k (q_k s + bias) = s * sum_k x_k q_k + bias * sum_k x_k,
 // where q_k enters an fp16 dot2 exactly as 1024 + q (exponent 2^10 with q in the 10-bit mantissa,
-// built by one and-or per pair for every code width) and s * 1024 * sum x is subtracted.
-// x is fp16; accumulation is fp32.
+// built by one and-or per pair) and s * 1024 * sum x is subtracted. At 4 bits the odd nibbles of
+// a byte are not shifted down: masked in place they read as 1024 + 16 q, also exact, and go to a
+// second accumulator that is scaled by 1/16 (exact), so a code word costs one shift and four
+// and-ors. x is fp16; accumulation is fp32.
 //
 // Layout: a wave owns a group of 4 rows (SwiGLU: 2 gate rows + the 2 matching up rows); lane l
 // streams chunks l, l+64, ... of each row (16 B of codes: 32 4-bit or 16 8-bit codes; 12 B of
@@ -38,12 +40,19 @@ template <int BITS> LFM3_DEV int pair_pos(int kk) {
   return kk;  // 6-bit: pairs of consecutive codes
 }
 
-template <int BITS> LFM3_DEV void unpack(const uint32_t (&w)[QT<BITS>::NDW], uint32_t (&p)[QT<BITS>::NP]) {
+// Codes of one chunk as fp16 pairs. `magic` is kMagic2 held in a VGPR, so that each pair is one
+// v_and_or_b32 (mask from an SGPR). 4-bit: pair 4d + j holds nibbles j and j + 4 of word d, as
+// 1024 + q for even j and as 1024 + 16 q (nibble left at bits 4..7) for odd j.
+template <int BITS> LFM3_DEV void unpack(const uint32_t (&w)[QT<BITS>::NDW], uint32_t (&p)[QT<BITS>::NP], uint32_t magic) {
   if constexpr (BITS == 4) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p[4 * d + j] = ((w[d] >> (4 * j)) & 0x000F000Fu) | kMagic2;
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t w8 = w[d] >> 8;
+      p[4 * d] = (w[d] & 0x000F000Fu) | magic;
+      p[4 * d + 1] = (w[d] & 0x00F000F0u) | magic;
+      p[4 * d + 2] = (w8 & 0x000F000Fu) | magic;
+      p[4 * d + 3] = (w8 & 0x00F000F0u) | magic;
+    }
   } else if constexpr (BITS == 6) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -56,13 +65,13 @@ template <int BITS> LFM3_DEV void unpack(const uint32_t (&w)[QT<BITS>::NDW], uin
         if (sh > 26) v |= w[d + 1] << (32 - sh);
         c[h] = v & 63u;
       }
-      p[i] = (c[0] | (c[1] << 16)) | kMagic2;
+      p[i] = (c[0] | (c[1] << 16)) | magic;
     }
   } else {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      p[2 * d] = (w[d] & 0x00FF00FFu) | kMagic2;
-      p[2 * d + 1] = ((w[d] >> 8) & 0x00FF00FFu) | kMagic2;
+      p[2 * d] = (w[d] & 0x00FF00FFu) | magic;
+      p[2 * d + 1] = ((w[d] >> 8) & 0x00FF00FFu) | magic;
     }
   }
 }
@@ -142,22 +151,29 @@ template <int BITS> LFM3_DEV uint4 pair_order8(const uint32_t (&h)[4]) {
 }
 
 // One vector block of one batch row into LDS: the pair-ordered fp16 values and, from the first lane
-// of each chunk, the chunk sum (8 values in order, then the lanes of the chunk by a DPP tree).
+// of each chunk, the chunk's (X, XO): X = sum of its x, XO = the offset the magic adds to its dot
+// products, 1024 * X at 6 and 8 bits and 1024 * X_even + 64 * X_odd at 4 bits (X_even / X_odd:
+// the x of the even / odd codes of each 8-code word). Sums: the block's values in order, then the
+// lanes of the chunk by a DPP tree.
 template <int BITS>
-LFM3_DEV void put_x8(uint16_t* xp, float* xsum, int K, int b, int v, const uint32_t (&h)[4], bool valid) {
+LFM3_DEV void put_x8(uint16_t* xp, float2* xsum, int K, int b, int v, const uint32_t (&h)[4], bool valid) {
   using Q = QT<BITS>;
-  float s = 0.f;
+  float e = 0.f, o = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s += h2f((f16_t)(h[i] & 0xffffu));
-    s += h2f((f16_t)(h[i] >> 16));
+    e += h2f((f16_t)(h[i] & 0xffffu));
+    o += h2f((f16_t)(h[i] >> 16));
   }
-  s = valid ? s : 0.f;
-  s += dpp_mov<0xb1>(s);                    // chunk = 2 vector blocks (16 codes) ...
-  if (Q::CH == 32) s += dpp_mov<0x4e>(s);   // ... or 4 (32 codes): adjacent lanes
+  e = valid ? e : 0.f;
+  o = valid ? o : 0.f;
+  e += dpp_mov<0xb1>(e);                    // chunk = 2 vector blocks (16 codes) ...
+  o += dpp_mov<0xb1>(o);
+  if (Q::CH == 32) { e += dpp_mov<0x4e>(e); o += dpp_mov<0x4e>(o); }   // ... or 4 (32 codes)
   if (!valid) return;
   *(uint4*)(xp + (size_t)b * K + 8 * v) = pair_order8<BITS>(h);
-  if ((v & (Q::CH / 8 - 1)) == 0) xsum[b * (K / Q::CH) + v / (Q::CH / 8)] = s;
+  const float X = e + o;
+  const float XO = BITS == 4 ? fmaf(kMagicOff, e, 64.f * o) : kMagicOff * X;
+  if ((v & (Q::CH / 8 - 1)) == 0) xsum[b * (K / Q::CH) + v / (Q::CH / 8)] = make_float2(X, XO);
 }
 
 // Decode norm prologue registers: the h / m rows of every batch row and the two norm weights.
@@ -190,7 +206,7 @@ LFM3_DEV void prologue_load(const GemvArgs& a, PrologueRegs<BT>& p) {
 // is carried as an fp16 pair (split), real row b stages its high parts as virtual row b and its
 // remainders as virtual row b + BT/2.
 template <int BITS, int BT>
-LFM3_DEV void prologue_compute(const GemvArgs& a, PrologueRegs<BT>& p, uint16_t* xp, float* xsum, float* red,
+LFM3_DEV void prologue_compute(const GemvArgs& a, PrologueRegs<BT>& p, uint16_t* xp, float2* xsum, float* red,
                                bool split) {
   const int K = a.w.k, nv = K / 8;
   constexpr int HB = BT / 2;
@@ -267,7 +283,7 @@ LFM3_DEV void plain_load(const GemvArgs& a, PlainRegs<BT>& p, int j0, bool split
 }
 
 template <int BITS, int BT>
-LFM3_DEV void plain_stage(const GemvArgs& a, const PlainRegs<BT>& p, int j0, uint16_t* xp, float* xsum, bool split) {
+LFM3_DEV void plain_stage(const GemvArgs& a, const PlainRegs<BT>& p, int j0, uint16_t* xp, float2* xsum, bool split) {
   const int K = a.w.k, nv = K / 8;
   constexpr int HB = BT > 1 ? BT / 2 : 1;
 #pragma unroll
@@ -289,13 +305,14 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   constexpr int RG = RowsPerGroup<EPI>::v;
   extern __shared__ uint32_t smem[];
   __shared__ float red[8 * BT];
+  __shared__ uint64_t wkeys[EPI == GEMV_LOGITS ? 4 * BT : 1];
   __shared__ float part[KW > 1 ? KW * BT * kRG : 1];
   const int K = a.w.k;
   const int NC = K / Q::CH;
   const int NIT = (NC + 63) / 64;          // k iterations of a group (a multiple of KW)
   const int NITW = NIT / KW;               // of them per wave
   uint16_t* xp = (uint16_t*)smem;                 // [BT][K] fp16 in pair order (virtual rows)
-  float* xsum = (float*)(smem + (BT * K) / 2);    // [BT][NC]
+  float2* xsum = (float2*)(smem + (BT * K) / 2);  // [BT][NC] (X, XO)
   // split: the input is carried as an fp16 pair; virtual rows BT/2.. hold the remainders and the
   // two partial totals of a row are added before the epilogue (the host guarantees BT >= 2)
   const bool split = BT > 1 && (a.split_x || a.x_lo);
@@ -387,6 +404,11 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   }
   __syncthreads();
 
+  // the magic exponent in a VGPR (opaque to constant folding), so that the unpack's and-or can take
+  // its mask from an SGPR
+  uint32_t vmagic = kMagic2;
+  asm volatile("" : "+v"(vmagic));
+
   uint64_t best[BT];
 #pragma unroll
   for (int b = 0; b < BT; ++b) best[b] = 0;
@@ -401,7 +423,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     const int c = lane + 64 * (kw + KW * sw);
     if (c < NC) {
       uint32_t xv[BT][Q::NP];
-      float X[BT];
+      float X[BT], XO[BT];
 #pragma unroll
       for (int b = 0; b < BT; ++b) {
         const uint4* xs4 = (const uint4*)(xp + b * K + c * Q::CH);
@@ -410,19 +432,34 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
           const uint4 v = xs4[q];
           xv[b][4 * q] = v.x; xv[b][4 * q + 1] = v.y; xv[b][4 * q + 2] = v.z; xv[b][4 * q + 3] = v.w;
         }
-        X[b] = xsum[b * NC + c];
+        const float2 xs = xsum[b * NC + c];
+        X[b] = xs.x;
+        XO[b] = xs.y;
       }
 #pragma unroll
       for (int r = 0; r < RG; ++r) {
         uint32_t wp[Q::NP];
-        unpack<BITS>(W.q[r], wp);
+        unpack<BITS>(W.q[r], wp, vmagic);
         const float sc = bf2f(W.s[r]), bi = bf2f(W.b[r]);
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
-          float d = 0.f;
+          float inner;
+          if constexpr (BITS == 4) {
+            // even pairs carry 1024 + q, odd pairs 1024 + 16 q
+            float da = 0.f, db = 0.f;
 #pragma unroll
-          for (int p = 0; p < Q::NP; ++p) d = dot2(wp[p], xv[b][p], d);
-          acc[r][b] += fmaf(sc, fmaf(-kMagicOff, X[b], d), bi * X[b]);
+            for (int p = 0; p < Q::NP; p += 2) {
+              da = dot2(wp[p], xv[b][p], da);
+              db = dot2(wp[p + 1], xv[b][p + 1], db);
+            }
+            inner = fmaf(db, 0.0625f, da) - XO[b];
+          } else {
+            float d = 0.f;
+#pragma unroll
+            for (int p = 0; p < Q::NP; ++p) d = dot2(wp[p], xv[b][p], d);
+            inner = d - XO[b];
+          }
+          acc[r][b] += fmaf(sc, inner, bi * X[b]);
         }
       }
     }
@@ -546,7 +583,16 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
         const uint64_t other = ((uint64_t)hi << 32) | lo;
         k = other > k ? other : k;
       }
-      if (lane == 0 && b < a.batch && k) atomicMax((unsigned long long*)&a.keys[b], (unsigned long long)k);
+      if (lane == 0) wkeys[wave * BT + b] = k;
+    }
+    // the block's best key per row, in one plain store to the row's partial slot
+    __syncthreads();
+    if ((int)threadIdx.x < BT && (int)threadIdx.x < a.batch) {
+      const int b = threadIdx.x;
+      uint64_t k = wkeys[b];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) k = wkeys[w * BT + b] > k ? wkeys[w * BT + b] : k;
+      a.keys[(size_t)b * kArgmaxParts + blockIdx.x] = k;
     }
   }
 }
@@ -569,7 +615,7 @@ template <int BITS, int BT>
 static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
   using Q = QT<BITS>;
   const int K = a.w.k;
-  const size_t lds = (size_t)BT * K * 2 + (size_t)BT * (K / Q::CH) * 4;
+  const size_t lds = (size_t)BT * K * 2 + (size_t)BT * (K / Q::CH) * sizeof(float2);
   const int N = a.w.n;
   const int n_groups = a.epi == GEMV_SWIGLU ? n_groups_of<GEMV_SWIGLU>(N)
                        : a.epi == GEMV_CONV ? n_groups_of<GEMV_CONV>(N) : n_groups_of<GEMV_STORE>(N);
@@ -578,8 +624,11 @@ static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
   const int nit = (K / Q::CH + 63) / 64;
   const bool split = nit % 4 == 0;
   const int cap = a.max_blocks > 0 ? a.max_blocks : LFM3_GEMV_MAX_BLOCKS;
+  // one wave per row group up to 512 groups, two up to 1024, then four (capped): a block's
+  // staging of the input is cheap next to leaving CUs idle on the small linears
   int grid = split ? n_groups : (n_groups + 3) / 4;
   if (grid > cap) grid = cap;
+  if (a.epi == GEMV_LOGITS && grid > kArgmaxParts) return hipErrorInvalidValue;
   if (a.h_src) {
     if constexpr (BT <= 2) {
       if (split) launch_epi<BITS, BT, 1, 4>(s, a, grid, lds);
@@ -598,7 +647,7 @@ template <int BITS>
 static hipError_t launch_bits(hipStream_t s, const GemvArgs& a) {
   using Q = QT<BITS>;
   const int K = a.w.k;
-  auto lds_for = [&](int bt) { return (size_t)bt * K * 2 + (size_t)bt * (K / Q::CH) * 4; };
+  auto lds_for = [&](int bt) { return (size_t)bt * K * 2 + (size_t)bt * (K / Q::CH) * sizeof(float2); };
   // a split input takes two virtual rows per row
   const bool split = a.split_x || a.x_lo;
   const int rows = split ? 2 * a.batch : a.batch;
@@ -618,7 +667,7 @@ static hipError_t launch_bits(hipStream_t s, const GemvArgs& a) {
       if (p.y) p.y = a.y + (size_t)b0 * a.ldy;
       if (p.yf) p.yf = a.yf + (size_t)b0 * a.ldy;
       if (p.logits) p.logits = a.logits + (size_t)b0 * a.ld_logits;
-      if (p.keys) p.keys = a.keys + b0;
+      if (p.keys) p.keys = a.keys + (size_t)b0 * kArgmaxParts;
       hipError_t e = launch_bits<BITS>(s, p);
       if (e != hipSuccess) return e;
     }

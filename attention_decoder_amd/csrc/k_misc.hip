@@ -353,18 +353,38 @@ hipError_t launch_zero(hipStream_t s, void* p, size_t bytes) {
 }
 
 // keys: (order_key(value) << 32) | (0xffffffff - index); the max key is the largest value with
-// the lowest index. Resets the keys for the next step.
-__global__ void k_argmax_finalize(uint64_t* keys, int32_t* ids, int rows) {
-  const int r = threadIdx.x;
-  if (r < rows) {
-    const uint64_t k = keys[r];
-    if (ids) ids[r] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
-    keys[r] = 0;
+// the lowest index. Block r takes the kArgmaxParts partials of row r (max is order-free, so the
+// result does not depend on which block wrote which part) and clears them for the next step.
+__global__ void __launch_bounds__(256) k_argmax_finalize(uint64_t* keys, int32_t* ids) {
+  __shared__ uint64_t wk[4];
+  const int r = blockIdx.x;
+  uint64_t* part = keys + (size_t)r * kArgmaxParts;
+  uint64_t k = 0;
+  for (int p = threadIdx.x; p < kArgmaxParts; p += 256) {
+    const uint64_t v = part[p];
+    k = v > k ? v : k;
+    part[p] = 0;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)k, o, 64), hi = __shfl_xor((uint32_t)(k >> 32), o, 64);
+    const uint64_t other = ((uint64_t)hi << 32) | lo;
+    k = other > k ? other : k;
+  }
+  if ((threadIdx.x & 63) == 0) wk[threadIdx.x >> 6] = k;
+  __syncthreads();
+  if (threadIdx.x == 0 && ids) {
+    k = wk[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) k = wk[w] > k ? wk[w] : k;
+    ids[r] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
   }
 }
 
 hipError_t launch_argmax_finalize(hipStream_t s, uint64_t* keys, int32_t* ids, int rows) {
-  hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(kMaxBatch), 0, s, keys, ids, rows);
+  if (rows <= 0) return hipSuccess;
+  if (rows > kMaxBatch) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_argmax_finalize, dim3(rows), dim3(256), 0, s, keys, ids);
   return hipGetLastError();
 }
 

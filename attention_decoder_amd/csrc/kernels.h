@@ -85,7 +85,7 @@ hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int ro
 enum GemvEpi { GEMV_STORE = 0, GEMV_SWIGLU = 1, GEMV_LOGITS = 2, GEMV_CONV = 3 };
 // y[b, n] = sum_k x[b, k] * (q[n, k] * s + bias) for b < batch (<= 8), exact weights (the per-group
 // factored form). STORE: fp32 yf [batch, ldy]. SWIGLU: rows n and n + N/2 -> fp16 silu(a) * b in
-// y. LOGITS: fp32 logits (nullable) + per-row argmax keys (atomicMax). CONV (in_proj, N = 3H): the
+// y. LOGITS: fp32 logits (nullable) + per-block argmax partials (keys, kArgmaxParts per row). CONV (in_proj, N = 3H): the
 // gated short conv of each channel with its kept state, fp16 out in y [batch, ldy].
 // Input: x fp16 [batch, ldx], or (h_src set) the decode norm prologue:
 //   h_new = h_src + (m ? rmsnorm(m) * w_post : 0), x = f16(rmsnorm(h_new) * w_pre),

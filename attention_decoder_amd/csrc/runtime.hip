@@ -225,7 +225,7 @@ Layout make_layout(const lfm3_config& c) {
   L.m2 = take(R * H * 4);
   L.xf = take(R * H * 2);
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
-  L.keys = take((size_t)std::max(kMaxBatch, (int)R) * 8);
+  L.keys = take((size_t)kMaxBatch * kArgmaxParts * 8);   // argmax partials [row][part]
   L.gemm_w_bytes = 0;
   for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits);
   if (c.has_embedding) L.gemm_w_bytes += gemm_w_bytes(c.vocab, c.hidden, c.embed_bits);   // the tied head
@@ -621,7 +621,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     g.keys = ctx->at<uint64_t>(L.keys);
     LFM3_TRY(normed_gemv(g, last_post, ctx->emb_norm, cap(c.n_layers - 1), hidden_out, logits ? (double)M * c.vocab * 4 : 0.0,
                          false, &ctx->g_emb));
-    LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, 12.0 * M, 0, [&] { return launch_argmax_finalize(s, g.keys, ids, M); }));
+    LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, (16.0 * kArgmaxParts + 4) * M, 0, [&] { return launch_argmax_finalize(s, g.keys, ids, M); }));
   } else {
     NormArgs nf{};
     nf.h_in = cur; nf.h_out = cur; nf.x_out = xf; nf.rows = M; nf.hidden = H; nf.eps = c.norm_eps;
@@ -640,7 +640,7 @@ lfm3_status head(lfm3_ctx* ctx, const f16_t* xrows, int n, float* logits, int32_
   g.logits = logits; g.ld_logits = ctx->cfg.vocab; g.keys = ctx->at<uint64_t>(ctx->L.keys);
   const double bytes = lin_bytes(g.w) + (double)n * g.w.k * 2 + (logits ? (double)n * g.w.n * 4 : 0.0);
   LFM3_TRY(timed(ctx, LFM3_PROF_GEMV, bytes, 2.0 * n * g.w.n * g.w.k, [&] { return launch_gemv(ctx->stream, g); }));
-  LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, 12.0 * n, 0, [&] { return launch_argmax_finalize(ctx->stream, g.keys, ids, n); }));
+  LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, (16.0 * kArgmaxParts + 4) * n, 0, [&] { return launch_argmax_finalize(ctx->stream, g.keys, ids, n); }));
   return LFM3_OK;
 }
 
@@ -831,7 +831,7 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
   // zero the conv states, page table and argmax keys
   if (launch_zero(ctx->stream, ctx->at<void>(L.conv_state), (size_t)c.max_slots * L.conv_slot * 2) != hipSuccess ||
       launch_zero(ctx->stream, ctx->at<void>(L.page_table), (size_t)c.max_slots * L.max_pages * 4) != hipSuccess ||
-      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)std::max(kMaxBatch, L.max_rows) * 8) != hipSuccess) {
+      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)kMaxBatch * kArgmaxParts * 8) != hipSuccess) {
     delete ctx;
     g_err = "workspace clear failed";
     return LFM3_ERR_DEVICE;
