@@ -114,8 +114,11 @@ template <int BITS, int T> LFM3_DEV f16x8_v deq8(const Run<BITS>& r, f16x2_v s2,
   return __builtin_bit_cast(f16x8_v, u32x4_v{p[0], p[1], p[2], p[3]});
 }
 
+// BITS = 16: the weights come from the fp16 copy (GemmW::w16), already in operand order.
 template <int BITS, int EPI, int BM>
 __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
+  constexpr bool F16 = BITS == 16;
+  constexpr int QB = F16 ? 4 : BITS;             // code width of the (unused) codes path
   constexpr int MT = BM / 32;                  // 32-row MFMA tiles per wave
   constexpr int AV = BM * BK / 8 / 256;        // 16-byte X pieces per thread per K tile
   __shared__ __attribute__((aligned(16))) f16_t As[2][BM * LDSK];
@@ -137,7 +140,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
     wtile[1] = min((int)blockIdx.y * (BN / 32) + 2 * wave + 1, a.w.ntile - 1);
     wrow0 = 0;
   }
-  constexpr uint32_t kTileBytes = 256u * BITS;    // one (32-row, 64-k) tile of codes
+  constexpr uint32_t kTileBytes = F16 ? 4096u : 256u * BITS;    // one (32-row, 64-k) tile
 
   // K tiles 0 .. nk-1 read x; with a remainder input, tiles nk .. 2nk-1 read x_lo against the same
   // weight tiles (Y = x W + x_lo W). With a K split, block z runs tiles [z nk/2, (z + 1) nk/2).
@@ -149,7 +152,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   const uint32_t xbytes = (uint32_t)((size_t)(M - 1) * a.ldx + K) * 2u;
   const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.x, xbytes);
   const __amdgpu_buffer_rsrc_t rxl = rsrc_of(a.x_lo ? a.x_lo : a.x, xbytes);
-  const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.w.codes, (uint32_t)a.w.ntile * nk * kTileBytes);
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(F16 ? (const void*)a.w.w16 : (const void*)a.w.codes, (uint32_t)a.w.ntile * nk * kTileBytes);
   const __amdgpu_buffer_rsrc_t rsb = rsrc_of(a.w.sb, (uint32_t)a.w.ntile * nk * 256u);
 
   // per-lane byte offsets, fixed over the K loop
@@ -163,7 +166,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   uint32_t qoff[2], sboff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    qoff[j] = (uint32_t)wtile[j] * nk * kTileBytes + (uint32_t)lane * Planes<BITS>::PB;
+    qoff[j] = (uint32_t)wtile[j] * nk * kTileBytes + (uint32_t)lane * (F16 ? 16u : (uint32_t)Planes<QB>::PB);
     sboff[j] = ((uint32_t)wtile[j] * nk * 64u + lane) * 4u;
   }
 
@@ -185,16 +188,25 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
   };
   // weight registers in two sets (even / odd K tiles), so that no value has to be copied across
   // the loop edge (a copy would make every iteration wait for the loads it just issued)
-  struct WSet {
-    Run<BITS> run[2];
+  struct WSetQ {
+    Run<QB> run[2];
     uint32_t sb[2];   // fp16 (scale, bias)
   };
+  struct WSet16 {
+    u32x4_v p[2][4];   // the operand registers themselves
+  };
+  using WSet = std::conditional_t<F16, WSet16, WSetQ>;
   auto load_w = [&](int kt, WSet& w) {
     const uint32_t kk = (uint32_t)(kt >= nk ? kt - nk : kt);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      load_run<BITS>(rq, qoff[j], kk * kTileBytes, w.run[j]);
-      w.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, sboff[j], kk * 256u, 0);
+      if constexpr (F16) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w.p[j][t] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j] + 1024u * t, kk * kTileBytes, 0);
+      } else {
+        load_run<QB>(rq, qoff[j], kk * kTileBytes, w.run[j]);
+        w.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, sboff[j], kk * 256u, 0);
+      }
     }
   };
 
@@ -221,12 +233,17 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
     f16x8_v bop[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const f16x2_v sbv = __builtin_bit_cast(f16x2_v, cur.sb[j]);
-      const f16x2_v s2 = __builtin_shufflevector(sbv, sbv, 0, 0), b2 = __builtin_shufflevector(sbv, sbv, 1, 1);
-      bop[j][0] = deq8<BITS, 0>(cur.run[j], s2, b2);
-      bop[j][1] = deq8<BITS, 1>(cur.run[j], s2, b2);
-      bop[j][2] = deq8<BITS, 2>(cur.run[j], s2, b2);
-      bop[j][3] = deq8<BITS, 3>(cur.run[j], s2, b2);
+      if constexpr (F16) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bop[j][t] = __builtin_bit_cast(f16x8_v, cur.p[j][t]);
+      } else {
+        const f16x2_v sbv = __builtin_bit_cast(f16x2_v, cur.sb[j]);
+        const f16x2_v s2 = __builtin_shufflevector(sbv, sbv, 0, 0), b2 = __builtin_shufflevector(sbv, sbv, 1, 1);
+        bop[j][0] = deq8<QB, 0>(cur.run[j], s2, b2);
+        bop[j][1] = deq8<QB, 1>(cur.run[j], s2, b2);
+        bop[j][2] = deq8<QB, 2>(cur.run[j], s2, b2);
+        bop[j][3] = deq8<QB, 3>(cur.run[j], s2, b2);
+      }
     }
     const f16_t* at = As[kt & 1];
 #pragma unroll
@@ -276,6 +293,40 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs a) {
 
 size_t gemm_codes_bytes(int n, int k, int bits) { return (size_t)((n + 31) / 32) * (k / BK) * 256u * bits; }
 size_t gemm_sb_bytes(int n, int k) { return (size_t)((n + 31) / 32) * (k / BK) * 256u; }
+size_t gemm_w16_bytes(int n, int k) { return (size_t)((n + 31) / 32) * (k / BK) * 4096u; }
+
+// One wave per (32-row, 64-k) tile: lane l dequantises its 32 codes with the GEMM's own deq8 and
+// writes them as the four 16-byte planes of the fp16 copy.
+template <int BITS>
+__global__ void __launch_bounds__(64) k_repack16(GemmW w, uint32_t* w16, int nk) {
+  const size_t tile = blockIdx.x;          // wtile * nk + kt
+  const int lane = threadIdx.x;
+  constexpr uint32_t kTileBytes = 256u * BITS;
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(w.codes, (uint32_t)w.ntile * nk * kTileBytes);
+  Run<BITS> run;
+  load_run<BITS>(rq, (uint32_t)lane * Planes<BITS>::PB, (uint32_t)(tile * kTileBytes), run);
+  const f16x2_v sbv = __builtin_bit_cast(f16x2_v, w.sb[tile * 64 + lane]);
+  const f16x2_v s2 = __builtin_shufflevector(sbv, sbv, 0, 0), b2 = __builtin_shufflevector(sbv, sbv, 1, 1);
+  u32x4_v* out = (u32x4_v*)(w16 + tile * 1024);
+  out[0 * 64 + lane] = __builtin_bit_cast(u32x4_v, deq8<BITS, 0>(run, s2, b2));
+  out[1 * 64 + lane] = __builtin_bit_cast(u32x4_v, deq8<BITS, 1>(run, s2, b2));
+  out[2 * 64 + lane] = __builtin_bit_cast(u32x4_v, deq8<BITS, 2>(run, s2, b2));
+  out[3 * 64 + lane] = __builtin_bit_cast(u32x4_v, deq8<BITS, 3>(run, s2, b2));
+}
+
+hipError_t launch_repack_gemm16(hipStream_t s, const GemmW& w, uint32_t* w16) {
+  if (!w.codes || !w.sb || !w16 || w.k % BK || w.ntile != (w.n + 31) / 32) return hipErrorInvalidValue;
+  const int nk = w.k / BK;
+  const size_t tiles = (size_t)w.ntile * nk;
+  if (tiles == 0 || tiles > 0x7fffffff || tiles * 4096u > 0xffffffffull) return hipErrorInvalidValue;
+  switch (w.bits) {
+    case 4: hipLaunchKernelGGL(k_repack16<4>, dim3((unsigned)tiles), dim3(64), 0, s, w, w16, nk); break;
+    case 6: hipLaunchKernelGGL(k_repack16<6>, dim3((unsigned)tiles), dim3(64), 0, s, w, w16, nk); break;
+    case 8: hipLaunchKernelGGL(k_repack16<8>, dim3((unsigned)tiles), dim3(64), 0, s, w, w16, nk); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 // One block of 64 threads per (32-row, 64-k) tile; thread l writes lane l's codes and (scale,
 // bias) pair of the re-tiled copy (the layout is described with GemmW).
@@ -350,6 +401,10 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
     return hipErrorInvalidValue;
   // a K split: two halves of an even number of K tiles, plain STORE
   if (a.yf2 && ((a.w.k / BK) % 4 || a.x_lo || a.epi != GEMM_STORE)) return hipErrorInvalidValue;
+  if (a.w.w16) {
+    if ((size_t)a.w.ntile * (a.w.k / BK) * 4096u > 0xffffffffull) return hipErrorInvalidValue;
+    return launch_bits<16>(s, a);
+  }
   switch (a.w.bits) {
     case 4: return launch_bits<4>(s, a);
     case 6: return launch_bits<6>(s, a);

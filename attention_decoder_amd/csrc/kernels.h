@@ -135,14 +135,24 @@ enum GemmEpi { GEMM_STORE = 0, GEMM_SWIGLU = 1 };
 // 8-byte planes; each plane is 64 lanes contiguous) and one dword of fp16 (scale, bias) for its
 // group. 4-bit codes are reordered inside each 32-bit word (code j of the word at nibble
 // 0, 2, 4, 6, 1, 3, 5, 7 for j = 0 .. 7) so that the byte-permute unpack yields k in order.
+//
+// w16 (nullable) holds the same weights already dequantised, f16(q * s + bias) computed exactly as
+// the GEMM's register dequantisation does, in its operand order: per tile, plane t (t = 0 .. 3) is
+// 64 lanes x 16 B, lane l's 8 fp16 weights of row 32t' + l % 32 at k 64kt + 32(l / 32) + 8t .. +7.
+// The prefill GEMM reads it when present (no dequantisation work in the K loop; 4x the bytes of
+// 4-bit codes), else it dequantises the codes.
 struct GemmW {
   const uint8_t* codes;
   const uint32_t* sb;
+  const uint32_t* w16;
   int32_t n, k, bits, group, ntile;
 };
 size_t gemm_codes_bytes(int n, int k, int bits);
 size_t gemm_sb_bytes(int n, int k);
+size_t gemm_w16_bytes(int n, int k);
 hipError_t launch_repack_gemm(hipStream_t s, const QLinear& w, uint8_t* codes, uint32_t* sb);
+// w16 from the re-tiled codes and (scale, bias) of w (which must already hold them).
+hipError_t launch_repack_gemm16(hipStream_t s, const GemmW& w, uint32_t* w16);
 
 // Decode linears of 3 .. 32 rows on MFMA from the re-tiled weights: the GEMV's STORE, SWIGLU,
 // CONV and LOGITS epilogues with its argument block (x, x_lo, batch, outputs, conv state, argmax

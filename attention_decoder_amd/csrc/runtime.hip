@@ -178,10 +178,15 @@ std::vector<std::pair<int, int>> gemm_shapes(const lfm3_config& c) {
   return v;
 }
 
-// codes then (scale, bias) pairs, each 256-byte aligned
-size_t gemm_w_bytes(int n, int k, int bits) {
+// Whether the layers' linears also get the fp16 operand copy for the prefill GEMM: at 6 bits, whose
+// in-loop unpack is the costliest (the copy's 4x weight bytes cost more than the unpack saves at
+// 4 and 8 bits, measured on the 8k prefill).
+bool gemm_f16_copy(const lfm3_config& c) { return c.bits == 6; }
+
+// codes, (scale, bias) pairs and (layer linears) the fp16 operand copy, each 256-byte aligned
+size_t gemm_w_bytes(int n, int k, int bits, bool f16) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-  return up(gemm_codes_bytes(n, k, bits)) + up(gemm_sb_bytes(n, k));
+  return up(gemm_codes_bytes(n, k, bits)) + up(gemm_sb_bytes(n, k)) + (f16 ? up(gemm_w16_bytes(n, k)) : 0);
 }
 
 Layout make_layout(const lfm3_config& c) {
@@ -227,8 +232,8 @@ Layout make_layout(const lfm3_config& c) {
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
   L.keys = take((size_t)kMaxBatch * kArgmaxParts * 8);   // argmax partials [row][part]
   L.gemm_w_bytes = 0;
-  for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits);
-  if (c.has_embedding) L.gemm_w_bytes += gemm_w_bytes(c.vocab, c.hidden, c.embed_bits);   // the tied head
+  for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits, gemm_f16_copy(c));
+  if (c.has_embedding) L.gemm_w_bytes += gemm_w_bytes(c.vocab, c.hidden, c.embed_bits, false);   // the tied head
   L.gemm_w = take(L.gemm_w_bytes);
   L.total = off;
   return L;
@@ -773,13 +778,19 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
   {
     size_t goff = L.gemm_w;
     hipError_t e = hipSuccess;
-    auto retile = [&](const QLinear& q, const std::string& name) {
+    // with16: also the fp16 operand copy the prefill GEMM reads (the layers' linears; the head
+    // runs only on the decode paths, which read the codes)
+    auto retile = [&](const QLinear& q, const std::string& name, bool with16) {
       GemmW g{};
+      auto up = [](size_t b) { return (b + 255) / 256 * 256; };
       uint8_t* codes = ctx->at<uint8_t>(goff);
-      uint32_t* sbp = (uint32_t*)(codes + (gemm_codes_bytes(q.n, q.k, q.bits) + 255) / 256 * 256);
-      goff += gemm_w_bytes(q.n, q.k, q.bits);
+      uint32_t* sbp = (uint32_t*)(codes + up(gemm_codes_bytes(q.n, q.k, q.bits)));
+      uint32_t* w16 = with16 ? (uint32_t*)((uint8_t*)sbp + up(gemm_sb_bytes(q.n, q.k))) : nullptr;
+      goff += gemm_w_bytes(q.n, q.k, q.bits, with16);
       g.codes = codes; g.sb = sbp; g.n = q.n; g.k = q.k; g.bits = q.bits; g.group = q.group; g.ntile = (q.n + 31) / 32;
       if (e == hipSuccess) e = launch_repack_gemm(ctx->stream, q, codes, sbp);
+      if (with16 && e == hipSuccess) e = launch_repack_gemm16(ctx->stream, g, w16);
+      g.w16 = w16;
       ctx->gemm_by_name[name] = g;
       return g;
     };
@@ -787,13 +798,14 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
       LayerW& lw = ctx->layers[i];
       const std::string p = "layers." + std::to_string(i) + ".";
       const bool conv = lw.type == LFM3_LAYER_CONV;
-      lw.g_in = retile(lw.mix_in, p + (conv ? "conv.in_proj" : "attn.qkvg_proj"));
-      lw.g_out = retile(lw.mix_out, p + (conv ? "conv.out_proj" : "attn.o_proj"));
-      lw.g13 = retile(lw.w13, p + "ffn.w13");
-      lw.g2 = retile(lw.w2, p + "ffn.w2");
+      const bool f16 = gemm_f16_copy(c);
+      lw.g_in = retile(lw.mix_in, p + (conv ? "conv.in_proj" : "attn.qkvg_proj"), f16);
+      lw.g_out = retile(lw.mix_out, p + (conv ? "conv.out_proj" : "attn.o_proj"), f16);
+      lw.g13 = retile(lw.w13, p + "ffn.w13", f16);
+      lw.g2 = retile(lw.w2, p + "ffn.w2", f16);
     }
     if (c.has_embedding) {
-      ctx->g_emb = retile(ctx->emb, "embedding");
+      ctx->g_emb = retile(ctx->emb, "embedding", false);
       ctx->gemm_by_name.erase("embedding");   // the GEMM hook paths stay off the head
     }
     if (e != hipSuccess || goff != L.gemm_w + L.gemm_w_bytes) {
@@ -979,12 +991,13 @@ lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uin
     GemvArgs g{};
     g.w = w; g.x = x_dev; g.ldx = w.k; g.batch = rows; g.epi = GEMV_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2;
     LFM3_TRY(launch_gemv(ctx->stream, g));
-  } else if (path == 1 || path == 3) {
+  } else if (path == 1 || path == 3 || path == 6) {
     if (rows < 1) return ctx->fail(LFM3_ERR_ARG, "GEMM rows must be >= 1");
     auto gt = ctx->gemm_by_name.find(name);
     if (gt == ctx->gemm_by_name.end()) return ctx->fail(LFM3_ERR_ARG, std::string(name) + " has no GEMM copy (the head is decode-only)");
     GemmArgs g{};
     g.w = gt->second; g.x = x_dev; g.ldx = w.k; g.m = rows;
+    if (path == 6) g.w.w16 = nullptr;   // dequantise the codes in the K loop instead of the fp16 copy
     if (path == 3) { g.epi = GEMM_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2; }
     else { g.epi = GEMM_STORE; g.yf = y_dev; g.ldy = w.n; }
     LFM3_TRY(launch_gemm(ctx->stream, g));
@@ -998,7 +1011,7 @@ lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uin
     else { g.epi = GEMV_STORE; g.yf = y_dev; g.ldy = w.n; }
     LFM3_TRY(launch_sgemm(ctx->stream, gt->second, g));
   } else {
-    return ctx->fail(LFM3_ERR_ARG, "path must be 0..5");
+    return ctx->fail(LFM3_ERR_ARG, "path must be 0..6");
   }
   return LFM3_OK;
 }

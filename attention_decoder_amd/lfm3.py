@@ -249,7 +249,8 @@ class Engine:
 
     def linear(self, name, x_f16, path):
         """y fp32 [rows, N] = x (torch fp16 [rows, K]) through the GEMV (path 0), the prefill GEMM
-        (path 1) or the decode MFMA GEMM (path 4); paths 2, 3, 5: the same with the SwiGLU epilogue
+        (path 1; path 6 dequantises the codes in the K loop instead of reading the fp16 copy) or the
+        decode MFMA GEMM (path 4); paths 2, 3, 5: the same with the SwiGLU epilogue
         (fp16 [rows, N/2])."""
         n = None
         from .synth import tensor_plan

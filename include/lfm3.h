@@ -78,8 +78,9 @@ typedef struct lfm3_config {
 typedef struct lfm3_ctx lfm3_ctx;
 
 /* Sizes the caller must allocate: the exact weight-blob size this config implies and the device
- * workspace (KV pool, sliding rings, conv states, RoPE tables, activation scratch, and a re-tiled
- * copy of every prefill GEMM weight: about the quantized size of the layers' linears). Host only. */
+ * workspace (KV pool, sliding rings, conv states, RoPE tables, activation scratch, a re-tiled copy
+ * of every linear's codes and scales for the MFMA paths, and at 6 bits an fp16 copy of the layers'
+ * dequantised linears for the prefill GEMM: 2 more bytes per weight). Host only. */
 lfm3_status lfm3_query_sizes(const lfm3_config* cfg, size_t* blob_bytes, size_t* workspace_bytes);
 
 /* Admission of a weight blob held in host memory: magic, version, every tensor's name, dtype,
@@ -157,10 +158,11 @@ lfm3_status lfm3_dequant_rows(lfm3_ctx* ctx, const char* name, int32_t row0, int
  * One stored linear (name without the .q/.scales/.biases suffix) applied to caller rows, for
  * kernel-level parity: y_dev fp32 [rows, N] = x_dev fp16 [rows, K] times the dequantised weight,
  * through the decode dequant-GEMV (path 0, rows in [1, 8], exact weights), the prefill MFMA GEMM
- * (path 1, weights rounded to fp16) or the decode MFMA GEMM of 3+ rows (path 4, rows in [1, 64],
- * weights rounded to fp16). Paths 2 (GEMV), 3 (GEMM) and 5 (decode MFMA) apply the SwiGLU epilogue
- * of a fused [gate | up] weight instead: y_dev then receives fp16 [rows, N/2] = silu(gate) * up.
- * The embedding (tied head) has only path 0.
+ * (path 1, weights rounded to fp16; at 6 bits read from the fp16 copy), the same GEMM always
+ * dequantising the codes in its K loop (path 6; bitwise the same result as path 1) or the decode MFMA GEMM of 3+ rows
+ * (path 4, rows in [1, 64], weights rounded to fp16). Paths 2 (GEMV), 3 (GEMM) and 5 (decode MFMA)
+ * apply the SwiGLU epilogue of a fused [gate | up] weight instead: y_dev then receives fp16
+ * [rows, N/2] = silu(gate) * up. The embedding (tied head) has only path 0.
  */
 lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uint16_t* x_dev,
                         int32_t rows, float* y_dev);
