@@ -217,15 +217,15 @@ struct AttnDecodeArgs {
 constexpr int kPartStride = kHeadDim + 4;   // split partial: o [128], max, sum, 2 pad (16-byte rows)
 hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a);
 
-// Keys per split of a decode row with `keys` visible keys (a multiple of the 64-key tile): single
-// tiles on sliding layers (the four tiles of a 256-key window run in parallel blocks); on full
-// layers two tiles while that gives at most 32 splits, beyond that the keys in 32 equal splits, so
-// a long row is at most 32 blocks per kv head and its merge reads at most 32 partials. It depends
-// on the row alone, which keeps a row's result independent of the batch it is decoded in.
+// Keys per split of a decode row with `keys` visible keys: one 64-key tile per split (a block per
+// tile runs in parallel) while that gives at most 64 splits, beyond that the keys in 64 equal
+// splits of whole tiles, so a long row is at most 64 blocks per kv head and its merge reads at most
+// 64 partials; sliding layers always take single tiles. It depends on the row alone, which keeps a
+// row's result independent of the batch it is decoded in.
 LFM3_HOST_DEV int attn_decode_split_keys(bool sliding, int keys) {
   if (sliding) return 64;
-  const int s = ((keys + 31) / 32 + 63) / 64 * 64;
-  return s > 128 ? s : 128;
+  const int s = ((keys + 63) / 64 + 63) / 64 * 64;
+  return s > 64 ? s : 64;
 }
 
 }  // namespace lfm3

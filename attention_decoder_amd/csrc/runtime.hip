@@ -138,7 +138,7 @@ bool check_config(const lfm3_config& c, std::string& err) {
   for (int i = 0; i < c.n_layers; ++i)
     if (c.layer_type[i] > LFM3_LAYER_SLIDING) return bad("layer %d has unknown type %d", i, c.layer_type[i]);
   if (c.max_slots < 1) return bad("max_slots %d", c.max_slots);
-  // decode attention merges at most 512 splits of >= 128 keys on full layers
+  // max_ctx sizes the RoPE tables and the page-table rows; 65536 is the largest context validated here
   if (c.max_ctx < 1 || c.max_ctx > 65536) return bad("max_ctx %d outside [1, 65536]", c.max_ctx);
   if (c.page_tokens != kPageTokens) return bad("page_tokens %d: this build runs 16", c.page_tokens);
   if (c.max_chunk < 1) return bad("max_chunk %d", c.max_chunk);
@@ -203,7 +203,7 @@ Layout make_layout(const lfm3_config& c) {
   L.max_rows = std::max(c.max_chunk, c.max_slots);
   L.max_pages = (c.max_ctx + kPageTokens - 1) / kPageTokens;
   L.ring_rows = c.window + c.max_chunk;
-  L.max_splits = std::max(32, c.window / 64) + 1;   // attn_decode_split_keys: <= 32 full splits, window / 64 sliding
+  L.max_splits = std::max(64, c.window / 64) + 1;   // attn_decode_split_keys: <= 64 full splits, window / 64 sliding
   L.big_ld = std::max<int>(3 * c.hidden, qkvg_rows(c));
   L.big_ld = (L.big_ld + 7) / 8 * 8;
   const size_t tab = (size_t)c.max_ctx * kHalfDim * 4;
