@@ -20,7 +20,7 @@ constexpr int kMaxBatch = 64;
 // Argmax partials of the head: block p of a logits launch stores its best key of row r at
 // keys[r * kArgmaxParts + p] (plain stores: no atomics on a shared word); the finalize takes the
 // max over all parts of a row and clears them, so unwritten parts read zero.
-constexpr int kArgmaxParts = 512;
+constexpr int kArgmaxParts = 1024;
 constexpr int kHeadDim = 128;
 constexpr int kHalfDim = 64;
 constexpr int kQPerKv = 4;

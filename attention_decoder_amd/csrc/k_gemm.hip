@@ -426,8 +426,9 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
 // ---------------------------------------------------------------------------------------------
 
 template <int EPI> struct SgTiles { static constexpr int v = EPI == GEMV_SWIGLU ? 2 : EPI == GEMV_CONV ? 3 : 1; };
-constexpr int kHeadTiles = 16;   // 32-row tiles of the head per block
+constexpr int kHeadTiles = 4;    // 32-row tiles of the head per block
 
+// STORE with g.yf_part set: blockIdx.y = K quarter (the block's waves share that quarter's tiles).
 template <int BITS, int EPI, int MT>
 __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
   constexpr int NT = SgTiles<EPI>::v;
@@ -481,9 +482,11 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
     uint32_t sb[NT];
     u32x4_v av[MT][4];
   };
-  const int ns = (nk - wave + 3) / 4;   // K tiles of this wave: wave, wave + 4, ...
+  // K tiles [k0, k0 + nkb) of this block; this wave's: k0 + wave, k0 + wave + 4, ...
+  const int nkb = nk / gridDim.y, k0 = blockIdx.y * nkb;
+  const int ns = (nkb - wave + 3) / 4;
   auto load = [&](int s, WSet& ws) {
-    const int kt = wave + 4 * min(s, ns - 1);
+    const int kt = k0 + wave + 4 * min(s, ns - 1);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       load_run<BITS>(rq, qoff[j], (uint32_t)kt * kTileBytes, ws.run[j]);
@@ -570,7 +573,8 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
       }
     } else if constexpr (EPI == GEMV_STORE) {
       const int n = 32 * tile[0] + c;
-      if (n < N) g.yf[(size_t)r * g.ldy + n] = val(r, c);
+      float* out = blockIdx.y == 0 ? g.yf : g.yf_part[blockIdx.y - 1];
+      if (n < N) out[(size_t)r * g.ldy + n] = val(r, c);
     } else if constexpr (EPI == GEMV_SWIGLU) {
       const float gt = val(r, c), up = val(r, 32 + c);
       g.y[(size_t)r * g.ldy + 32 * tb + c] = f2h_sep(gt / (1.f + __expf(-gt)) * up);
@@ -614,7 +618,7 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
 }
 
 template <int BITS, int EPI, int MT>
-static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks) {
+static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int ksplit = 1) {
   const size_t lds = (size_t)4 * MT * 32 * SgTiles<EPI>::v * 32 * sizeof(float);
   static bool attr = false;
   if (!attr) {
@@ -622,19 +626,24 @@ static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, in
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_sgemm<BITS, EPI, MT>), dim3(blocks), dim3(256), lds, s, w, g);
+  hipLaunchKernelGGL((k_sgemm<BITS, EPI, MT>), dim3(blocks, ksplit), dim3(256), lds, s, w, g);
   return hipGetLastError();
 }
 
 template <int BITS, int EPI>
-static hipError_t launch_sg_epi(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int meff) {
-  return meff <= 32 ? launch_sg<BITS, EPI, 1>(s, w, g, blocks) : launch_sg<BITS, EPI, 2>(s, w, g, blocks);
+static hipError_t launch_sg_epi(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int meff, int ksplit = 1) {
+  return meff <= 32 ? launch_sg<BITS, EPI, 1>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2>(s, w, g, blocks, ksplit);
 }
 
 template <int BITS>
 static hipError_t launch_sg_bits(hipStream_t s, const GemmW& w, const GemvArgs& g, int meff) {
   switch (g.epi) {
-    case GEMV_STORE: return launch_sg_epi<BITS, GEMV_STORE>(s, w, g, w.ntile, meff);
+    case GEMV_STORE: {
+      // narrow outputs (fewer than 128 tiles: one block per tile would leave most CUs idle) split
+      // K in four quarters when the caller provides the partial outputs
+      const bool ks = g.yf_part[0] && g.yf_part[1] && g.yf_part[2] && sgemm_store_ksplit(w);
+      return launch_sg_epi<BITS, GEMV_STORE>(s, w, g, w.ntile, meff, ks ? 4 : 1);
+    }
     case GEMV_SWIGLU: return launch_sg_epi<BITS, GEMV_SWIGLU>(s, w, g, w.n / 64, meff);
     case GEMV_CONV: return launch_sg_epi<BITS, GEMV_CONV>(s, w, g, (w.n / 3) / 32, meff);
     case GEMV_LOGITS:

@@ -116,6 +116,13 @@ __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
       load_f32x8(a.m2 + base + 8 * v, m2v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) mv[j][e] = mv[j][e] + m2v[e];
+      if (a.m3) {
+        float m3v[8], m4v[8];
+        load_f32x8(a.m3 + base + 8 * v, m3v);
+        load_f32x8(a.m4 + base + 8 * v, m4v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mv[j][e] = (mv[j][e] + m3v[e]) + m4v[e];
+      }
     }
   }
   bool ok[kVecBlocks];

@@ -22,6 +22,8 @@ struct NormArgs {
   const float* h_in;
   const float* m;
   const float* m2;  // nullable: the mixer/FFN output is m + m2 (two K-half partials, added in that order)
+  const float* m3;  // nullable (with m2): four K-quarter partials, added as ((m + m2) + m3) + m4
+  const float* m4;
   const bf16_t* w_post;
   const bf16_t* w_pre;
   float* h_out;
@@ -121,6 +123,9 @@ struct GemvArgs {
   int conv_taps;
   int32_t conv_slot[kMaxBatch];
   int max_blocks;             // grid cap (0: default)
+  // decode MFMA GEMM, STORE epilogue (nullable): K split in four quarters run by separate blocks;
+  // quarter 0's sums go to yf, quarters 1..3's to yf_part[0..2] (the consumer adds them in order)
+  float* yf_part[3];
 };
 hipError_t launch_gemv(hipStream_t s, const GemvArgs& a);
 
@@ -158,6 +163,8 @@ hipError_t launch_repack_gemm16(hipStream_t s, const GemmW& w, uint32_t* w16);
 // CONV and LOGITS epilogues with its argument block (x, x_lo, batch, outputs, conv state, argmax
 // keys); the input rows (x, and x_lo as extra rows when set) number at most 64.
 hipError_t launch_sgemm(hipStream_t s, const GemmW& w, const GemvArgs& g);
+// Whether launch_sgemm splits a STORE linear's K in four (when the caller passes yf_part).
+inline bool sgemm_store_ksplit(const GemmW& w) { return w.ntile < 128 && (w.k / 64) % 4 == 0 && w.k / 64 >= 16; }
 
 // Y[m, n] = sum_k X[m, k] * f16(q[n, k] * s + bias), MFMA fp16 with fp32 accumulation.
 // STORE writes fp32 yf; SWIGLU writes fp16 y.

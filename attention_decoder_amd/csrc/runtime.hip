@@ -153,7 +153,7 @@ bool check_config(const lfm3_config& c, std::string& err) {
 struct Layout {
   size_t cos_f, sin_f, cos_s, sin_s;
   size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
-  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, m2, xf, part, keys;
+  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, m2, m3, m4, xf, part, keys;
   size_t gemm_w, gemm_w_bytes;   // re-tiled copies of every prefill GEMM weight
   size_t total;
   int max_rows, max_pages, ring_rows, max_splits, big_ld;
@@ -228,6 +228,8 @@ Layout make_layout(const lfm3_config& c) {
   L.qrot = take(R * c.n_q_heads * kHeadDim * 2);
   L.m = take(R * H * 4);
   L.m2 = take(R * H * 4);
+  L.m3 = take((size_t)kMaxBatch * H * 4);   // decode K-split partials 3 and 4 (m2 holds partial 2)
+  L.m4 = take((size_t)kMaxBatch * H * 4);
   L.xf = take(R * H * 2);
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
   L.keys = take((size_t)kMaxBatch * kArgmaxParts * 8);   // argmax partials [row][part]
@@ -527,6 +529,10 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
   f16_t* sb = ctx->at<f16_t>(L.sbuf);
   f16_t* mix = ctx->at<f16_t>(L.mix);
   float* m = ctx->at<float>(L.m);
+  // the mixer / FFN output projections of 3+ rows split K in four (sgemm_store_ksplit); m then
+  // holds the first quarter's sums and mq[0..2] the others, which the next norm adds
+  float* mq[3] = {ctx->at<float>(L.m2), ctx->at<float>(L.m3), ctx->at<float>(L.m4)};
+  bool m_split = false;
   f16_t* xf = ctx->at<f16_t>(L.xf);
   f16_t* xlo = ctx->at<f16_t>(L.xlo);
   const bool fuse = M <= 2;
@@ -559,6 +565,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     }
     NormArgs na{};
     na.h_in = cur; na.h_out = cur; na.m = w_post ? m : nullptr; na.w_post = w_post; na.w_pre = w_pre;
+    if (w_post && m_split) { na.m2 = mq[0]; na.m3 = mq[1]; na.m4 = mq[2]; }
     na.x_out = x; na.x_lo = split ? xlo : nullptr;
     na.capture = capture; na.x_copy = x_copy; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
     hipError_t e = timed(ctx, LFM3_PROF_NORM, (double)M * H * 14, 0, [&] { return launch_resid_norm(s, na); });
@@ -606,7 +613,9 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     {
       GemvArgs g{};
       g.w = lw.mix_out; g.x = mix; g.ldx = H; g.batch = M; g.epi = GEMV_STORE; g.yf = m; g.ldy = H;
+      if (mfma) for (int q = 0; q < 3; ++q) g.yf_part[q] = mq[q];
       LFM3_TRY(gemv(g, (double)M * H * 4, &lw.g_out));
+      m_split = mfma && sgemm_store_ksplit(lw.g_out);
     }
     {
       GemvArgs g{};
@@ -616,7 +625,9 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     {
       GemvArgs g{};
       g.w = lw.w2; g.x = sb; g.ldx = c.ffn; g.batch = M; g.epi = GEMV_STORE; g.yf = m; g.ldy = H;
+      if (mfma) for (int q = 0; q < 3; ++q) g.yf_part[q] = mq[q];
       LFM3_TRY(gemv(g, (double)M * H * 4, &lw.g2));
+      m_split = mfma && sgemm_store_ksplit(lw.g2);
     }
   }
   const bf16_t* last_post = ctx->layers[c.n_layers - 1].post_ffn;
@@ -631,6 +642,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     NormArgs nf{};
     nf.h_in = cur; nf.h_out = cur; nf.x_out = xf; nf.rows = M; nf.hidden = H; nf.eps = c.norm_eps;
     nf.m = m; nf.w_post = last_post; nf.w_pre = ctx->emb_norm;
+    if (m_split) { nf.m2 = mq[0]; nf.m3 = mq[1]; nf.m4 = mq[2]; }
     nf.capture = cap(c.n_layers - 1);
     nf.x_copy = hidden_out;
     LFM3_TRY(timed(ctx, LFM3_PROF_NORM, (double)M * H * 14, 0, [&] { return launch_resid_norm(s, nf); }));
