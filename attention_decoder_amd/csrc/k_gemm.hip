@@ -426,16 +426,23 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
 // ---------------------------------------------------------------------------------------------
 
 template <int EPI> struct SgTiles { static constexpr int v = EPI == GEMV_SWIGLU ? 2 : EPI == GEMV_CONV ? 3 : 1; };
+// Whether the waves' partial tiles exceed 96 KB of LDS together (then they are reduced per column tile).
+template <int EPI, int MT, int WV> struct SgTwoPhase {
+  static constexpr bool v = (size_t)WV * MT * 32 * SgTiles<EPI>::v * 32 * sizeof(float) > 96 * 1024;
+};
 constexpr int kHeadTiles = 4;    // 32-row tiles of the head per block
 
 // STORE with g.yf_part set: blockIdx.y = K quarter (the block's waves share that quarter's tiles).
-template <int BITS, int EPI, int MT>
-__global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
+// WV waves per block (4, or 8 to halve each wave's K walk on the short-M, one-block-per-CU launches).
+template <int BITS, int EPI, int MT, int WV>
+__global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
   constexpr int NT = SgTiles<EPI>::v;
+  constexpr int NTH = 64 * WV;
+  static_assert(EPI != GEMV_LOGITS || WV == 4, "the head's argmax slots assume 256 threads");
   constexpr int D = MT == 1 ? 4 : 2;   // K tiles in flight per wave
   constexpr int TW = NT * 32, TR = MT * 32;
   constexpr uint32_t kTileBytes = 256u * BITS;
-  extern __shared__ __attribute__((aligned(16))) float sg_smem[];   // [4 waves][TR][TW]
+  extern __shared__ __attribute__((aligned(16))) float sg_smem[];   // [WV][TR][32] partials, [TR][TW] sums
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hf = lane >> 5, c32 = lane & 31;
   const int R = g.batch;
@@ -482,11 +489,11 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
     uint32_t sb[NT];
     u32x4_v av[MT][4];
   };
-  // K tiles [k0, k0 + nkb) of this block; this wave's: k0 + wave, k0 + wave + 4, ...
+  // K tiles [k0, k0 + nkb) of this block; this wave's: k0 + wave, k0 + wave + WV, ...
   const int nkb = nk / gridDim.y, k0 = blockIdx.y * nkb;
-  const int ns = (nkb - wave + 3) / 4;
+  const int ns = (nkb - wave + WV - 1) / WV;
   auto load = [&](int s, WSet& ws) {
-    const int kt = k0 + wave + 4 * min(s, ns - 1);
+    const int kt = k0 + wave + WV * min(s, ns - 1);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       load_run<BITS>(rq, qoff[j], (uint32_t)kt * kTileBytes, ws.run[j]);
@@ -541,26 +548,56 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
     }
   }
 
-  // the partial tiles into LDS: acc[i][j][v] is virtual row 32i + 8(v/4) + 4(lane/32) + v%4,
-  // column 32j + lane%32 of the block's tile
-  float* mine = sg_smem + (size_t)wave * TR * TW;
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mine[(32 * i + 8 * (v >> 2) + 4 * hf + (v & 3)) * TW + 32 * j + c32] = acc[i][j][v];
-  __syncthreads();
+  // the partial tiles: acc[i][j][v] is virtual row 32i + 8(v/4) + 4(lane/32) + v%4, column
+  // 32j + lane%32 of the block's tile; an element's total adds the waves' partials in wave order.
+  // All waves' tiles at once when they fit (SgTwoPhase false), else one column tile at a time
+  // into a table of sums (the same additions in the same order).
   auto total = [&](int vr, int col) {
-    const int e = vr * TW + col;
-    return ((sg_smem[e] + sg_smem[TR * TW + e]) + sg_smem[2 * TR * TW + e]) + sg_smem[3 * TR * TW + e];
+    if constexpr (SgTwoPhase<EPI, MT, WV>::v) {
+      return sg_smem[WV * TR * 32 + vr * TW + col];
+    } else {
+      const int e = vr * TW + col;
+      float t = sg_smem[e];
+#pragma unroll
+      for (int q = 1; q < WV; ++q) t += sg_smem[q * TR * TW + e];
+      return t;
+    }
   };
+  if constexpr (SgTwoPhase<EPI, MT, WV>::v) {
+    float* part = sg_smem;
+    float* sums = sg_smem + WV * TR * 32;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      float* mine = part + (size_t)wave * TR * 32;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[(32 * i + 8 * (v >> 2) + 4 * hf + (v & 3)) * 32 + c32] = acc[i][j][v];
+      __syncthreads();
+      for (int e = tid; e < TR * 32; e += NTH) {
+        float t = part[e];
+#pragma unroll
+        for (int q = 1; q < WV; ++q) t += part[q * TR * 32 + e];
+        sums[(e >> 5) * TW + 32 * j + (e & 31)] = t;
+      }
+      __syncthreads();
+    }
+  } else {
+    float* mine = sg_smem + (size_t)wave * TR * TW;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[(32 * i + 8 * (v >> 2) + 4 * hf + (v & 3)) * TW + 32 * j + c32] = acc[i][j][v];
+    __syncthreads();
+  }
   auto val = [&](int r, int col) {
     float v = total(r, col);
     if (pair) v = v + total(r + R, col);
     return v;
   };
-  for (int idx = tid; idx < R * 32; idx += 256) {
+  for (int idx = tid; idx < R * 32; idx += NTH) {
     const int r = idx >> 5, c = idx & 31;
     if constexpr (EPI == GEMV_LOGITS) {
       // logits, and the running argmax key of the row (order key, then the lower id)
@@ -617,22 +654,33 @@ __global__ void __launch_bounds__(256) k_sgemm(GemmW w, GemvArgs g) {
   }
 }
 
-template <int BITS, int EPI, int MT>
-static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int ksplit = 1) {
-  const size_t lds = (size_t)4 * MT * 32 * SgTiles<EPI>::v * 32 * sizeof(float);
+template <int BITS, int EPI, int MT, int WV>
+static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int ksplit) {
+  const size_t lds = SgTwoPhase<EPI, MT, WV>::v ? ((size_t)WV * MT * 32 * 32 + (size_t)MT * 32 * SgTiles<EPI>::v * 32) * sizeof(float)
+                                                : (size_t)WV * MT * 32 * SgTiles<EPI>::v * 32 * sizeof(float);
   static bool attr = false;
   if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_sgemm<BITS, EPI, MT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute((const void*)k_sgemm<BITS, EPI, MT, WV>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_sgemm<BITS, EPI, MT>), dim3(blocks, ksplit), dim3(256), lds, s, w, g);
+  hipLaunchKernelGGL((k_sgemm<BITS, EPI, MT, WV>), dim3(blocks, ksplit), dim3(64 * WV), lds, s, w, g);
   return hipGetLastError();
 }
 
+// Up to 32 operand rows: 8 waves per block (the partial tiles of 8 waves fit in LDS); the head keeps
+// 4 (its argmax slots are laid out for 256 threads).
+// 8 waves per block for the conv in_proj (one block per 32 channels: 64 blocks, each with a long
+// K walk), 4 for the rest (measured: 8 waves elsewhere lost), and 4 when the block's K range has
+// fewer than 8 tiles (every wave needs one). The wave count depends on the weight shape and
+// epilogue alone, never on the row count, so a row's sums do not depend on its batch.
 template <int BITS, int EPI>
 static hipError_t launch_sg_epi(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int meff, int ksplit = 1) {
-  return meff <= 32 ? launch_sg<BITS, EPI, 1>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2>(s, w, g, blocks, ksplit);
+  constexpr int W1 = EPI == GEMV_CONV ? 8 : 4;
+  const int nkb = (w.k / BK) / ksplit;
+  if (nkb < 4) return hipErrorInvalidValue;
+  if (nkb < W1) return meff <= 32 ? launch_sg<BITS, EPI, 1, 4>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2, 4>(s, w, g, blocks, ksplit);
+  return meff <= 32 ? launch_sg<BITS, EPI, 1, W1>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2, W1>(s, w, g, blocks, ksplit);
 }
 
 template <int BITS>

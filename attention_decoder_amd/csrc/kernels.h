@@ -164,7 +164,7 @@ hipError_t launch_repack_gemm16(hipStream_t s, const GemmW& w, uint32_t* w16);
 // keys); the input rows (x, and x_lo as extra rows when set) number at most 64.
 hipError_t launch_sgemm(hipStream_t s, const GemmW& w, const GemvArgs& g);
 // Whether launch_sgemm splits a STORE linear's K in four (when the caller passes yf_part).
-inline bool sgemm_store_ksplit(const GemmW& w) { return w.ntile < 128 && (w.k / 64) % 4 == 0 && w.k / 64 >= 16; }
+inline bool sgemm_store_ksplit(const GemmW& w) { return w.ntile < 128 && (w.k / 64) % 4 == 0 && w.k / 64 >= 32; }
 
 // Y[m, n] = sum_k X[m, k] * f16(q[n, k] * s + bias), MFMA fp16 with fp32 accumulation.
 // STORE writes fp32 yf; SWIGLU writes fp16 y.
