@@ -144,13 +144,16 @@ __global__ void __launch_bounds__(512, 1) k_attn_prefill(AttnArgs a) {
     }
     // acc v of sub-tile sub is key kb + 32 sub + 16(v/8) + 8(lane/32) + v%8
     const bool interior = kb >= k_lo && kb + PKT - 1 <= p_first && (a.window == 0 || p_last - kb < a.window);
+    // the running max is kept in scaled units; the tile's max is taken on the raw scores (the
+    // scale is positive, so the maximum commutes with it) and the scale enters each exponent
+    // through one fma
     float sv[2][16];
     float mloc = -__builtin_huge_valf();
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = st[sub][v] * scale;
+        float x = st[sub][v];
         if (!interior) {
           const int j = kb + 32 * sub + 16 * (v >> 3) + 8 * (lane >> 5) + (v & 7);
           bool vis = j >= k_lo && j <= qpos;
@@ -161,7 +164,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_prefill(AttnArgs a) {
         mloc = fmaxf(mloc, x);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
+    const float m_new = fmaxf(m_run, mloc * scale);
     const bool none = m_new == -__builtin_huge_valf();
     const float alpha = none ? 1.f : exp2f(m_run - m_new);
     float lsum = 0.f;
@@ -170,17 +173,20 @@ __global__ void __launch_bounds__(512, 1) k_attn_prefill(AttnArgs a) {
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float pr = none ? 0.f : exp2f(sv[sub][v] - m_new);
+        const float pr = none ? 0.f : exp2f(fmaf(sv[sub][v], scale, -m_new));
         lsum += pr;
         pv[sub][v >> 3][v & 7] = (_Float16)pr;
       }
     lsum += __shfl_xor(lsum, 32, 64);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
+    // O is rescaled only when some lane's max moved (alpha is exactly 1 otherwise)
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[d][v] *= alpha;
+        for (int v = 0; v < 16; ++v) o[d][v] *= alpha;
+    }
     // O^T[dim][query] += V^T[dim][keys] P^T[keys][query]
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
