@@ -208,23 +208,25 @@ __global__ void __launch_bounds__(512, 1) k_attn_prefill(AttnArgs a) {
   // local tile i + 1 is stored while local tile i is computed; local tile i + 3 is loaded into the
   // registers the store freed (register sets A and B alternate, so nothing is copied across the
   // loop edge). Both halves run the same number of iterations (a past-the-end tile of the odd half
-  // is not computed) so that they meet at every barrier.
+  // is not computed) so that they meet at every barrier; tiles past a half's end are not loaded
+  // (a spare load would hold the wave until it returns), and their stores are never read.
   const int nloc = (ntiles + 1) / 2;
-  u32x4_v kA[4], vA[4], kB[4], vB[4];
+  u32x4_v kA[4], vA[4], kB[4] = {}, vB[4] = {};
+  auto live = [&](int i_loc) { return 2 * i_loc + kh < ntiles; };
   gload(0, kA, vA);
   sstore(0, kA, vA);
-  gload(1, kA, vA);
-  gload(2, kB, vB);
+  if (live(1)) gload(1, kA, vA);
+  if (live(2)) gload(2, kB, vB);
   __syncthreads();
   for (int i = 0; i < nloc; i += 2) {
     sstore(1, kA, vA);
-    gload(i + 3, kA, vA);
-    if (2 * i + kh < ntiles) compute(i);
+    if (live(i + 3)) gload(i + 3, kA, vA);
+    if (live(i)) compute(i);
     __syncthreads();
     if (i + 1 >= nloc) break;
     sstore(0, kB, vB);
-    gload(i + 4, kB, vB);
-    if (2 * (i + 1) + kh < ntiles) compute(i + 1);
+    if (live(i + 4)) gload(i + 4, kB, vB);
+    if (live(i + 1)) compute(i + 1);
     __syncthreads();
   }
 
@@ -334,7 +336,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
   // tile loads, branch-free: thread t moves 16-byte chunks t + 256 q (q < 4) of the 64 key x 16
   // chunk tile; keys past the split read the split's last key (not used)
   auto key_of = [&](int tile, int q) { return min(j0 + tile * TILE + ((tid + 256 * q) >> 4), j_end); };
-  int pg[4], pgn[4];
+  int pg[4], pgn[4] = {0, 0, 0, 0};
   u32x4_v kr[4], vr[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) pg[q] = PAGED ? pt[key_of(0, q) / kPageTokens] : 0;
@@ -356,8 +358,9 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
     kr[q] = *(const u32x4_v*)(a.kv.k + o);
     vr[q] = *(const u32x4_v*)(a.kv.v + o);
   }
+  if (PAGED && n_tiles > 1)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) pgn[q] = PAGED ? pt[key_of(1, q) / kPageTokens] : 0;
+    for (int q = 0; q < 4; ++q) pgn[q] = pt[key_of(1, q) / kPageTokens];
 
   // q heads 4 kvh + w (wave w): per-head RMSNorm + RoPE ("LFM3-1.7B port": partial RoPE on the
   // full layers); lane holds dims lane, lane + 64; q rounded to fp16 as the prefill path stores it
@@ -410,15 +413,19 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
       else *(u32x4_v*)(vt + kk * KVS + 8 * (tid - 16)) = *(const u32x4_v*)(vnew + 8 * (tid - 16));
     }
     __syncthreads();
-    // 2. the next tile's loads (clamped past the split: valid keys, unused), page ids one further
+    // 2. the next tile's loads and the page ids one further, only where the split has that tile
+    //    (a spare load would hold the block until it returns)
+    if (tile + 1 < n_tiles) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const size_t o = kv_off<PAGED>(a.kv, slot, key_of(tile + 1, q), pgn[q], kvh, nkv) + 8 * ((tid + 256 * q) & 15);
-      kr[q] = *(const u32x4_v*)(a.kv.k + o);
-      vr[q] = *(const u32x4_v*)(a.kv.v + o);
+      for (int q = 0; q < 4; ++q) {
+        const size_t o = kv_off<PAGED>(a.kv, slot, key_of(tile + 1, q), pgn[q], kvh, nkv) + 8 * ((tid + 256 * q) & 15);
+        kr[q] = *(const u32x4_v*)(a.kv.k + o);
+        vr[q] = *(const u32x4_v*)(a.kv.v + o);
+      }
     }
+    if (PAGED && tile + 2 < n_tiles)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) pgn[q] = PAGED ? pt[key_of(tile + 2, q) / kPageTokens] : 0;
+      for (int q = 0; q < 4; ++q) pgn[q] = pt[key_of(tile + 2, q) / kPageTokens];
     // 3. scores: thread -> key t / 4, dims [32 (t % 4), + 32) for the 4 heads; sum over 4 lanes
     {
       const int key = tid >> 2, qd = tid & 3;

@@ -328,9 +328,11 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   const int ngw = g0 < n_groups ? (n_groups - 1 - g0) / gstride + 1 : 0;
   const int nsteps = ngw * NITW;
 
-  // The wave walks a flat sequence of (group, k iteration) steps. Weights for step s + 1 are
-  // loaded into the other of two register sets while step s is computed. Loads are branch-free:
-  // out-of-range steps load a valid clamped address and are not computed.
+  // The wave walks a flat sequence of (group, k iteration) steps in two register sets: the first
+  // two steps' weights are requested before the input is staged, and the load of step s + 2 is
+  // issued as soon as step s is computed. Addresses are clamped into range; no step past the
+  // wave's last is requested (a spare load of a clamped address still costs its full latency at
+  // the end of the wave).
   struct WRegs {
     uint32_t q[RG][Q::NDW];
     bf16_t s[RG], b[RG];   // raw bits: converted when used
@@ -376,13 +378,14 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
 
   WRegs wa, wb;
   if constexpr (PRO) {
-    // prologue loads first, then the weight prefetch, then the prologue arithmetic: the in-order
-    // load counter lets the weights stay in flight through the prologue
+    // prologue loads first, then the weight prefetch (two steps), then the prologue arithmetic:
+    // the in-order load counter lets the weights stay in flight through the prologue
     PrologueRegs<BT> p;
     prologue_load<BT>(a, p);
     conv_prefetch();
     __builtin_amdgcn_sched_barrier(0);
     fetch(wa, 0);
+    if (nsteps > 1) fetch(wb, 1);
     __builtin_amdgcn_sched_barrier(0);
     prologue_compute<BITS, BT>(a, p, xp, xsum, red, split);
   } else {
@@ -395,6 +398,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     fetch(wa, 0);
+    if (nsteps > 1) fetch(wb, 1);
     __builtin_amdgcn_sched_barrier(0);
     plain_stage<BITS, BT>(a, p, 0, xp, xsum, split);
     for (int j0 = PlainVB<BT>::v; 256 * j0 < K / 8; j0 += PlainVB<BT>::v) {
@@ -568,10 +572,12 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   };
 
   for (int step = 0; step < nsteps; step += 2) {
-    fetch(wb, step + 1);
     consume(wa, step);
-    fetch(wa, step + 2);
-    if (step + 1 < nsteps) consume(wb, step + 1);
+    if (step + 2 < nsteps) fetch(wa, step + 2);
+    if (step + 1 < nsteps) {
+      consume(wb, step + 1);
+      if (step + 3 < nsteps) fetch(wb, step + 3);
+    }
   }
   if constexpr (EPI == GEMV_LOGITS) {
 #pragma unroll
