@@ -312,11 +312,17 @@ LFM3_DEV size_t kv_off(const KvRef& kv, int slot, int pos, int page, int kvh, in
   else return (((size_t)slot * n_kv + kvh) * kv.ring + (pos % kv.ring)) * kHeadDim;
 }
 
+// a.x * b.x + a.y * b.y + c over fp16 pairs (the words are taken by value: a bit cast of a vector
+// element in place was seen to read element 0 for every index)
+LFM3_DEV float dot2_h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_v, a), __builtin_bit_cast(f16x2_v, b), c, false);
+}
+
 template <bool PAGED>
 __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) f16_t kt[(TILE + 1) * KVS];   // row TILE: spare (unused keys)
   __shared__ __attribute__((aligned(16))) f16_t vt[(TILE + 1) * KVS];
-  __shared__ float qs[kQPerKv][kHeadDim];
+  __shared__ __attribute__((aligned(16))) f16_t qs[kQPerKv][kHeadDim];   // the fp16 queries
   __shared__ float sc[kQPerKv][TILE];
   __shared__ __attribute__((aligned(16))) f16_t knew[kHeadDim], vnew[kHeadDim];
   const int split = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
@@ -367,8 +373,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
   {
     const float rr = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)kHeadDim + a.eps);
     const float n0 = x0 * rr * qn0, n1 = x1 * rr * qn1;
-    qs[wave][lane] = h2f(f2h(n0 * c - n1 * sn));
-    qs[wave][lane + kHalfDim] = h2f(f2h(n1 * c + n0 * sn));
+    qs[wave][lane] = f2h(n0 * c - n1 * sn);
+    qs[wave][lane + kHalfDim] = f2h(n1 * c + n0 * sn);
   }
   if (has_new && wave < 2) {
     float o0, o1;
@@ -426,7 +432,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
     if (PAGED && tile + 2 < n_tiles)
 #pragma unroll
       for (int q = 0; q < 4; ++q) pgn[q] = pt[key_of(tile + 2, q) / kPageTokens];
-    // 3. scores: thread -> key t / 4, dims [32 (t % 4), + 32) for the 4 heads; sum over 4 lanes
+    // 3. scores: thread -> key t / 4, dims [32 (t % 4), + 32) for the 4 heads, as fp16 pair dot
+    //    products with fp32 accumulation; sum over 4 lanes
     {
       const int key = tid >> 2, qd = tid & 3;
       float d[kQPerKv] = {0.f, 0.f, 0.f, 0.f};
@@ -435,10 +442,11 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
       for (int e8 = 0; e8 < 4; ++e8) {
         const u32x4_v v = *(const u32x4_v*)(kp + 8 * e8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kf = h2f((f16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu)));
+        for (int hh = 0; hh < kQPerKv; ++hh) {
+          const u32x4_v qv = *(const u32x4_v*)(&qs[hh][32 * qd + 8 * e8]);
 #pragma unroll
-          for (int hh = 0; hh < kQPerKv; ++hh) d[hh] = fmaf(qs[hh][32 * qd + 8 * e8 + e], kf, d[hh]);
+          for (int e = 0; e < 4; ++e)
+            d[hh] = dot2_h(v[e], qv[e], d[hh]);
         }
       }
 #pragma unroll
