@@ -329,8 +329,8 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   const int nsteps = ngw * NITW;
 
   // The wave walks a flat sequence of (group, k iteration) steps in two register sets: the first
-  // two steps' weights are requested before the input is staged, and the load of step s + 2 is
-  // issued as soon as step s is computed. Addresses are clamped into range; no step past the
+  // step's weights are requested before the input is staged, the second's before (plain input) or
+  // after (norm prologue) the staging, and the load of step s + 2 as soon as step s is computed. Addresses are clamped into range; no step past the
   // wave's last is requested (a spare load of a clamped address still costs its full latency at
   // the end of the wave).
   struct WRegs {
@@ -378,16 +378,18 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
 
   WRegs wa, wb;
   if constexpr (PRO) {
-    // prologue loads first, then the weight prefetch (two steps), then the prologue arithmetic:
-    // the in-order load counter lets the weights stay in flight through the prologue
+    // prologue loads first, then the first step's weights, then the prologue arithmetic (the
+    // in-order load counter lets the weights stay in flight through it), then the second step's
+    // weights (requested before the arithmetic, they measured slower: the prologue is the longer
+    // path)
     PrologueRegs<BT> p;
     prologue_load<BT>(a, p);
     conv_prefetch();
     __builtin_amdgcn_sched_barrier(0);
     fetch(wa, 0);
-    if (nsteps > 1) fetch(wb, 1);
     __builtin_amdgcn_sched_barrier(0);
     prologue_compute<BITS, BT>(a, p, xp, xsum, red, split);
+    if (nsteps > 1) fetch(wb, 1);
   } else {
     // (a barrier without a wait: every wave of the block has its input loads queued before any
     // wave queues weight loads behind them)
