@@ -24,8 +24,9 @@ LFM3_DEV float sigmoidf_(float g) { return 1.f / (1.f + __expf(-g)); }
 // prefill: one block per (32 query rows, kv head), 8 waves: wave w is query head 4 * kvh + w % 4 over
 // the even (w < 4) or odd (w >= 4) key tiles; the two halves' softmax states are merged at the end.
 // Keys are walked in 64-key tiles staged in LDS: the K and V rows of a tile are loaded into
-// registers two tiles ahead (branch-free; keys outside [k_lo, p_last] read a clamped valid key,
-// masked in the softmax) and stored into one of two LDS buffers one tile ahead. The page ids of the
+// registers two tiles ahead (keys outside [k_lo, p_last] read a clamped valid key, masked in the
+// softmax; no tile past a half's end is loaded) and stored into one of two LDS buffers one tile
+// ahead. The page ids of the
 // block's key range are staged in LDS once, so no global load result feeds an address in the loop.
 // LDS rows are 256 bytes (128 dims) with the 16-byte chunk c of row r stored at chunk c ^ (r & 15),
 // which keeps the K reads, the V transpose reads and the stores free of bank conflicts.
@@ -339,8 +340,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeArgs a) {
   const bool has_new = split == ns - 1;   // the current position is this split's last key
   const int32_t* pt = PAGED ? a.kv.page_table + (size_t)slot * a.kv.max_pages : nullptr;
 
-  // tile loads, branch-free: thread t moves 16-byte chunks t + 256 q (q < 4) of the 64 key x 16
-  // chunk tile; keys past the split read the split's last key (not used)
+  // tile loads: thread t moves 16-byte chunks t + 256 q (q < 4) of the 64 key x 16 chunk tile;
+  // keys past the split in its last tile read the split's last key (not used)
   auto key_of = [&](int tile, int q) { return min(j0 + tile * TILE + ((tid + 256 * q) >> 4), j_end); };
   int pg[4], pgn[4] = {0, 0, 0, 0};
   u32x4_v kr[4], vr[4];
