@@ -631,10 +631,10 @@ static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
   // narrow matrices still spread over the whole chip.
   const int nit = (K / Q::CH + 63) / 64;
   const bool split = nit % 4 == 0;
-  // the head (147 MB at 4 bits, bandwidth-bound) takes two blocks per CU for more loads in flight
+  // a block per 4 row groups (one per wave), or per group when its 4 waves share the group's K
+  // range, at most one block per CU; the head (147 MB at 4 bits, bandwidth-bound) takes two blocks
+  // per CU for more loads in flight. Waves with more groups than one walk them in steps.
   const int cap = a.max_blocks > 0 ? a.max_blocks : (a.epi == GEMV_LOGITS ? 2 * LFM3_GEMV_MAX_BLOCKS : LFM3_GEMV_MAX_BLOCKS);
-  // one wave per row group up to 512 groups, two up to 1024, then four (capped): a block's
-  // staging of the input is cheap next to leaving CUs idle on the small linears
   int grid = split ? n_groups : (n_groups + 3) / 4;
   if (grid > cap) grid = cap;
   if (a.epi == GEMV_LOGITS && grid > kArgmaxParts) return hipErrorInvalidValue;
