@@ -301,7 +301,8 @@ hipError_t launch_attn_prefill(hipStream_t s, const AttnArgs& a) {
 // partials (max, sum, o) go to the workspace and k_attn_merge, the next launch, combines them (the
 // kernel boundary orders the partials' stores before its loads; an in-kernel last-block merge
 // would need an agent-scope release and acquire per block, a write-back and an invalidate of the
-// L2, which measured slower than the extra launch).
+// L2, which measured slower than the extra launch). With merge_in_consumer set (sliding layers at
+// 1-2 rows, at most kFusedMergeSplits splits) the o_proj GEMV merges them in its prologue instead.
 // ---------------------------------------------------------------------------------------------
 
 constexpr int TILE = 64;
@@ -561,7 +562,7 @@ hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a) {
     hipLaunchKernelGGL(k_attn_decode<true>, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_attn_decode<false>, dim3(a.max_splits, a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
-  if (a.max_splits > 1) hipLaunchKernelGGL(k_attn_merge, dim3(a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
+  if (a.max_splits > 1 && !a.merge_in_consumer) hipLaunchKernelGGL(k_attn_merge, dim3(a.n_kv_heads, a.rows.n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -297,6 +297,74 @@ LFM3_DEV void plain_stage(const GemvArgs& a, const PlainRegs<BT>& p, int j0, uin
     }
 }
 
+// Attention-merge input (PRO = 2, the o_proj of 1-2 rows): thread t stages vector block t (dims
+// 8 (t % 16) .. + 7 of head t / 16) of each row from the decode attention's split partials: with
+// M the largest split max, x = sigmoid(g) * sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, the
+// online-softmax merge ("LFM3-1.7B port": sigmoid head gate in fp32), rounded to fp16; a row with
+// one split takes x as the attention kernel wrote it. Every load (clamped to the row's last split)
+// is issued before the weights', the arithmetic after.
+template <int BT> struct MergeRegs {
+  float4 o[BT][kFusedMergeSplits][2];
+  float2 ml[BT][kFusedMergeSplits];
+  uint4 xr[BT];
+  float g[BT];
+};
+
+template <int BT>
+LFM3_DEV void merge_load(const GemvArgs& a, MergeRegs<BT>& p) {
+  const int nq = a.w.k / kHeadDim;
+  const int v = min((int)threadIdx.x, a.w.k / 8 - 1);
+  const int h = v >> 4, d0 = 8 * (v & 15);
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    const int rb = min(b, a.batch - 1);
+    const int ns = a.merge_splits[rb];
+    p.g[b] = a.gate_src[(size_t)rb * a.gate_ld + h];
+    p.xr[b] = load_u16x8(a.x + (size_t)rb * a.ldx + 8 * v);
+    const float* ph = a.part + ((size_t)rb * nq + h) * a.part_splits * kPartStride;
+#pragma unroll
+    for (int q = 0; q < kFusedMergeSplits; ++q) {
+      const float* ps = ph + (size_t)min(q, ns - 1) * kPartStride;
+      p.o[b][q][0] = *(const float4*)(ps + d0);
+      p.o[b][q][1] = *(const float4*)(ps + d0 + 4);
+      p.ml[b][q] = *(const float2*)(ps + kHeadDim);
+    }
+  }
+}
+
+template <int BITS, int BT>
+LFM3_DEV void merge_stage(const GemvArgs& a, const MergeRegs<BT>& p, uint16_t* xp, float2* xsum) {
+  const int K = a.w.k, v = threadIdx.x;
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    const int ns = a.merge_splits[min(b, a.batch - 1)];
+    uint32_t hw[4] = {p.xr[b].x, p.xr[b].y, p.xr[b].z, p.xr[b].w};
+    if (ns > 1) {
+      float mx = p.ml[b][0].x;
+#pragma unroll
+      for (int q = 1; q < kFusedMergeSplits; ++q) mx = q < ns ? fmaxf(mx, p.ml[b][q].x) : mx;
+      float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < kFusedMergeSplits; ++q) {
+        if (q >= ns) continue;
+        const float w = __expf(p.ml[b][q].x - mx);
+        l = fmaf(w, p.ml[b][q].y, l);
+        const float ov[8] = {p.o[b][q][0].x, p.o[b][q][0].y, p.o[b][q][0].z, p.o[b][q][0].w,
+                             p.o[b][q][1].x, p.o[b][q][1].y, p.o[b][q][1].z, p.o[b][q][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(w, ov[e], o[e]);
+      }
+      const float inv = l > 0.f ? (1.f / (1.f + __expf(-p.g[b]))) / l : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hw[e] = (uint32_t)f2h(o[2 * e] * inv) | ((uint32_t)f2h(o[2 * e + 1] * inv) << 16);
+    }
+    if (b >= a.batch)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hw[e] = 0u;
+    put_x8<BITS>(xp, xsum, K, b, v, hw, v < K / 8);
+  }
+}
+
 // KW waves share one row group (each takes every KW-th k iteration; the partial totals are added
 // in wave order through LDS), or KW = 1: each wave owns its groups.
 template <int BITS, int BT, int EPI, int PRO, int KW>
@@ -377,7 +445,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   };
 
   WRegs wa, wb;
-  if constexpr (PRO) {
+  if constexpr (PRO == 1) {
     // prologue loads first, then the first step's weights, then the prologue arithmetic (the
     // in-order load counter lets the weights stay in flight through it), then the second step's
     // weights (requested before the arithmetic, they measured slower: the prologue is the longer
@@ -390,6 +458,16 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     prologue_compute<BITS, BT>(a, p, xp, xsum, red, split);
     if (nsteps > 1) fetch(wb, 1);
+  } else if constexpr (PRO == 2) {
+    MergeRegs<BT> mr;
+    merge_load<BT>(a, mr);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(wa, 0);
+    if (nsteps > 1) fetch(wb, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    merge_stage<BITS, BT>(a, mr, xp, xsum);
   } else {
     // (a barrier without a wait: every wave of the block has its input loads queued before any
     // wave queues weight loads behind them)
@@ -645,6 +723,13 @@ static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
     } else {
       return hipErrorInvalidValue;
     }
+  } else if (a.part) {
+    if constexpr (BT <= 2) {
+      if (split || a.epi != GEMV_STORE) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, 2, 1>), dim3(grid), dim3(256), lds, s, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
     if (split) launch_epi<BITS, BT, 0, 4>(s, a, grid, lds);
     else launch_epi<BITS, BT, 0, 1>(s, a, grid, lds);
@@ -692,6 +777,16 @@ static hipError_t launch_bits(hipStream_t s, const GemvArgs& a) {
 
 hipError_t launch_gemv(hipStream_t s, const GemvArgs& a) {
   if (a.batch <= 0) return hipSuccess;
+  // attention-merge input: one vector block per thread, whole heads, 1-2 rows of at most
+  // kFusedMergeSplits splits, plain STORE
+  if (a.part) {
+    if (a.h_src || a.x_lo || a.split_x || a.epi != GEMV_STORE || a.batch > 2 || a.w.k > 256 * 8 ||
+        a.w.k % kHeadDim || !a.gate_src || !a.x || a.part_splits < 1)
+      return hipErrorInvalidValue;
+    for (int b = 0; b < a.batch; ++b)
+      if (a.merge_splits[b] < 1 || a.merge_splits[b] > kFusedMergeSplits || a.merge_splits[b] > a.part_splits)
+        return hipErrorInvalidValue;
+  }
   // vector staging: rows of 8-element blocks, 16-byte aligned; the norm prologue takes K <= 4096
   if (a.w.k % 8 || (a.h_src && a.w.k > 256 * 8 * kVecBlocks)) return hipErrorInvalidValue;
   if (a.h_src ? ((uintptr_t)a.h_src % 16 || (a.m && (uintptr_t)a.m % 16) || (uintptr_t)a.w_pre % 16 ||

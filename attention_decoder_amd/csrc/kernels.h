@@ -126,6 +126,16 @@ struct GemvArgs {
   // decode MFMA GEMM, STORE epilogue (nullable): K split in four quarters run by separate blocks;
   // quarter 0's sums go to yf, quarters 1..3's to yf_part[0..2] (the consumer adds them in order)
   float* yf_part[3];
+  // attention-merge input (o_proj at 1-2 rows; part nullable): x row b is the gated merge of row
+  // b's decode-attention split partials ([batch, K / 128 heads, part_splits, kPartStride]) when
+  // merge_splits[b] > 1, else x itself (the attention kernel's gated output of a one-split row);
+  // the gate logit of head h of row b is gate_src[b * gate_ld + h]. At most kFusedMergeSplits
+  // splits a row, K <= 2048, no norm prologue.
+  const float* part;
+  int part_splits;
+  const float* gate_src;
+  int gate_ld;
+  int32_t merge_splits[kMaxBatch];
 };
 hipError_t launch_gemv(hipStream_t s, const GemvArgs& a);
 
@@ -220,8 +230,10 @@ struct AttnDecodeArgs {
   f16_t* out;          // [rows, n_q_heads * 128]
   float* part;         // [rows, n_q_heads, max_splits, kPartStride]
   int max_splits;      // grid extent: the most splits any row needs
+  int merge_in_consumer;   // the next linear merges the partials itself (no merge launch)
 };
 constexpr int kPartStride = kHeadDim + 4;   // split partial: o [128], max, sum, 2 pad (16-byte rows)
+constexpr int kFusedMergeSplits = 4;        // most splits per row the o_proj GEMV merges itself
 hipError_t launch_attn_decode(hipStream_t s, const AttnDecodeArgs& a);
 
 // Keys per split of a decode row with `keys` visible keys: one 64-key tile per split (a block per

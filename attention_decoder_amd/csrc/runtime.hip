@@ -577,6 +577,9 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
   for (int i = 0; i < c.n_layers; ++i) {
     const LayerW& lw = ctx->layers[i];
     const bf16_t* w_post = i > 0 ? ctx->layers[i - 1].post_ffn : nullptr;
+    // sliding layers at 1-2 rows: the o_proj GEMV merges the attention's split partials itself
+    // (a window of at most kFusedMergeSplits tiles), which saves the merge launch
+    GemvArgs merge_in{};
     if (lw.type == LFM3_LAYER_CONV) {
       GemvArgs g{};
       g.w = lw.mix_in; g.epi = GEMV_CONV; g.y = mix; g.ldy = H;
@@ -604,14 +607,21 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
       double kv_bytes = 0;
       for (int r = 0; r < M; ++r) {
         const int lo = full ? 0 : std::max(0, rows.pos[r] - (c.window - 1));
-        ms = std::max(ms, (rows.pos[r] - lo) / attn_decode_split_keys(!full, rows.pos[r] - lo + 1) + 1);
+        const int ns = (rows.pos[r] - lo) / attn_decode_split_keys(!full, rows.pos[r] - lo + 1) + 1;
+        ms = std::max(ms, ns);
+        merge_in.merge_splits[r] = ns;
         kv_bytes += (double)(rows.pos[r] - lo + 1) * c.n_kv_heads * kHeadDim * 2 * 2;
       }
       aa.max_splits = ms;
+      if (!mfma && !full && c.window <= kFusedMergeSplits * 64) {
+        aa.merge_in_consumer = 1;
+        merge_in.part = aa.part; merge_in.part_splits = ms;
+        merge_in.gate_src = big + aa.gate_col; merge_in.gate_ld = L.big_ld;
+      }
       LFM3_TRY(timed(ctx, LFM3_PROF_ATTN_DECODE, kv_bytes, 0, [&] { return launch_attn_decode(s, aa); }));
     }
     {
-      GemvArgs g{};
+      GemvArgs g = merge_in;
       g.w = lw.mix_out; g.x = mix; g.ldx = H; g.batch = M; g.epi = GEMV_STORE; g.yf = m; g.ldy = H;
       if (mfma) for (int q = 0; q < 3; ++q) g.yf_part[q] = mq[q];
       LFM3_TRY(gemv(g, (double)M * H * 4, &lw.g_out));
