@@ -365,8 +365,9 @@ LFM3_DEV void merge_stage(const GemvArgs& a, const MergeRegs<BT>& p, uint16_t* x
   }
 }
 
-// KW waves share one row group (each takes every KW-th k iteration; the partial totals are added
-// in wave order through LDS), or KW = 1: each wave owns its groups.
+// The input: PRO = 0 plain fp16 rows, 1 the decode norm prologue, 2 the attention merge. KW waves
+// share one row group (each takes every KW-th k iteration; the partial totals are added in wave
+// order through LDS), or KW = 1: each wave owns its groups.
 template <int BITS, int BT, int EPI, int PRO, int KW>
 __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   using Q = QT<BITS>;
