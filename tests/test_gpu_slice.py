@@ -5,7 +5,8 @@ oracle on the same seeded inputs:
 - dequantised weights bit-exact (fp32 value and its RNE fp16, the prefill GEMM's LDS value);
 - hidden state after every layer within rel-L2 1e-2, final normed hidden within rel-L2 1e-2;
 - prompt prefill vs one-row decode at cut points; chunked prefill across the 256-token seam;
-- concurrent == solo: a batched decode row is bitwise equal to the same row decoded alone.
+- concurrent == solo: a batched decode row is bitwise equal to the same row decoded alone (1-2
+  rows), or to the same row in another batch of its class (3+ rows).
 """
 import numpy as np
 import pytest
@@ -165,6 +166,34 @@ def test_concurrent_rows(eng, torch_dev):
         rel = float(torch.linalg.norm(a - b) / torch.linalg.norm(b))
         print(f"slot {i}: batched vs solo rel-L2 {rel:.2e}")
         assert rel < 1e-2, (i, rel)
+
+
+def test_two_rows_equal_one_row(eng, torch_dev):
+    """Two slots decoded together (the exact GEMV path of 1-2 rows; the sliding layer's split
+    partials merged in the o_proj GEMV's prologue) equal, bitwise, each slot decoded alone. On the
+    sliding layer one row has a single split (41-43 keys) and the other two (71-73 keys)."""
+    torch = torch_dev
+    prompts = [synth.hidden_rows(30 + i, n) for i, n in enumerate([40, 70])]
+    steps = [synth.hidden_rows(40 + i, 3) for i in range(2)]
+    solo = []
+    for i in range(2):
+        eng.reset(i)
+        eng.prefill(i, hidden=_rows_dev(torch, prompts[i]))
+        rows = [eng.decode([i], hidden=_rows_dev(torch, steps[i][t:t + 1]), hidden_out=True)["hidden"].clone()
+                for t in range(3)]
+        solo.append(torch.cat(rows))
+    for i in range(2):
+        eng.reset(i)
+        eng.prefill(i, hidden=_rows_dev(torch, prompts[i]))
+    pair = [[], []]
+    for t in range(3):
+        xb = np.stack([steps[0][t], steps[1][t]])
+        o = eng.decode([0, 1], hidden=_rows_dev(torch, xb), hidden_out=True)["hidden"]
+        for j in range(2):
+            pair[j].append(o[j:j + 1].clone())
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert torch.equal(torch.cat(pair[i]), solo[i]), i
 
 
 def test_reset_equals_fresh_and_pool_census(eng, torch_dev, oracle80):
