@@ -253,6 +253,25 @@ def prefill_8k(eng, synth, torch, dev):
     return round(8192 / (ms / 1e3), 1), ms, toks
 
 
+def cold_prefill_8k(synth, torch, dev):
+    """The first 8192-token prefill of a freshly created q4 g64 context, to the last row's logits and
+    id (weights already copied to HBM and re-tiled at create; caches, TLBs and the new context's
+    KV pages cold): the cold time to first token, in ms."""
+    from attention_decoder_amd.lfm3 import Engine
+    cfg = synth.full_config(bits=4, group=64, max_slots=8, max_ctx=8704, max_chunk=2048)
+    e = Engine(cfg, synth.cached_blob(cfg, seed=0))
+    toks = torch.from_numpy(synth.prompt_tokens(5, 8192)).to(dev)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(e.stream)
+    e.prefill(0, tokens=toks, logits=True, argmax=True)
+    b.record(e.stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    e.close()
+    return ms
+
+
 def run_extras(eng, synth, torch, dev, schemes=True):
     from attention_decoder_amd.lfm3 import Engine
     out = {}
@@ -277,6 +296,8 @@ def run_extras(eng, synth, torch, dev, schemes=True):
     total_flops = sum(v["flops"] for v in prof.values()) + 2.0 * 128000 * 2048
     out["prefill_8k_frac_of_f16_peak"] = round(total_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
     log(f"8k prefill {out['prefill_8k_tok_s']} tok/s ({ms:.2f} ms); {out['prefill_8k_breakdown_ms']}")
+    out["prefill_8k_cold_ttft_ms"] = round(cold_prefill_8k(synth, torch, dev), 3)
+    log(f"8k prefill, first pass of a fresh context: {out['prefill_8k_cold_ttft_ms']} ms")
     if schemes:
         # the same two workloads at the 8-bit (8 streams) and 6-bit (8k prefill) schemes
         for bits, key in [(8, "q8"), (6, "q6")]:
