@@ -44,6 +44,8 @@ def main():
     ap.add_argument("--profile-only", action="store_true", help="one short step for rocprofv3 runs")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="one 8192-token prefill in 2048-row passes, for rocprofv3 runs")
+    ap.add_argument("--profile-8stream", action="store_true",
+                    help="the 8-stream job (prompts U[300, 2960], then 16 greedy steps at B = 8), for rocprofv3 runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --profile-only: also run three 256 MiB device copies (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -90,6 +92,20 @@ def main():
         eng.prefill(0, tokens=toks, logits=True, argmax=True)
         torch.cuda.synchronize()
         log("profile-prefill step done")
+        return
+
+    if args.profile_8stream:
+        lens = synth.stream_prompt_lengths(4, 8)
+        prompts = synth.stream_prompts(4, lens)
+        for i in range(8):
+            eng.reset(i)
+            eng.prefill(i, tokens=torch.from_numpy(prompts[i]).to(dev), logits=False, argmax=False)
+        sid = torch.empty((17, 8), dtype=torch.int32, device=dev)
+        sid[0] = torch.from_numpy(np.array([p[-1] for p in prompts], dtype=np.int32)).to(dev)
+        for t in range(16):
+            eng.decode(list(range(8)), tokens=sid[t], logits=False, argmax=True, out={"argmax": sid[t + 1]})
+        torch.cuda.synchronize()
+        log("profile-8stream job done")
         return
 
     if args.profile_only:
