@@ -47,6 +47,30 @@ def test_gemv_matches_float64(eng, weights, name):
         assert err < 1e-4, (name, rows, err)
 
 
+@pytest.mark.parametrize("bits,group", [(8, 64), (6, 64), (4, 32)])
+def test_gemv_other_schemes(bits, group):
+    """The decode GEMV (exact weights) at 8-bit, 6-bit and 4-bit g32 on the slice's shapes, at 1, 2 and
+    5 rows, against the float64 product with the exactly dequantised weights."""
+    import torch
+    from attention_decoder_amd import synth
+    from attention_decoder_amd.lfm3 import Engine
+    cfg = synth.slice3_config(bits=bits, group=group, max_slots=1, max_chunk=64)
+    blob = synth.cached_blob(cfg, seed=0)
+    eng = Engine(cfg, blob)
+    b = ref.Blob(blob)
+    try:
+        for name in SHAPES:
+            w = ref.load_linear(b, name, bits, group)
+            for rows in (1, 2, 5):
+                x, xd = _x(torch, rows, w.shape[1], 100 + bits + group + rows)
+                y = eng.linear(name, xd, 0).float().cpu().numpy().astype(np.float64)
+                want = x.astype(np.float64) @ w.T
+                err = np.abs(y - want).max() / np.abs(want).max()
+                assert err < 1e-4, (bits, group, name, rows, err)
+    finally:
+        eng.close()
+
+
 @pytest.mark.parametrize("name", SHAPES)
 def test_gemm_matches_float64(eng, weights, name):
     import torch
