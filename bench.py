@@ -3,9 +3,12 @@
 Headline (one JSON line on stdout): decode tokens/s at batch 1 on the 24-layer geometry with 4-bit
 g64 weights -- a step is one whole job: a 2048-token prompt prefilled in one 2048-row pass, then
 256 greedy decode steps; value = decode tokens / decode time over the timed steps. The same line
-carries the 2048-token prefill rate, the 8-stream decode and the 8192-token prefill (extras), the
-roofline figure of the dominant kernel (the dequant-GEMV: algorithmic bytes per launch over its
-event-timed launch duration) and the float64 oracle timed on the host cores (cpu_baseline).
+carries the 2048-token prefill rate, the 8-stream decode, the 8192-token prefill (warm, and the
+first pass of a fresh context) and the other weight schemes (extras), the roofline figure of the
+dominant kernel (the dequant-GEMV: algorithmic bytes per launch over its event-timed launch
+duration, with the HBM bytes of the committed counter record) and the float64 oracle timed on the
+host cores (cpu_baseline). --profile-only, --profile-8stream and --profile-prefill run one short
+job each for profiler runs.
 
 Inputs are seeded and synthetic (random-init weights quantized from N(0, 0.02), token ids uniform
 in [0, 128000)); they are resident in HBM before the timed region starts.
