@@ -24,12 +24,14 @@ LFM3_DEV float deq_value(uint32_t q, float s, float b) { return fmaf((float)q, s
 // linears, 8-bit in the VL 4-bit export)
 // ---------------------------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) k_embed(QLinear e, const int32_t* __restrict__ tokens, float* __restrict__ h) {
+__global__ void __launch_bounds__(256) k_embed(QLinear e, const int32_t* __restrict__ tokens, float* __restrict__ h,
+                                                uint32_t* flags) {
   const int r = blockIdx.x;
   const int tok = tokens[r];
   float* out = h + (size_t)r * e.k;
   if (tok < 0 || tok >= e.n) {
     for (int k = threadIdx.x; k < e.k; k += blockDim.x) out[k] = 0.f;
+    if (threadIdx.x == 0) atomicOr(flags, 1u);
     return;
   }
   const size_t row_bytes = (size_t)e.k * e.bits / 8;
@@ -43,9 +45,9 @@ __global__ void __launch_bounds__(256) k_embed(QLinear e, const int32_t* __restr
   }
 }
 
-hipError_t launch_embed(hipStream_t s, const QLinear& emb, const int32_t* tokens, int rows, float* h) {
+hipError_t launch_embed(hipStream_t s, const QLinear& emb, const int32_t* tokens, int rows, float* h, uint32_t* flags) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, emb, tokens, h);
+  hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, emb, tokens, h, flags);
   return hipGetLastError();
 }
 

@@ -7,9 +7,9 @@ namespace lfm3 {
 
 // ---- k_misc.hip ------------------------------------------------------------------------------
 
-// h[r, :] = q * scale + bias (fp32, exact) of embedding row tokens[r] (ids outside [0, vocab)
-// give zeros).
-hipError_t launch_embed(hipStream_t s, const QLinear& emb, const int32_t* tokens, int rows, float* h);
+// h[r, :] = q * scale + bias (fp32, exact) of embedding row tokens[r]; an id outside [0, vocab)
+// gives a zero row and sets bit 0 of *flags (a device word the host reads at its next sync).
+hipError_t launch_embed(hipStream_t s, const QLinear& emb, const int32_t* tokens, int rows, float* h, uint32_t* flags);
 // h[r, :] = float(bf16 input row)
 hipError_t launch_bf16_to_f32(hipStream_t s, const bf16_t* in, int rows, int cols, float* out);
 

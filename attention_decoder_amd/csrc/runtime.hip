@@ -153,7 +153,7 @@ bool check_config(const lfm3_config& c, std::string& err) {
 struct Layout {
   size_t cos_f, sin_f, cos_s, sin_s;
   size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
-  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, m2, m3, m4, xf, part, keys;
+  size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, m2, m3, m4, xf, part, keys, flags;
   size_t gemm_w, gemm_w_bytes;   // re-tiled copies of every prefill GEMM weight
   size_t total;
   int max_rows, max_pages, ring_rows, max_splits, big_ld;
@@ -233,6 +233,7 @@ Layout make_layout(const lfm3_config& c) {
   L.xf = take(R * H * 2);
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
   L.keys = take((size_t)kMaxBatch * kArgmaxParts * 8);   // argmax partials [row][part]
+  L.flags = take(256);                                     // device-side argument errors (bit 0: token id)
   L.gemm_w_bytes = 0;
   for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits, gemm_f16_copy(c));
   if (c.has_embedding) L.gemm_w_bytes += gemm_w_bytes(c.vocab, c.hidden, c.embed_bits, false);   // the tied head
@@ -865,7 +866,8 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
   // zero the conv states, page table and argmax keys
   if (launch_zero(ctx->stream, ctx->at<void>(L.conv_state), (size_t)c.max_slots * L.conv_slot * 2) != hipSuccess ||
       launch_zero(ctx->stream, ctx->at<void>(L.page_table), (size_t)c.max_slots * L.max_pages * 4) != hipSuccess ||
-      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)kMaxBatch * kArgmaxParts * 8) != hipSuccess) {
+      launch_zero(ctx->stream, ctx->at<void>(L.keys), (size_t)kMaxBatch * kArgmaxParts * 8) != hipSuccess ||
+      launch_zero(ctx->stream, ctx->at<void>(L.flags), 256) != hipSuccess) {
     delete ctx;
     g_err = "workspace clear failed";
     return LFM3_ERR_DEVICE;
@@ -901,7 +903,7 @@ lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
     rows.n = M; rows.mode = 0; rows.slot0 = slot; rows.pos0 = ctx->len[slot];
     if (tokens_dev) {
       LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, (double)M * (lin_bytes(ctx->emb) / ctx->emb.n + 4.0 * c.hidden), 0,
-                     [&] { return launch_embed(ctx->stream, ctx->emb, tokens_dev + r0, M, h); }));
+                     [&] { return launch_embed(ctx->stream, ctx->emb, tokens_dev + r0, M, h, ctx->at<uint32_t>(ctx->L.flags)); }));
     } else {
       LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev + (size_t)r0 * H, M, H, h));
     }
@@ -949,7 +951,7 @@ lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_hos
   float* h = ctx->at<float>(ctx->L.h);
   if (tokens_dev) {
     LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, (double)n * (lin_bytes(ctx->emb) / ctx->emb.n + 4.0 * c.hidden), 0,
-                   [&] { return launch_embed(ctx->stream, ctx->emb, tokens_dev, n, h); }));
+                   [&] { return launch_embed(ctx->stream, ctx->emb, tokens_dev, n, h, ctx->at<uint32_t>(ctx->L.flags)); }));
   } else {
     LFM3_TRY(launch_bf16_to_f32(ctx->stream, hidden_dev, n, c.hidden, h));
   }
@@ -974,6 +976,18 @@ lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot) {
 int32_t lfm3_slot_length(const lfm3_ctx* ctx, int32_t slot) {
   if (!ctx || slot < 0 || slot >= ctx->cfg.max_slots) return -1;
   return ctx->len[slot];
+}
+
+lfm3_status lfm3_synchronize(lfm3_ctx* ctx) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  LFM3_TRY(hipStreamSynchronize(ctx->stream));
+  uint32_t flags = 0;
+  LFM3_TRY(hipMemcpy(&flags, ctx->at<uint32_t>(ctx->L.flags), 4, hipMemcpyDeviceToHost));
+  if (flags == 0) return LFM3_OK;
+  LFM3_TRY(launch_zero(ctx->stream, ctx->at<void>(ctx->L.flags), 256));
+  LFM3_TRY(hipStreamSynchronize(ctx->stream));
+  return ctx->fail(LFM3_ERR_ARG, "a token id outside [0, vocab) reached the embedding since the last synchronize "
+                                 "(its row was embedded as zeros)");
 }
 
 int32_t lfm3_free_pages(const lfm3_ctx* ctx) { return ctx ? (int32_t)ctx->free_pages.size() : -1; }
@@ -1034,6 +1048,100 @@ lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uin
     LFM3_TRY(launch_sgemm(ctx->stream, gt->second, g));
   } else {
     return ctx->fail(LFM3_ERR_ARG, "path must be 0..6");
+  }
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io) {
+  if (!ctx || !io) { g_err = "NULL argument"; return LFM3_ERR_ARG; }
+  const lfm3_config& c = ctx->cfg;
+  const Layout& L = ctx->L;
+  const int n = io->n_rows;
+  if (!io->slots_host || !io->pos_host || !io->qkvg_dev || !io->q_norm_dev || !io->k_norm_dev || !io->k_cache_dev ||
+      !io->v_cache_dev || !io->out_dev)
+    return ctx->fail(LFM3_ERR_ARG, "NULL buffer in lfm3_attn_io");
+  const int width = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim + c.n_q_heads;
+  if (io->ld < width) return ctx->fail(LFM3_ERR_ARG, "ld below the qkvg row width");
+  if (io->n_slots < 1) return ctx->fail(LFM3_ERR_ARG, "n_slots must be >= 1");
+  const bool decode = io->decode != 0, sliding = io->sliding != 0;
+  if (decode && (n < 1 || n > std::min(c.max_slots, (int)kMaxBatch)))
+    return ctx->fail(LFM3_ERR_ARG, "decode rows outside [1, min(max_slots, 64)]");
+  if (!decode && (n < 1 || n > L.max_rows)) return ctx->fail(LFM3_ERR_ARG, "prefill rows outside [1, max(max_chunk, max_slots)]");
+  const int nrow_pos = decode ? n : 1;
+  std::vector<char> seen(io->n_slots, 0);
+  int last_pos_max = 0;
+  for (int b = 0; b < nrow_pos; ++b) {
+    const int sl = io->slots_host[b], p = io->pos_host[b];
+    if (sl < 0 || sl >= io->n_slots) return ctx->fail(LFM3_ERR_ARG, "slot outside [0, n_slots)");
+    if (seen[sl]) return ctx->fail(LFM3_ERR_ARG, "slot appears twice in one decode launch");
+    seen[sl] = 1;
+    const int last = decode ? p : p + n - 1;
+    if (p < 0 || (int64_t)last >= c.max_ctx) return ctx->fail(LFM3_ERR_ARG, "position outside [0, max_ctx)");
+    last_pos_max = std::max(last_pos_max, last);
+  }
+  KvRef kv{};
+  kv.k = (f16_t*)io->k_cache_dev;
+  kv.v = (f16_t*)io->v_cache_dev;
+  if (sliding) {
+    const int need = decode ? c.window : c.window + n - 1;
+    if (io->ring_rows < need) return ctx->fail(LFM3_ERR_ARG, "ring_rows below what the window and pass need");
+    kv.ring = io->ring_rows;
+  } else {
+    if (!io->page_table_dev || io->max_pages < 1 || io->max_pages > 8192 || io->n_pool_pages < 1)
+      return ctx->fail(LFM3_ERR_ARG, "full layers need a page table, max_pages in [1, 8192] and n_pool_pages >= 1");
+    if (last_pos_max / kPageTokens >= io->max_pages) return ctx->fail(LFM3_ERR_ARG, "positions past the page table row");
+    std::vector<int32_t> pt((size_t)io->n_slots * io->max_pages);
+    LFM3_TRY(hipStreamSynchronize(ctx->stream));
+    LFM3_TRY(hipMemcpy(pt.data(), io->page_table_dev, pt.size() * 4, hipMemcpyDeviceToHost));
+    for (int b = 0; b < nrow_pos; ++b) {
+      const int sl = io->slots_host[b], last = decode ? io->pos_host[b] : io->pos_host[b] + n - 1;
+      for (int g = 0; g <= last / kPageTokens; ++g) {
+        const int32_t pg = pt[(size_t)sl * io->max_pages + g];
+        if (pg < 0 || pg >= io->n_pool_pages) return ctx->fail(LFM3_ERR_ARG, "page table entry outside [0, n_pool_pages)");
+      }
+    }
+    kv.page_table = io->page_table_dev;
+    kv.max_pages = io->max_pages;
+    kv.ring = 0;
+  }
+  Rows rows{};
+  rows.n = n;
+  if (decode) {
+    rows.mode = 1;
+    for (int b = 0; b < n; ++b) { rows.slot[b] = io->slots_host[b]; rows.pos[b] = io->pos_host[b]; }
+  } else {
+    rows.mode = 0; rows.slot0 = io->slots_host[0]; rows.pos0 = io->pos_host[0];
+  }
+  const float* cos_t = ctx->at<float>(sliding ? L.cos_s : L.cos_f);
+  const float* sin_t = ctx->at<float>(sliding ? L.sin_s : L.sin_f);
+  const int gate_col = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
+  if (decode) {
+    AttnDecodeArgs aa{};
+    aa.qkvg = io->qkvg_dev; aa.ld = io->ld; aa.gate_col = gate_col;
+    aa.q_norm = io->q_norm_dev; aa.k_norm = io->k_norm_dev; aa.cos_t = cos_t; aa.sin_t = sin_t;
+    aa.kv = kv; aa.rows = rows; aa.window = sliding ? c.window : 0;
+    aa.n_q_heads = c.n_q_heads; aa.n_kv_heads = c.n_kv_heads; aa.eps = c.norm_eps;
+    aa.out = (f16_t*)io->out_dev; aa.part = ctx->at<float>(L.part);
+    int ms = 1;
+    for (int b = 0; b < n; ++b) {
+      const int p = rows.pos[b];
+      const int lo = sliding ? std::max(0, p - (c.window - 1)) : 0;
+      ms = std::max(ms, (p - lo) / attn_decode_split_keys(sliding, p - lo + 1) + 1);
+    }
+    if (ms > L.max_splits) return ctx->fail(LFM3_ERR_ARG, "more decode splits than the workspace holds");
+    aa.max_splits = ms;
+    LFM3_TRY(launch_attn_decode(ctx->stream, aa));
+  } else {
+    QkRopeArgs qa{};
+    qa.qkvg = io->qkvg_dev; qa.ld = io->ld; qa.q_norm = io->q_norm_dev; qa.k_norm = io->k_norm_dev;
+    qa.cos_t = cos_t; qa.sin_t = sin_t; qa.q_out = ctx->at<f16_t>(L.qrot); qa.kv = kv; qa.rows = rows;
+    qa.n_q_heads = c.n_q_heads; qa.n_kv_heads = c.n_kv_heads; qa.eps = c.norm_eps;
+    LFM3_TRY(launch_qk_rope(ctx->stream, qa));
+    AttnArgs aa{};
+    aa.q = qa.q_out; aa.gate = io->qkvg_dev + gate_col; aa.ldg = io->ld; aa.kv = kv; aa.rows = rows;
+    aa.window = sliding ? c.window : 0; aa.n_q_heads = c.n_q_heads; aa.n_kv_heads = c.n_kv_heads;
+    aa.out = (f16_t*)io->out_dev;
+    LFM3_TRY(launch_attn_prefill(ctx->stream, aa));
   }
   return LFM3_OK;
 }

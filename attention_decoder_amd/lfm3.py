@@ -46,6 +46,18 @@ def config_from_dict(d: dict) -> Config:
     return c
 
 
+class AttnIO(ctypes.Structure):
+    """lfm3_attn_io: the attention-core hook's buffers (include/lfm3.h)."""
+    _fields_ = [("sliding", ctypes.c_int32), ("decode", ctypes.c_int32), ("n_rows", ctypes.c_int32),
+                ("slots_host", ctypes.POINTER(ctypes.c_int32)), ("pos_host", ctypes.POINTER(ctypes.c_int32)),
+                ("qkvg_dev", ctypes.c_void_p), ("ld", ctypes.c_int32),
+                ("q_norm_dev", ctypes.c_void_p), ("k_norm_dev", ctypes.c_void_p),
+                ("k_cache_dev", ctypes.c_void_p), ("v_cache_dev", ctypes.c_void_p),
+                ("page_table_dev", ctypes.c_void_p),
+                ("max_pages", ctypes.c_int32), ("n_pool_pages", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("ring_rows", ctypes.c_int32), ("out_dev", ctypes.c_void_p)]
+
+
 _lib = None
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 
@@ -67,12 +79,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lfm3_prefill": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp]),
         "lfm3_decode_batch": (_i32, [_vp, _i32, P(_i32), _vp, _vp, _vp, _vp, _vp]),
         "lfm3_reset_slot": (_i32, [_vp, _i32]),
+        "lfm3_synchronize": (_i32, [_vp]),
         "lfm3_slot_length": (_i32, [_vp, _i32]),
         "lfm3_free_pages": (_i32, [_vp]),
         "lfm3_last_error": (ctypes.c_char_p, [_vp]),
         "lfm3_capture_layers": (_i32, [_vp, _vp, _i32]),
         "lfm3_dequant_rows": (_i32, [_vp, ctypes.c_char_p, _i32, _i32, _vp, _vp]),
         "lfm3_linear": (_i32, [_vp, ctypes.c_char_p, _i32, _vp, _i32, _vp]),
+        "lfm3_attention": (_i32, [_vp, P(AttnIO)]),
         "lfm3_profile": (_i32, [_vp, _i32]),
         "lfm3_profile_read": (_i32, [_vp, _i32, P(ctypes.c_double), P(ctypes.c_int64), P(ctypes.c_double),
                                      P(ctypes.c_double)]),
@@ -137,6 +151,10 @@ def lfm3_reset_slot(ctx, slot):
     _check(load_library().lfm3_reset_slot(ctx, slot), ctx)
 
 
+def lfm3_synchronize(ctx):
+    _check(load_library().lfm3_synchronize(ctx), ctx)
+
+
 def lfm3_slot_length(ctx, slot) -> int:
     return load_library().lfm3_slot_length(ctx, slot)
 
@@ -159,6 +177,19 @@ def lfm3_destroy(ctx):
 
 def lfm3_linear(ctx, name: str, path: int, x, rows: int, y):
     _check(load_library().lfm3_linear(ctx, name.encode(), path, _ptr(x), rows, _ptr(y)), ctx)
+
+
+def lfm3_attention(ctx, *, sliding, decode, slots, pos, qkvg, q_norm, k_norm, k_cache, v_cache, out,
+                   page_table=None, max_pages=0, n_pool_pages=0, n_slots=1, ring_rows=0):
+    """The attention-core hook: torch device tensors in, marshalled into lfm3_attn_io."""
+    n = int(qkvg.shape[0])
+    sl = (ctypes.c_int32 * len(slots))(*[int(v) for v in slots])
+    ps = (ctypes.c_int32 * len(pos))(*[int(v) for v in pos])
+    io = AttnIO(int(sliding), int(decode), n, sl, ps, qkvg.data_ptr(), int(qkvg.stride(0)), q_norm.data_ptr(),
+                k_norm.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                None if page_table is None else page_table.data_ptr(), int(max_pages), int(n_pool_pages),
+                int(n_slots), int(ring_rows), out.data_ptr())
+    _check(load_library().lfm3_attention(ctx, ctypes.byref(io)), ctx)
 
 
 PROF_KINDS = {"gemv": 0, "gemm": 1, "attn_decode": 2, "attn_prefill": 3, "conv": 4, "norm": 5, "other": 6}
@@ -237,6 +268,9 @@ class Engine:
 
     def reset(self, slot):
         lfm3_reset_slot(self.ctx, slot)
+
+    def synchronize(self):
+        lfm3_synchronize(self.ctx)
 
     def length(self, slot):
         return lfm3_slot_length(self.ctx, slot)

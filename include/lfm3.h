@@ -21,6 +21,11 @@
  *    that stream is synchronised. Greedy ids stay on the device, so a decode loop needs no host sync.
  *  - Errors: every argument, capacity and slot check runs on the host before anything is enqueued;
  *    on error nothing is enqueued, the state is unchanged, and lfm3_last_error() names the cause.
+ *    Two kinds of error are found later. Token ids live on the device, so they are checked by the
+ *    embedding kernel: an id outside [0, vocab) embeds as a zero row and raises a device flag that
+ *    the next lfm3_synchronize() reports as LFM3_ERR_ARG (the call that enqueued it returned
+ *    LFM3_OK). A HIP launch failure (LFM3_ERR_DEVICE) inside lfm3_prefill or lfm3_decode_batch can
+ *    leave the slots of that call partly advanced: reset them before using them again.
  *  - Threading: one context per stream; a context is not thread-safe.
  *  - Layouts: row-major. bf16/fp16 are passed as uint16_t bit patterns. Hidden rows are [rows, hidden].
  */
@@ -36,7 +41,8 @@ extern "C" {
 
 typedef enum {
   LFM3_OK = 0,
-  LFM3_ERR_ARG = 1,      /* null pointer, bad row count, token id out of [0, vocab), duplicate slot */
+  LFM3_ERR_ARG = 1,      /* null pointer, bad row count, duplicate slot; token id out of [0, vocab)
+                            (reported by lfm3_synchronize)                                           */
   LFM3_ERR_CONFIG = 2,   /* geometry or scheme this build does not run (named in the message)      */
   LFM3_ERR_BLOB = 3,     /* weight blob header: magic, names, shapes, dtypes, byte ranges, size      */
   LFM3_ERR_SLOT = 4,     /* slot index outside [0, max_slots)                                       */
@@ -77,9 +83,12 @@ typedef struct lfm3_config {
 
 typedef struct lfm3_ctx lfm3_ctx;
 
-/* Sizes the caller must allocate: the exact weight-blob size this config implies and the device
- * workspace (KV pool, sliding rings, conv states, RoPE tables, activation scratch, a re-tiled copy
- * of every linear's codes and scales for the MFMA paths, and at 6 bits an fp16 copy of the layers'
+/* Sizes the caller must allocate: the exact weight-blob size this config implies (the tensor set
+ * and byte ranges of the MLX affine exports, TensorFold issue #1491 "Checkpoint handling"; 594
+ * tensors and 973,008,384 data bytes at 4-bit g64 per TensorFold PR #1508's admission commit) and
+ * the device workspace (KV pool pages allocated once within a budget, as PR #1508's pool-page
+ * commit does; sliding rings, conv states, RoPE tables, activation scratch, a re-tiled copy of
+ * every linear's codes and scales for the MFMA paths, and at 6 bits an fp16 copy of the layers'
  * dequantised linears for the prefill GEMM: 2 more bytes per weight). Host only. */
 lfm3_status lfm3_query_sizes(const lfm3_config* cfg, size_t* blob_bytes, size_t* workspace_bytes);
 
@@ -89,7 +98,9 @@ lfm3_status lfm3_query_sizes(const lfm3_config* cfg, size_t* blob_bytes, size_t*
 lfm3_status lfm3_validate_blob(const lfm3_config* cfg, const void* blob_host, size_t blob_bytes,
                                char* err, size_t err_len);
 
-/* Create a context. blob_dev holds the blob (validated by reading its header back); workspace_dev
+/* Create a context (TensorFold issue #1491, "Checkpoint handling": names, shapes, dtypes and byte
+ * ranges are admitted before any kernel runs; unsupported schemes are refused by name).
+ * blob_dev holds the blob (validated by reading its header back); workspace_dev
  * holds at least workspace_bytes from lfm3_query_sizes. hip_stream is a hipStream_t (NULL = the
  * default stream). Zeroes every slot, uploads the RoPE tables (built in float64, stored fp32) and
  * enqueues the re-tiling of the prefill GEMM weights from the blob on hip_stream (the blob must
@@ -113,7 +124,9 @@ lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
                          int32_t* argmax_last_dev, float* hidden_out_dev);
 
 /*
- * One decode step for n distinct slots (1 <= n <= min(max_slots, LFM3_MAX_BATCH)): row b appends
+ * One decode step over several streams in one launch per kernel (TensorFold PR #1508: decode rows
+ * of up to eight streams a launch, per-slot conv states, rings and pages; --parallel lanes), for
+ * n distinct slots (1 <= n <= min(max_slots, LFM3_MAX_BATCH)): row b appends
  * one position to slots_host[b]. Input: tokens_dev int32 [n] or hidden_dev bf16 [n, hidden].
  * Outputs (NULL to skip): logits_dev fp32 [n, vocab], argmax_dev int32 [n] (greedy id: ties go to
  * the lower id, NaN ranks as -inf), hidden_out_dev fp32 [n, hidden].
@@ -122,8 +135,15 @@ lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_hos
                               const int32_t* tokens_dev, const uint16_t* hidden_dev,
                               float* logits_dev, int32_t* argmax_dev, float* hidden_out_dev);
 
-/* Empty a slot: length 0, conv state zero, its pages back to the pool. */
+/* Empty a slot: length 0, conv state zero, its pages back to the pool (TensorFold issue #1491,
+ * "Validation": snapshots and reset are among the exactness cases; a reset slot must decode as a
+ * fresh one). */
 lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot);
+
+/* Synchronise the context's stream and report the device-side argument checks of the calls
+ * enqueued since the last synchronize: LFM3_ERR_ARG if a token id outside [0, vocab) reached the
+ * embedding (the flag is then cleared), LFM3_ERR_DEVICE if the stream failed, else LFM3_OK. */
+lfm3_status lfm3_synchronize(lfm3_ctx* ctx);
 
 /* Current length of a slot (positions held), or -1 for a bad slot. */
 int32_t lfm3_slot_length(const lfm3_ctx* ctx, int32_t slot);
@@ -166,6 +186,58 @@ lfm3_status lfm3_dequant_rows(lfm3_ctx* ctx, const char* name, int32_t row0, int
  */
 lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uint16_t* x_dev,
                         int32_t rows, float* y_dev);
+
+/*
+ * Kernel-level hook of one attention layer's core on caller buffers, for parity at the served
+ * shapes: the per-head q/k RMSNorm + RoPE of the rows' own queries and keys, the store of their
+ * keys and values into the caller's cache, attention over every visible key, and the sigmoid head
+ * gate, through the same launches a prefill pass or decode step makes ("LFM3-1.7B port":
+ * comparison table rows 2-4, the sliding-window mask section and "partial_rotary_factor";
+ * "TensorFold PR #1508": KV in 16-token pool pages under a per-slot page table, four query heads
+ * a KV head, decode rows of several streams in one launch).
+ *
+ *   sliding       0: a full layer (RoPE theta_full on rope_pairs_full pairs; keys j <= p; the cache
+ *                 is paged); 1: a sliding layer (theta_sliding, rope_pairs_sliding; keys with
+ *                 0 <= p - j < window; the cache is a per-slot ring).
+ *   decode        1: n_rows rows, row b appends position pos_host[b] to slot slots_host[b]
+ *                 (distinct slots, 1 <= n_rows <= min(max_slots, LFM3_MAX_BATCH)): the split-K
+ *                 decode kernel and its merge. 0: one prefill pass, n_rows consecutive positions
+ *                 from pos_host[0] of slot slots_host[0] (1 <= n_rows <= max(max_chunk, max_slots)):
+ *                 the q/k norm + RoPE + KV-store kernel, then the flash prefill kernel.
+ *   qkvg_dev      fp32 [n_rows, ld]: the raw qkvg linear output of each row, q (n_q_heads x 128) |
+ *                 k (n_kv_heads x 128) | v (n_kv_heads x 128) | g (n_q_heads), ld >= that width.
+ *   q_norm_dev, k_norm_dev   bf16 [128]: the per-head RMSNorm weights.
+ *   k_cache_dev, v_cache_dev fp16 caches, caller-owned; positions before each row's own hold the
+ *                 keys (after norm + RoPE) and values of the slot's history. Full: [n_pool_pages,
+ *                 n_kv_heads, 16, 128], position p of slot s in page page_table_dev[s * max_pages +
+ *                 p / 16], row p % 16. Sliding: [n_slots, n_kv_heads, ring_rows, 128], position p at
+ *                 ring row p % ring_rows. The call writes each row's own key and value there; it
+ *                 reads no cache row that holds no visible key (such rows may hold anything).
+ *   page_table_dev int32 [n_slots, max_pages] (full layers only; every page covering positions
+ *                 0 .. the last row's position of a used slot in [0, n_pool_pages)).
+ *   out_dev       fp16 [n_rows, n_q_heads * 128]: sigmoid(g_h) * attention output of head h.
+ * Every position must be < max_ctx (the context's RoPE tables). Sliding rings need ring_rows >=
+ * window in decode and >= window + n_rows - 1 in prefill (a pass's own keys must not overwrite
+ * keys its first row still sees); full layers need max_pages <= 8192. Split partials and the prefill's rotated queries use the
+ * context's workspace, so one call at a time per context. The full layer's page table is copied
+ * to the host and checked before anything is enqueued (this synchronises the device); any check
+ * failing returns LFM3_ERR_ARG with nothing enqueued.
+ */
+typedef struct lfm3_attn_io {
+  int32_t sliding, decode, n_rows;
+  const int32_t* slots_host;
+  const int32_t* pos_host;
+  const float* qkvg_dev;
+  int32_t ld;
+  const uint16_t* q_norm_dev;
+  const uint16_t* k_norm_dev;
+  uint16_t* k_cache_dev;
+  uint16_t* v_cache_dev;
+  const int32_t* page_table_dev;
+  int32_t max_pages, n_pool_pages, n_slots, ring_rows;
+  uint16_t* out_dev;
+} lfm3_attn_io;
+lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io);
 
 /*
  * Kernel-family timing for roofline figures. lfm3_profile(ctx, 1) starts recording: every later

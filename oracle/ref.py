@@ -179,7 +179,8 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, qpos: np.ndarray
     rep = hq // hkv
     kk = np.repeat(k, rep, axis=1)          # [T, Hq, D]
     vv = np.repeat(v, rep, axis=1)
-    scores = np.einsum("mhd,thd->hmt", q, kk) / np.sqrt(d)
+    # scores[h, m, t] = q[m, h, :] . k[t, h, :] / sqrt(D), as one batched matmul over heads
+    scores = np.matmul(q.transpose(1, 0, 2), kk.transpose(1, 2, 0)) / np.sqrt(d)
     j = np.arange(t)[None, :]
     p = np.asarray(qpos)[:, None]
     vis = j <= p
@@ -190,7 +191,8 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, qpos: np.ndarray
     e = np.exp(scores - mx)
     e = np.where(vis[None], e, 0.0)
     pr = e / e.sum(axis=2, keepdims=True)
-    return np.einsum("hmt,thd->mhd", pr, vv)
+    # o[m, h, :] = sum_t pr[h, m, t] v[t, h, :]
+    return np.matmul(pr, vv.transpose(1, 0, 2)).transpose(1, 0, 2)
 
 
 def greedy_argmax(logits: np.ndarray) -> np.ndarray:
@@ -202,6 +204,39 @@ def greedy_argmax(logits: np.ndarray) -> np.ndarray:
 def top2_margin(logits: np.ndarray) -> np.ndarray:
     x = np.sort(np.where(np.isnan(logits), -np.inf, logits), axis=-1)
     return x[..., -1] - x[..., -2]
+
+
+def attention_core(qkvg, q_norm, k_norm, k_hist, v_hist, pos, cfg, theta, n_pairs, window, gate=True,
+                   rnd=lambda x: x):
+    """The attention mixer from its qkvg linear output to the gated head outputs, for rows at
+    absolute positions ``pos`` appended after the cached keys / values ``k_hist``, ``v_hist``
+    [T0, Hkv, D] of positions 0 .. T0-1 ("LFM3-1.7B port", comparison table rows 2-4: per-head q/k
+    RMSNorm, RoPE, GQA attention, sigmoid output gate in fp32; "window_size" section for the sliding
+    mask). qkvg [M, Hq*D + 2*Hkv*D + Hq] splits into q | k | v | g. Norm first, then RoPE.
+
+    Returns (o [M, Hq*D] gated, K [T0+M, Hkv, D], V [T0+M, Hkv, D]) -- the cache after the append.
+    ``rnd`` is the storage-point rounding of the diagnostic mode (identity by default).
+    """
+    hq, hkv, d, eps = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["norm_eps"]
+    m = qkvg.shape[0]
+    q = qkvg[:, : hq * d].reshape(m, hq, d)
+    k = qkvg[:, hq * d: hq * d + hkv * d].reshape(m, hkv, d)
+    v = qkvg[:, hq * d + hkv * d: hq * d + 2 * hkv * d].reshape(m, hkv, d)
+    g = qkvg[:, hq * d + 2 * hkv * d: hq * d + 2 * hkv * d + hq]
+    q = rmsnorm(q, q_norm, eps)
+    k = rmsnorm(k, k_norm, eps)
+    ang = rope_angles(pos, theta, n_pairs, d)
+    q = rnd(rope_apply(q, ang))
+    k = rnd(rope_apply(k, ang))
+    kc = np.concatenate([k_hist, k], axis=0)
+    vc = np.concatenate([v_hist, rnd(v)], axis=0)
+    o = np.empty((m, hq, d))
+    for r0 in range(0, m, 256):
+        r1 = min(m, r0 + 256)
+        o[r0:r1] = attention_rows(q[r0:r1], kc, vc, pos[r0:r1], window)
+    if gate:
+        o = o * sigmoid(g)[:, :, None]
+    return o.reshape(m, hq * d), kc, vc
 
 
 # ----------------------------------------------------------------------------------------------
@@ -225,11 +260,18 @@ class Oracle:
     """The decoder in float64. ``controls`` plants model-level mistakes for negative tests:
     'no_gate', 'rotate_all' (full layers rotate every pair), 'no_window', 'no_conv_state'."""
 
-    def __init__(self, cfg: dict, blob: bytes, controls: tuple = (), storage_points: bool = False):
+    def __init__(self, cfg: dict, blob: bytes, controls: tuple = (), storage_points=False):
         self.cfg = cfg
         self.blob = Blob(blob)
         self.controls = set(controls)
-        self.storage = storage_points
+        # storage diagnostic: False (plain float64, the parity reference), "bf16" or "fp16" (round
+        # every storage point to that format), "fp16_pair" (fp16, with the operator-norm output
+        # carried as an fp16 pair); True means "fp16_pair"
+        if storage_points is True:
+            storage_points = "fp16_pair"
+        if storage_points not in (False, None, "bf16", "fp16", "fp16_pair"):
+            raise ValueError(f"unknown storage_points {storage_points!r}")
+        self.storage = storage_points or None
         self._w = {}
 
     # weights -------------------------------------------------------------------------------
@@ -273,16 +315,18 @@ class Oracle:
 
     def _r(self, x):
         """Storage diagnostic mode (off by default; parity is judged against plain float64): round
-        to fp16 where the GPU stores fp16 -- the matmul inputs (the ffn-norm rows, the conv's z and
-        C*y, the gated attention output, the SwiGLU product), the cached k and v, and the conv
-        state. Linear outputs and the residual stream stay wide."""
-        return f16_round(x) if self.storage else x
+        where the GPU stores a 16-bit value -- the matmul inputs (the ffn-norm rows, the conv's z
+        and C*y, the gated attention output, the SwiGLU product), the cached k and v, and the conv
+        state -- to bf16 or fp16. Linear outputs and the residual stream stay wide."""
+        if self.storage is None:
+            return x
+        return bf16_round(x) if self.storage == "bf16" else f16_round(x)
 
     def _r2(self, x):
-        """Storage diagnostic for a value the GPU carries as an fp16 pair (the operator-norm output
-        feeding in_proj and qkvg): the high part and the rounded remainder."""
-        if not self.storage:
-            return x
+        """Storage diagnostic for the operator-norm output feeding in_proj and qkvg: one rounding,
+        or in "fp16_pair" mode the high part plus its rounded remainder."""
+        if self.storage != "fp16_pair":
+            return self._r(x)
         hi = f16_round(x)
         return hi + f16_round(x - hi)
 
@@ -305,36 +349,19 @@ class Oracle:
 
     def _attn_mixer(self, i, st, u, pos, lt):
         c = self.cfg
-        hq, hkv, d = c["n_q_heads"], c["n_kv_heads"], c["head_dim"]
-        m = u.shape[0]
         qkvg = u @ self._lin(f"layers.{i}.attn.qkvg_proj").T
-        q = qkvg[:, : hq * d].reshape(m, hq, d)
-        k = qkvg[:, hq * d: hq * d + hkv * d].reshape(m, hkv, d)
-        v = qkvg[:, hq * d + hkv * d: hq * d + 2 * hkv * d].reshape(m, hkv, d)
-        g = qkvg[:, hq * d + 2 * hkv * d:]
-        eps = c["norm_eps"]
-        q = rmsnorm(q, self.blob.bf16(f"layers.{i}.attn.q_norm"), eps)
-        k = rmsnorm(k, self.blob.bf16(f"layers.{i}.attn.k_norm"), eps)
         if lt == LT_FULL:
             theta, pairs = c["rope_theta_full"], c["rope_pairs_full"]
             if "rotate_all" in self.controls:
-                pairs = d // 2
+                pairs = c["head_dim"] // 2
         else:
             theta, pairs = c["rope_theta_sliding"], c["rope_pairs_sliding"]
-        ang = rope_angles(pos, theta, pairs, d)
-        q = self._r(rope_apply(q, ang))
-        k = self._r(rope_apply(k, ang))
-        st.k[i] = np.concatenate([st.k[i], k], axis=0)
-        st.v[i] = np.concatenate([st.v[i], self._r(v)], axis=0)
         win = c["window"] if (lt == LT_SLIDING and "no_window" not in self.controls) else None
-        o = np.empty((m, hq, d))
-        for r0 in range(0, m, 256):
-            r1 = min(m, r0 + 256)
-            o[r0:r1] = attention_rows(q[r0:r1], st.k[i], st.v[i], pos[r0:r1], win)
-        if "no_gate" not in self.controls:
-            o = o * sigmoid(g)[:, :, None]
-        o = self._r(o.reshape(m, hq * d))
-        return o @ self._lin(f"layers.{i}.attn.o_proj").T
+        o, k, v = attention_core(qkvg, self.blob.bf16(f"layers.{i}.attn.q_norm"),
+                                 self.blob.bf16(f"layers.{i}.attn.k_norm"), st.k[i], st.v[i], pos, c,
+                                 theta, pairs, win, gate="no_gate" not in self.controls, rnd=self._r)
+        st.k[i], st.v[i] = k, v
+        return self._r(o) @ self._lin(f"layers.{i}.attn.o_proj").T
 
     def _ffn(self, i, h):
         c = self.cfg

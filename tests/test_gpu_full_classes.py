@@ -1,0 +1,79 @@
+"""Concurrent == solo across the decode batch classes, full LFM3-1.7B geometry at 4-bit g64
+("TensorFold PR #1508", Verification: concurrent == solo; issue #1491, Validation: concurrent
+1/2/4-stream outputs matched).
+
+A stream's decode runs on the exact-weight GEMV when its step has 1-2 rows, on the MFMA GEMM with
+fp16-rounded weights at 3-32 rows, and on the MFMA GEMM with in_proj and qkvg on the GEMV at 33-64
+rows, so its logits are not bitwise the same across classes (they are within each class). What must
+hold across classes is the stated bar: eight streams, decoded alone (B = 1), together (B = 8) and
+inside a 40-row batch (B = 40), teacher-forced on the same ids for 16 steps, give logits within
+2e-2 of the float64 oracle at every step in every class, and the same greedy id in every class at
+every step whose oracle top-2 margin is at least 4e-2.
+"""
+import numpy as np
+import pytest
+
+from attention_decoder_amd import synth
+from oracle import Oracle, greedy_argmax, top2_margin
+
+from gpu_full_common import LOGIT_TOL, MARGIN, compare_logits, dev_tokens, oracle_teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+STEPS = 16
+
+
+def test_concurrent_equals_solo_across_batch_classes():
+    import torch
+    from attention_decoder_amd.lfm3 import Engine
+    cfg = synth.full_config(bits=4, group=64, max_slots=40, max_ctx=512, max_chunk=2048)
+    blob = synth.cached_blob(cfg, seed=0)
+    eng = Engine(cfg, blob)
+    try:
+        lens = [20, 57, 83, 130, 250, 256, 300, 41]
+        prompts = [synth.prompt_tokens(600 + i, n) for i, n in enumerate(lens)]
+        prompts += [synth.prompt_tokens(650 + i, 10 + 3 * i) for i in range(32)]   # fillers for B = 40
+        forced = [synth.prompt_tokens(700 + i, STEPS) for i in range(40)]
+
+        def run(groups):
+            used = sorted({i for g in groups for i in g})
+            for i in used:
+                eng.reset(i)
+                eng.prefill(i, tokens=dev_tokens(torch, prompts[i]), logits=False, argmax=False)
+            lg = {i: [] for i in range(8)}
+            ids = {i: [] for i in range(8)}
+            for t in range(STEPS):
+                for grp in groups:
+                    o = eng.decode(list(grp), tokens=dev_tokens(torch, [forced[i][t] for i in grp]), logits=True,
+                                   argmax=True)
+                    for j, i in enumerate(grp):
+                        if i < 8:
+                            lg[i].append(o["logits"][j].cpu().numpy().astype(np.float64))
+                            ids[i].append(int(o["argmax"][j].item()))
+            torch.cuda.synchronize()
+            return {i: (np.stack(lg[i]), ids[i]) for i in range(8)}
+
+        solo = run([[i] for i in range(8)])
+        b8 = run([list(range(8))])
+        b40 = run([[7, 3, 0, 5, 1, 6, 2, 4] + list(range(8, 40))])
+        print("GPU runs done", flush=True)
+    finally:
+        eng.close()
+    orc = Oracle(cfg, blob)
+    orc.preload(16)
+    try:
+        for i in range(8):
+            ref = oracle_teacher_forced(orc, prompts[i], list(forced[i][:STEPS]))[1:]
+            margins = top2_margin(ref)
+            ref_ids = greedy_argmax(ref)
+            for name, res in (("B=1", solo), ("B=8", b8), ("B=40", b40)):
+                compare_logits(res[i][0], res[i][1], ref, f"stream {i} {name}")
+            for t in range(STEPS):
+                if margins[t] >= MARGIN:
+                    assert solo[i][1][t] == b8[i][1][t] == b40[i][1][t] == ref_ids[t], (i, t)
+            d8 = np.abs(solo[i][0] - b8[i][0]).max()
+            d40 = np.abs(solo[i][0] - b40[i][0]).max()
+            print(f"stream {i}: max|solo - B=8| {d8:.3e}, max|solo - B=40| {d40:.3e}")
+            assert d8 <= 2 * LOGIT_TOL and d40 <= 2 * LOGIT_TOL
+    finally:
+        orc.drop_cache()
