@@ -1052,7 +1052,15 @@ lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uin
   return LFM3_OK;
 }
 
-lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io) {
+}  // extern "C"
+
+namespace {
+
+// The attention-core hook. part / part_floats: where the decode split partials go (the context's
+// workspace, or the no-allocation entry point's static scratch); pt_host: a host copy of the
+// page table to check (NULL: read the device table back).
+lfm3_status attention_impl(lfm3_ctx* ctx, const lfm3_attn_io* io, float* part, size_t part_floats,
+                           const int32_t* pt_host) {
   if (!ctx || !io) { g_err = "NULL argument"; return LFM3_ERR_ARG; }
   const lfm3_config& c = ctx->cfg;
   const Layout& L = ctx->L;
@@ -1090,9 +1098,14 @@ lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io) {
     if (!io->page_table_dev || io->max_pages < 1 || io->max_pages > 8192 || io->n_pool_pages < 1)
       return ctx->fail(LFM3_ERR_ARG, "full layers need a page table, max_pages in [1, 8192] and n_pool_pages >= 1");
     if (last_pos_max / kPageTokens >= io->max_pages) return ctx->fail(LFM3_ERR_ARG, "positions past the page table row");
-    std::vector<int32_t> pt((size_t)io->n_slots * io->max_pages);
-    LFM3_TRY(hipStreamSynchronize(ctx->stream));
-    LFM3_TRY(hipMemcpy(pt.data(), io->page_table_dev, pt.size() * 4, hipMemcpyDeviceToHost));
+    std::vector<int32_t> pt_copy;
+    const int32_t* pt = pt_host;
+    if (!pt) {
+      pt_copy.resize((size_t)io->n_slots * io->max_pages);
+      LFM3_TRY(hipStreamSynchronize(ctx->stream));
+      LFM3_TRY(hipMemcpy(pt_copy.data(), io->page_table_dev, pt_copy.size() * 4, hipMemcpyDeviceToHost));
+      pt = pt_copy.data();
+    }
     for (int b = 0; b < nrow_pos; ++b) {
       const int sl = io->slots_host[b], last = decode ? io->pos_host[b] : io->pos_host[b] + n - 1;
       for (int g = 0; g <= last / kPageTokens; ++g) {
@@ -1121,14 +1134,15 @@ lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io) {
     aa.q_norm = io->q_norm_dev; aa.k_norm = io->k_norm_dev; aa.cos_t = cos_t; aa.sin_t = sin_t;
     aa.kv = kv; aa.rows = rows; aa.window = sliding ? c.window : 0;
     aa.n_q_heads = c.n_q_heads; aa.n_kv_heads = c.n_kv_heads; aa.eps = c.norm_eps;
-    aa.out = (f16_t*)io->out_dev; aa.part = ctx->at<float>(L.part);
+    aa.out = (f16_t*)io->out_dev; aa.part = part;
     int ms = 1;
     for (int b = 0; b < n; ++b) {
       const int p = rows.pos[b];
       const int lo = sliding ? std::max(0, p - (c.window - 1)) : 0;
       ms = std::max(ms, (p - lo) / attn_decode_split_keys(sliding, p - lo + 1) + 1);
     }
-    if (ms > L.max_splits) return ctx->fail(LFM3_ERR_ARG, "more decode splits than the workspace holds");
+    if ((size_t)n * c.n_q_heads * ms * kPartStride > part_floats)
+      return ctx->fail(LFM3_ERR_CAPACITY, "decode split partials exceed their buffer (" + std::to_string(part_floats) + " floats)");
     aa.max_splits = ms;
     LFM3_TRY(launch_attn_decode(ctx->stream, aa));
   } else {
@@ -1144,6 +1158,17 @@ lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io) {
     LFM3_TRY(launch_attn_prefill(ctx->stream, aa));
   }
   return LFM3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io) {
+  if (!ctx) { g_err = "NULL argument"; return LFM3_ERR_ARG; }
+  const Layout& L = ctx->L;
+  return attention_impl(ctx, io, ctx->at<float>(L.part),
+                        (size_t)ctx->cfg.max_slots * ctx->cfg.n_q_heads * L.max_splits * kPartStride, nullptr);
 }
 
 lfm3_status lfm3_profile(lfm3_ctx* ctx, int32_t enable) {
