@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -1162,6 +1163,36 @@ lfm3_status attention_impl(lfm3_ctx* ctx, const lfm3_attn_io* io, float* part, s
 
 }  // namespace
 
+// Split partials of lfm3_attention_noalloc: one file-scope device array per GPU, so that entry
+// point allocates nothing. Up to kNoAllocRows decode rows of 16 query heads with up to 65 splits
+// each (the most attn_decode_split_keys gives): 4.4 MB, held on every GPU the library runs on
+// until the process ends. Every call on a GPU shares its copy; calls that overlap on one GPU race.
+constexpr int kNoAllocRows = 8;
+constexpr size_t kNoAllocFloats = (size_t)kNoAllocRows * 16 * 65 * kPartStride;
+static __device__ __align__(256) float scratch[kNoAllocFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+float* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, looked up once per device (host code
+// must use this address, never the array's name, which is a host-side stand-in).
+lfm3_status noalloc_scratch(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) { g_err = "no usable HIP device"; return LFM3_ERR_DEVICE; }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) { g_err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e); return LFM3_ERR_DEVICE; }
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LFM3_OK;
+}
+}  // namespace
+
 extern "C" {
 
 lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io) {
@@ -1169,6 +1200,18 @@ lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io) {
   const Layout& L = ctx->L;
   return attention_impl(ctx, io, ctx->at<float>(L.part),
                         (size_t)ctx->cfg.max_slots * ctx->cfg.n_q_heads * L.max_splits * kPartStride, nullptr);
+}
+
+lfm3_status lfm3_attention_noalloc(lfm3_ctx* ctx, const lfm3_attn_io* io, const int32_t* page_table_host) {
+  if (!ctx || !io) { g_err = "NULL argument"; return LFM3_ERR_ARG; }
+  if (!io->decode) return ctx->fail(LFM3_ERR_ARG, "lfm3_attention_noalloc runs decode rows only");
+  if (io->n_rows < 1 || io->n_rows > kNoAllocRows)
+    return ctx->fail(LFM3_ERR_CAPACITY, "lfm3_attention_noalloc takes 1 .. " + std::to_string(kNoAllocRows) + " rows");
+  if (!io->sliding && !page_table_host) return ctx->fail(LFM3_ERR_ARG, "full layers need page_table_host");
+  float* part = nullptr;
+  const lfm3_status st = noalloc_scratch(&part);
+  if (st != LFM3_OK) return ctx->fail(st, g_err);
+  return attention_impl(ctx, io, part, kNoAllocFloats, io->sliding ? nullptr : page_table_host);
 }
 
 lfm3_status lfm3_profile(lfm3_ctx* ctx, int32_t enable) {

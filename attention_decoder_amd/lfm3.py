@@ -87,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lfm3_dequant_rows": (_i32, [_vp, ctypes.c_char_p, _i32, _i32, _vp, _vp]),
         "lfm3_linear": (_i32, [_vp, ctypes.c_char_p, _i32, _vp, _i32, _vp]),
         "lfm3_attention": (_i32, [_vp, P(AttnIO)]),
+        "lfm3_attention_noalloc": (_i32, [_vp, P(AttnIO), P(_i32)]),
         "lfm3_profile": (_i32, [_vp, _i32]),
         "lfm3_profile_read": (_i32, [_vp, _i32, P(ctypes.c_double), P(ctypes.c_int64), P(ctypes.c_double),
                                      P(ctypes.c_double)]),
@@ -180,8 +181,9 @@ def lfm3_linear(ctx, name: str, path: int, x, rows: int, y):
 
 
 def lfm3_attention(ctx, *, sliding, decode, slots, pos, qkvg, q_norm, k_norm, k_cache, v_cache, out,
-                   page_table=None, max_pages=0, n_pool_pages=0, n_slots=1, ring_rows=0):
-    """The attention-core hook: torch device tensors in, marshalled into lfm3_attn_io."""
+                   page_table=None, max_pages=0, n_pool_pages=0, n_slots=1, ring_rows=0, noalloc=False):
+    """The attention-core hook: torch device tensors in, marshalled into lfm3_attn_io (noalloc:
+    through lfm3_attention_noalloc, with a host copy of the page table)."""
     n = int(qkvg.shape[0])
     sl = (ctypes.c_int32 * len(slots))(*[int(v) for v in slots])
     ps = (ctypes.c_int32 * len(pos))(*[int(v) for v in pos])
@@ -189,7 +191,14 @@ def lfm3_attention(ctx, *, sliding, decode, slots, pos, qkvg, q_norm, k_norm, k_
                 k_norm.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                 None if page_table is None else page_table.data_ptr(), int(max_pages), int(n_pool_pages),
                 int(n_slots), int(ring_rows), out.data_ptr())
-    _check(load_library().lfm3_attention(ctx, ctypes.byref(io)), ctx)
+    if noalloc:
+        pth = None
+        if page_table is not None:
+            flat = [int(v) for v in page_table.cpu().reshape(-1).tolist()]
+            pth = (ctypes.c_int32 * len(flat))(*flat)
+        _check(load_library().lfm3_attention_noalloc(ctx, ctypes.byref(io), pth), ctx)
+    else:
+        _check(load_library().lfm3_attention(ctx, ctypes.byref(io)), ctx)
 
 
 PROF_KINDS = {"gemv": 0, "gemm": 1, "attn_decode": 2, "attn_prefill": 3, "conv": 4, "norm": 5, "other": 6}

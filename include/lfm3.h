@@ -240,6 +240,19 @@ typedef struct lfm3_attn_io {
 lfm3_status lfm3_attention(lfm3_ctx* ctx, const lfm3_attn_io* io);
 
 /*
+ * lfm3_attention in decode mode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * results, with the split partials in a fixed device array of the library (4.4 MB per GPU, kept
+ * until the process ends) instead of the context's workspace, and no device-to-host copy: the
+ * page table of a full layer is checked from page_table_host, a host copy of page_table_dev with
+ * the same layout (NULL for sliding layers). Takes decode rows only, 1 <= n_rows <= 8; more
+ * rows return LFM3_ERR_CAPACITY, other argument errors LFM3_ERR_ARG, with nothing enqueued. The
+ * array is shared by every call on a GPU: calls that overlap on one GPU (several contexts or
+ * streams at once) race; calls in one stream's order do not.
+ */
+lfm3_status lfm3_attention_noalloc(lfm3_ctx* ctx, const lfm3_attn_io* io, const int32_t* page_table_host);
+
+/*
  * Kernel-family timing for roofline figures. lfm3_profile(ctx, 1) starts recording: every later
  * launch is tagged with its family and the algorithmic bytes and flops it implies (weights +
  * activations read and written; 2*M*N*K for a linear; 4*128*heads per visible key for
