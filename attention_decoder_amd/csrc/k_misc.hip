@@ -235,6 +235,45 @@ hipError_t launch_qk_rope(hipStream_t s, const QkRopeArgs& a) {
   return hipGetLastError();
 }
 
+// Keys and values of positions [p0, p0 + n) of one slot between the cache (pool pages or the
+// slot's ring) and contiguous buffers kbuf / vbuf [n, n_kv, 128]: a kept state's save (dir 0,
+// cache -> buffer) and load (dir 1). Block per position; thread t < 64 moves 16-byte chunk t of
+// the key row, t >= 64 chunk t - 64 of the value row.
+__global__ void __launch_bounds__(128) k_kv_move(KvRef kv, int slot, int p0, f16_t* kbuf, f16_t* vbuf, int n_kv,
+                                                 int dir) {
+  const int i = blockIdx.x, t = threadIdx.x;
+  const int pos = p0 + i;
+  const bool is_k = t < 64;
+  const int c = (t & 63) * 8;   // element offset within the n_kv * 128 row
+  const int h = c / kHeadDim, e = c % kHeadDim;
+  f16_t* cache = kv_row(kv, is_k ? kv.k : kv.v, slot, pos, h, n_kv) + e;
+  f16_t* buf = (is_k ? kbuf : vbuf) + ((size_t)i * n_kv + h) * kHeadDim + e;
+  if (dir == 0) *(uint4*)buf = *(const uint4*)cache;
+  else *(uint4*)cache = *(const uint4*)buf;
+}
+
+hipError_t launch_kv_move(hipStream_t s, const KvRef& kv, int slot, int p0, int n, f16_t* kbuf, f16_t* vbuf, int n_kv,
+                          int dir) {
+  if (n <= 0) return hipSuccess;
+  if (n_kv * kHeadDim != 512) return hipErrorInvalidValue;   // 64 chunks of 8 per key row
+  hipLaunchKernelGGL(k_kv_move, dim3(n), dim3(128), 0, s, kv, slot, p0, kbuf, vbuf, n_kv, dir);
+  return hipGetLastError();
+}
+
+__global__ void k_copy16(uint4* dst, const uint4* src, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) dst[i] = src[i];
+}
+
+hipError_t launch_copy(hipStream_t s, void* dst, const void* src, size_t bytes) {
+  if (bytes == 0) return hipSuccess;
+  if (bytes % 16 || (uintptr_t)dst % 16 || (uintptr_t)src % 16) return hipErrorInvalidValue;
+  const size_t n = bytes / 16;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(k_copy16, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)dst, (const uint4*)src, n);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------------------------
 // gated short conv ("LFM3-1.7B port" table row 1: kernel 7, state = last 6 columns of B*x;
 // "--pad-tail": the new state is columns [n, n + 6) of [state | Bx] after n real rows).
@@ -305,7 +344,10 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
 #pragma unroll
     for (int j = 0; j < kMaxTaps - 1; ++j)
       if (j < S) y = fmaf(ker[j], z[i + j], y);
-    if (r < M) a.out[(size_t)r * H + c] = f2h_sep(cz[i] * y);
+    if (r < M) {
+      a.out[(size_t)r * H + c] = f2h_sep(cz[i] * y);
+      if (a.z_out) a.z_out[(size_t)r * H + c] = f2h(zc);
+    }
   }
   if (blockIdx.y == 0) {
     // new state: the last S entries of [state | z_0 .. z_{M-1}]; ascending j reads state[M + j]
@@ -324,6 +366,31 @@ hipError_t launch_conv(hipStream_t s, const ConvArgs& a) {
   if (a.taps > kMaxTaps || a.taps < 2 || a.hidden % 256) return hipErrorInvalidValue;
   const int rb = a.rows.mode == 1 ? a.rows.n : (a.rows.n + kConvRun - 1) / kConvRun;
   hipLaunchKernelGGL(k_conv, dim3(cb, rb), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Verify-window commit ("TensorFold PR #1508": the commit of an accepted row's conv state): block
+// (channel block, conv layer).
+__global__ void __launch_bounds__(256) k_conv_commit(f16_t* state, const f16_t* pre, const f16_t* z, int zrows,
+                                                     int accept, int hidden, int S) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int l = blockIdx.y;
+  if (c >= hidden) return;
+  const f16_t* pl = pre + (size_t)l * S * hidden;
+  const f16_t* zl = z + (size_t)l * zrows * hidden;
+  f16_t* st = state + (size_t)l * S * hidden;
+  for (int j = 0; j < S; ++j) {
+    const int w = accept + j;   // index into [pre (S columns) | z_0 .. z_{accept-1}]
+    st[(size_t)j * hidden + c] = w < S ? pl[(size_t)w * hidden + c] : zl[(size_t)(w - S) * hidden + c];
+  }
+}
+
+hipError_t launch_conv_commit(hipStream_t s, f16_t* state, const f16_t* pre, const f16_t* z, int zrows, int accept,
+                              int n_conv, int hidden, int taps) {
+  if (n_conv <= 0) return hipSuccess;
+  if (accept < 0 || accept > zrows || taps < 2 || taps > kMaxTaps) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_conv_commit, dim3((hidden + 255) / 256, n_conv), dim3(256), 0, s, state, pre, z, zrows, accept,
+                     hidden, taps - 1);
   return hipGetLastError();
 }
 

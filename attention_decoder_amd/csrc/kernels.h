@@ -72,11 +72,24 @@ struct ConvArgs {
   f16_t* state;          // this layer's state of slot 0: [taps-1, hidden]; slot stride below
   int64_t slot_stride;
   f16_t* out;            // [rows, hidden]
+  f16_t* z_out;          // nullable (prefill): every row's z = f16(B * x), [rows, hidden], for a
+                         // verify window's commit
   Rows rows;
   int hidden, taps;
 };
 hipError_t launch_conv(hipStream_t s, const ConvArgs& a);
+// Commit of a verify window's accepted rows: each conv layer's state of one slot becomes the last
+// taps - 1 columns of [pre | z_0 .. z_{accept-1}], where pre is the state before the window
+// ([n_conv, taps-1, hidden]) and z the window rows' z ([n_conv, zrows, hidden]).
+hipError_t launch_conv_commit(hipStream_t s, f16_t* state, const f16_t* pre, const f16_t* z, int zrows, int accept,
+                              int n_conv, int hidden, int taps);
 
+// Keys and values of positions [p0, p0 + n) of `slot` between the cache and contiguous fp16
+// buffers [n, n_kv, 128] (dir 0: save, cache -> buffers; 1: load, buffers -> cache). n_kv = 4.
+hipError_t launch_kv_move(hipStream_t s, const KvRef& kv, int slot, int p0, int n, f16_t* kbuf, f16_t* vbuf, int n_kv,
+                          int dir);
+// Device-to-device copy of `bytes` (16-byte multiple, 16-byte aligned) by a kernel.
+hipError_t launch_copy(hipStream_t s, void* dst, const void* src, size_t bytes);
 hipError_t launch_set_pages(hipStream_t s, int32_t* page_table, int index0, int count, const int32_t* pages);
 hipError_t launch_zero(hipStream_t s, void* p, size_t bytes);
 hipError_t launch_argmax_finalize(hipStream_t s, uint64_t* keys, int32_t* ids, int rows);

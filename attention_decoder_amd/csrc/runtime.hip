@@ -19,6 +19,8 @@ namespace {
 
 thread_local std::string g_err;
 
+constexpr int kMaxVerify = 16;   // rows of a verify window
+
 // ------------------------------------------------------------------------------------------------
 // blob format (the writer is the seeded input generator; this reader is independent)
 //   64-byte header: "LFM3BLB1", u32 version 1, u32 n_tensors, u64 table_offset, u64 data_offset,
@@ -155,6 +157,7 @@ struct Layout {
   size_t cos_f, sin_f, cos_s, sin_s;
   size_t conv_state, ring_k, ring_v, pool_k, pool_v, page_table;
   size_t h, h2, x, xlo, big, sbuf, mix, qrot, m, m2, m3, m4, xf, part, keys, flags;
+  size_t vpre, vz;   // verify windows: each slot's conv state before its window, and the window rows' z
   size_t gemm_w, gemm_w_bytes;   // re-tiled copies of every prefill GEMM weight
   size_t total;
   int max_rows, max_pages, ring_rows, max_splits, big_ld;
@@ -235,6 +238,8 @@ Layout make_layout(const lfm3_config& c) {
   L.part = take((size_t)c.max_slots * c.n_q_heads * L.max_splits * kPartStride * 4);
   L.keys = take((size_t)kMaxBatch * kArgmaxParts * 8);   // argmax partials [row][part]
   L.flags = take(256);                                     // device-side argument errors (bit 0: token id)
+  L.vpre = take((size_t)c.max_slots * L.conv_slot * 2);
+  L.vz = take((size_t)c.max_slots * n_conv * kMaxVerify * H * 2);
   L.gemm_w_bytes = 0;
   for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits, gemm_f16_copy(c));
   if (c.has_embedding) L.gemm_w_bytes += gemm_w_bytes(c.vocab, c.hidden, c.embed_bits, false);   // the tied head
@@ -273,6 +278,8 @@ struct lfm3_ctx {
   GemmW g_emb{};   // the head's re-tiled copy (decode batches of 3+ rows)
   const bf16_t* emb_norm = nullptr;
   std::vector<int> len;
+  std::vector<int> pending;   // rows of a slot's uncommitted verify window (0: none)
+  f16_t* verify_z = nullptr;  // while a verify pass runs: its slot's z rows [n_conv, kMaxVerify, H]
   std::vector<std::vector<int32_t>> pages;
   std::vector<int32_t> free_pages;
   float* capture = nullptr;
@@ -430,7 +437,8 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
   f16_t* xlo = ctx->at<f16_t>(L.xlo);
 
   // fp32 output (STORE) or fp16 SwiGLU output
-  // x_lo: the input is carried as the fp16 pair in + x_lo (two K passes; counted as such)
+  // x_lo: the input is carried as the fp16 pair in + x_lo (two K passes over the same weight tiles;
+  // the second pass is overhead, so the flops recorded stay the algorithmic 2 M N K)
   // outf2: the hidden-width outputs (mixer output projection, w2) run as two K halves, whose
   // partial sums (outf, outf2) the next residual norm adds; the narrow N would otherwise give one
   // block per CU
@@ -439,7 +447,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
     const double out_bytes = epi == GEMM_SWIGLU ? (double)M * (w.n / 2) * 2.0 : (double)M * w.n * 4.0;
     const double passes = x_lo ? 2.0 : 1.0;
     const double bytes = lin_bytes(w) + passes * M * w.k * 2.0 + out_bytes;
-    const double flops = passes * 2.0 * M * (double)w.n * w.k;
+    const double flops = 2.0 * M * (double)w.n * w.k;
     GemmArgs g{};
     g.w = w; g.x = in; g.x_lo = x_lo; g.ldx = ldin; g.m = M; g.epi = epi; g.y = outb; g.yf = outf; g.yf2 = outf2;
     g.ldy = ldout;
@@ -467,6 +475,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
       ca.state = ctx->at<f16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
       ca.slot_stride = (int64_t)L.conv_slot;
       ca.out = mix; ca.rows = rows; ca.hidden = H; ca.taps = c.conv_taps;
+      ca.z_out = ctx->verify_z ? ctx->verify_z + (size_t)lw.sub * kMaxVerify * H : nullptr;
       LFM3_TRY(timed(ctx, LFM3_PROF_CONV, (double)M * H * (12 + 2) + 2.0 * H * 2 * (c.conv_taps - 1), 0,
                      [&] { return launch_conv(s, ca); }));
     } else {
@@ -701,6 +710,51 @@ lfm3_status commit_pages(lfm3_ctx* ctx, int slot, int new_len) {
   return LFM3_OK;
 }
 
+// A kept state of a slot at `length` positions, in a caller buffer: the conv states of every conv
+// layer, the full layers' keys and values of positions [0, length) and the sliding layers' of the
+// last window - 1 positions (all the next position sees), each region 256-byte aligned.
+struct StateLayout {
+  size_t conv, full, swa, total;
+  int swa_p0, swa_n;
+  size_t row;   // bytes of one position's keys (or values): n_kv * 128 fp16
+};
+
+StateLayout state_layout(const lfm3_config& c, const Layout& L, int length) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  StateLayout s{};
+  s.row = (size_t)c.n_kv_heads * kHeadDim * 2;
+  s.swa_n = std::min(length, c.window - 1);
+  s.swa_p0 = length - s.swa_n;
+  s.conv = 0;
+  s.full = up(L.conv_slot * 2);
+  s.swa = s.full + up((size_t)n_of_type(c, LFM3_LAYER_FULL) * 2 * length * s.row);
+  s.total = s.swa + up((size_t)n_of_type(c, LFM3_LAYER_SLIDING) * 2 * s.swa_n * s.row);
+  return s;
+}
+
+// Move a slot's state between the cache and a state buffer (dir 0: save, 1: load); the slot's
+// pages for `length` positions are in its page table already.
+lfm3_status move_state(lfm3_ctx* ctx, int slot, int length, uint8_t* buf, int dir) {
+  const lfm3_config& c = ctx->cfg;
+  const Layout& L = ctx->L;
+  const StateLayout sl = state_layout(c, L, length);
+  f16_t* conv = ctx->at<f16_t>(L.conv_state) + (size_t)slot * L.conv_slot;
+  if (L.conv_slot) {
+    if (dir == 0) LFM3_TRY(launch_copy(ctx->stream, buf + sl.conv, conv, L.conv_slot * 2));
+    else LFM3_TRY(launch_copy(ctx->stream, conv, buf + sl.conv, L.conv_slot * 2));
+  }
+  for (const LayerW& lw : ctx->layers) {
+    if (lw.type == LFM3_LAYER_CONV) continue;
+    const KvRef kv = kv_for(ctx, lw);
+    const bool full = lw.type == LFM3_LAYER_FULL;
+    const int p0 = full ? 0 : sl.swa_p0, n = full ? length : sl.swa_n;
+    uint8_t* k = buf + (full ? sl.full : sl.swa) + (size_t)lw.sub * 2 * n * sl.row;
+    uint8_t* v = k + (size_t)n * sl.row;
+    LFM3_TRY(launch_kv_move(ctx->stream, kv, slot, p0, n, (f16_t*)k, (f16_t*)v, c.n_kv_heads, dir));
+  }
+  return LFM3_OK;
+}
+
 }  // namespace
 
 // ================================================================================================
@@ -839,6 +893,7 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
     }
   }
   ctx->len.assign(c.max_slots, 0);
+  ctx->pending.assign(c.max_slots, 0);
   ctx->pages.assign(c.max_slots, {});
   for (int p = c.n_pages - 1; p >= 0; --p) ctx->free_pages.push_back(p);
 
@@ -888,6 +943,7 @@ lfm3_status lfm3_prefill(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev,
   if ((tokens_dev == nullptr) == (hidden_dev == nullptr)) return ctx->fail(LFM3_ERR_ARG, "pass exactly one of tokens and hidden");
   if (tokens_dev && !c.has_embedding) return ctx->fail(LFM3_ERR_ARG, "token input needs has_embedding = 1");
   if ((logits_last_dev || argmax_last_dev) && !c.has_embedding) return ctx->fail(LFM3_ERR_ARG, "logits need the tied head (has_embedding = 1)");
+  if (ctx->pending[slot]) return ctx->fail(LFM3_ERR_ARG, "slot " + std::to_string(slot) + " has an uncommitted verify window");
   if ((int64_t)ctx->len[slot] + n_rows > c.max_ctx)
     return ctx->fail(LFM3_ERR_CAPACITY, "slot length " + std::to_string(ctx->len[slot]) + " + rows " + std::to_string(n_rows) + " > max_ctx");
   if (ctx->capture && n_rows > ctx->capture_rows) return ctx->fail(LFM3_ERR_CAPACITY, "capture buffer holds fewer rows than this call");
@@ -937,6 +993,7 @@ lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_hos
     const int sl = slots_host[b];
     if (sl < 0 || sl >= c.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(sl) + " outside [0, max_slots)");
     if (seen[sl]) return ctx->fail(LFM3_ERR_ARG, "slot " + std::to_string(sl) + " appears twice in one step");
+    if (ctx->pending[sl]) return ctx->fail(LFM3_ERR_ARG, "slot " + std::to_string(sl) + " has an uncommitted verify window");
     seen[sl] = 1;
     if (ctx->len[sl] + 1 > c.max_ctx) return ctx->fail(LFM3_ERR_CAPACITY, "slot " + std::to_string(sl) + " is at max_ctx");
     if (!reserve_pages(ctx, sl, ctx->len[sl] + 1, writes, budget)) return ctx->fail(LFM3_ERR_CAPACITY, "KV page pool exhausted");
@@ -963,6 +1020,120 @@ lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_hos
   return LFM3_OK;
 }
 
+lfm3_status lfm3_state_bytes(const lfm3_ctx* ctx, int32_t length, size_t* bytes) {
+  if (!ctx || !bytes) { g_err = "NULL argument"; return LFM3_ERR_ARG; }
+  if (length < 0 || length > ctx->cfg.max_ctx) { g_err = "length outside [0, max_ctx]"; return LFM3_ERR_ARG; }
+  *bytes = state_layout(ctx->cfg, ctx->L, length).total;
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_save_state(lfm3_ctx* ctx, int32_t slot, void* dst_dev, size_t dst_bytes, int32_t* length_out) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  if (slot < 0 || slot >= ctx->cfg.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
+  if (!dst_dev || (uintptr_t)dst_dev % 256) return ctx->fail(LFM3_ERR_ARG, "dst_dev must be a 256-byte-aligned device pointer");
+  if (ctx->pending[slot]) return ctx->fail(LFM3_ERR_ARG, "slot " + std::to_string(slot) + " has an uncommitted verify window");
+  const int length = ctx->len[slot];
+  const size_t need = state_layout(ctx->cfg, ctx->L, length).total;
+  if (dst_bytes < need) return ctx->fail(LFM3_ERR_CAPACITY, "state buffer " + std::to_string(dst_bytes) + " B < " + std::to_string(need) + " B");
+  lfm3_status st = move_state(ctx, slot, length, (uint8_t*)dst_dev, 0);
+  if (st != LFM3_OK) return st;
+  if (length_out) *length_out = length;
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_load_state(lfm3_ctx* ctx, int32_t slot, const void* src_dev, size_t src_bytes, int32_t length) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  const lfm3_config& c = ctx->cfg;
+  if (slot < 0 || slot >= c.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
+  if (!src_dev || (uintptr_t)src_dev % 256) return ctx->fail(LFM3_ERR_ARG, "src_dev must be a 256-byte-aligned device pointer");
+  if (length < 0 || length > c.max_ctx) return ctx->fail(LFM3_ERR_CAPACITY, "length outside [0, max_ctx]");
+  const size_t need = state_layout(c, ctx->L, length).total;
+  if (src_bytes < need) return ctx->fail(LFM3_ERR_ARG, "state buffer " + std::to_string(src_bytes) + " B < " + std::to_string(need) + " B");
+  if (n_of_type(c, LFM3_LAYER_FULL) > 0) {
+    const int need_pages = (length + kPageTokens - 1) / kPageTokens;
+    if (need_pages > (int)ctx->free_pages.size() + (int)ctx->pages[slot].size())
+      return ctx->fail(LFM3_ERR_CAPACITY, "KV page pool exhausted");
+  }
+  // empty the slot, lease pages for `length` positions, then copy the state in
+  for (auto it = ctx->pages[slot].rbegin(); it != ctx->pages[slot].rend(); ++it) ctx->free_pages.push_back(*it);
+  ctx->pages[slot].clear();
+  ctx->len[slot] = 0;
+  ctx->pending[slot] = 0;
+  lfm3_status st = commit_pages(ctx, slot, length);
+  if (st != LFM3_OK) return st;
+  st = move_state(ctx, slot, length, (uint8_t*)const_cast<void*>(src_dev), 1);
+  if (st != LFM3_OK) return st;
+  ctx->len[slot] = length;
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_verify(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev, int32_t n_rows, float* logits_dev,
+                        int32_t* argmax_dev) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  const lfm3_config& c = ctx->cfg;
+  if (slot < 0 || slot >= c.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
+  if (!c.has_embedding) return ctx->fail(LFM3_ERR_ARG, "verify windows need the embedding and tied head");
+  if (!tokens_dev || (!logits_dev && !argmax_dev)) return ctx->fail(LFM3_ERR_ARG, "tokens and an output are required");
+  if (n_rows < 1 || n_rows > std::min(kMaxVerify, c.max_chunk))
+    return ctx->fail(LFM3_ERR_ARG, "verify rows outside [1, min(16, max_chunk)]");
+  if (ctx->pending[slot]) return ctx->fail(LFM3_ERR_ARG, "slot " + std::to_string(slot) + " has an uncommitted verify window");
+  if (ctx->capture) return ctx->fail(LFM3_ERR_ARG, "layer capture is not available in a verify pass");
+  if ((int64_t)ctx->len[slot] + n_rows > c.max_ctx) return ctx->fail(LFM3_ERR_CAPACITY, "window runs past max_ctx");
+  std::vector<std::pair<int, int>> writes;
+  int budget = (int)ctx->free_pages.size();
+  if (!reserve_pages(ctx, slot, ctx->len[slot] + n_rows, writes, budget)) return ctx->fail(LFM3_ERR_CAPACITY, "KV page pool exhausted");
+  lfm3_status st = commit_pages(ctx, slot, ctx->len[slot] + n_rows);
+  if (st != LFM3_OK) return st;
+  const Layout& L = ctx->L;
+  const int n_conv = n_of_type(c, LFM3_LAYER_CONV);
+  if (L.conv_slot)
+    LFM3_TRY(launch_copy(ctx->stream, ctx->at<f16_t>(L.vpre) + (size_t)slot * L.conv_slot,
+                         ctx->at<f16_t>(L.conv_state) + (size_t)slot * L.conv_slot, L.conv_slot * 2));
+  LFM3_TRY(timed(ctx, LFM3_PROF_OTHER, (double)n_rows * (lin_bytes(ctx->emb) / ctx->emb.n + 4.0 * c.hidden), 0, [&] {
+    return launch_embed(ctx->stream, ctx->emb, tokens_dev, n_rows, ctx->at<float>(L.h), ctx->at<uint32_t>(L.flags));
+  }));
+  Rows rows{};
+  rows.n = n_rows; rows.mode = 0; rows.slot0 = slot; rows.pos0 = ctx->len[slot];
+  ctx->verify_z = ctx->at<f16_t>(L.vz) + (size_t)slot * n_conv * kMaxVerify * c.hidden;
+  st = run_layers(ctx, rows, 0, nullptr);
+  ctx->verify_z = nullptr;
+  if (st != LFM3_OK) return st;
+  st = head(ctx, ctx->at<f16_t>(L.xf), n_rows, logits_dev, argmax_dev);
+  if (st != LFM3_OK) return st;
+  ctx->len[slot] += n_rows;
+  ctx->pending[slot] = n_rows;
+  LFM3_TRY(prof_close(ctx));
+  return LFM3_OK;
+}
+
+lfm3_status lfm3_commit(lfm3_ctx* ctx, int32_t slot, int32_t n_accept) {
+  if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
+  const lfm3_config& c = ctx->cfg;
+  if (slot < 0 || slot >= c.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
+  const int n = ctx->pending[slot];
+  if (n == 0) return ctx->fail(LFM3_ERR_ARG, "slot " + std::to_string(slot) + " has no verify window to commit");
+  if (n_accept < 0 || n_accept > n) return ctx->fail(LFM3_ERR_ARG, "n_accept outside [0, window rows]");
+  const Layout& L = ctx->L;
+  const int n_conv = n_of_type(c, LFM3_LAYER_CONV);
+  if (n_accept < n)
+    LFM3_TRY(launch_conv_commit(ctx->stream, ctx->at<f16_t>(L.conv_state) + (size_t)slot * L.conv_slot,
+                                ctx->at<f16_t>(L.vpre) + (size_t)slot * L.conv_slot,
+                                ctx->at<f16_t>(L.vz) + (size_t)slot * n_conv * kMaxVerify * c.hidden, kMaxVerify,
+                                n_accept, n_conv, c.hidden, c.conv_taps));
+  const int len = ctx->len[slot] - n + n_accept;
+  ctx->len[slot] = len;
+  ctx->pending[slot] = 0;
+  // pages past the accepted rows go back to the pool (their stale rows are never read: a later
+  // position's key and value are written before any query sees them)
+  auto& pg = ctx->pages[slot];
+  const int keep = n_of_type(c, LFM3_LAYER_FULL) ? (len + kPageTokens - 1) / kPageTokens : 0;
+  while ((int)pg.size() > keep) {
+    ctx->free_pages.push_back(pg.back());
+    pg.pop_back();
+  }
+  return LFM3_OK;
+}
+
 lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot) {
   if (!ctx) { g_err = "ctx is NULL"; return LFM3_ERR_ARG; }
   if (slot < 0 || slot >= ctx->cfg.max_slots) return ctx->fail(LFM3_ERR_SLOT, "slot " + std::to_string(slot) + " outside [0, max_slots)");
@@ -971,6 +1142,7 @@ lfm3_status lfm3_reset_slot(lfm3_ctx* ctx, int32_t slot) {
   for (auto it = ctx->pages[slot].rbegin(); it != ctx->pages[slot].rend(); ++it) ctx->free_pages.push_back(*it);
   ctx->pages[slot].clear();
   ctx->len[slot] = 0;
+  ctx->pending[slot] = 0;
   return LFM3_OK;
 }
 

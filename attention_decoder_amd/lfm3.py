@@ -80,6 +80,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lfm3_decode_batch": (_i32, [_vp, _i32, P(_i32), _vp, _vp, _vp, _vp, _vp]),
         "lfm3_reset_slot": (_i32, [_vp, _i32]),
         "lfm3_synchronize": (_i32, [_vp]),
+        "lfm3_state_bytes": (_i32, [_vp, _i32, P(_sz)]),
+        "lfm3_verify": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp]),
+        "lfm3_commit": (_i32, [_vp, _i32, _i32]),
+        "lfm3_save_state": (_i32, [_vp, _i32, _vp, _sz, P(_i32)]),
+        "lfm3_load_state": (_i32, [_vp, _i32, _vp, _sz, _i32]),
         "lfm3_slot_length": (_i32, [_vp, _i32]),
         "lfm3_free_pages": (_i32, [_vp]),
         "lfm3_last_error": (ctypes.c_char_p, [_vp]),
@@ -154,6 +159,31 @@ def lfm3_reset_slot(ctx, slot):
 
 def lfm3_synchronize(ctx):
     _check(load_library().lfm3_synchronize(ctx), ctx)
+
+
+def lfm3_verify(ctx, slot, tokens, n_rows, logits, argmax):
+    _check(load_library().lfm3_verify(ctx, slot, _ptr(tokens), n_rows, _ptr(logits), _ptr(argmax)), ctx)
+
+
+def lfm3_commit(ctx, slot, n_accept):
+    _check(load_library().lfm3_commit(ctx, slot, n_accept), ctx)
+
+
+def lfm3_state_bytes(ctx, length) -> int:
+    b = _sz()
+    _check(load_library().lfm3_state_bytes(ctx, length, ctypes.byref(b)), ctx)
+    return b.value
+
+
+def lfm3_save_state(ctx, slot, buf) -> int:
+    n = _i32()
+    _check(load_library().lfm3_save_state(ctx, slot, _ptr(buf), buf.numel() * buf.element_size(), ctypes.byref(n)),
+           ctx)
+    return n.value
+
+
+def lfm3_load_state(ctx, slot, buf, length):
+    _check(load_library().lfm3_load_state(ctx, slot, _ptr(buf), buf.numel() * buf.element_size(), length), ctx)
 
 
 def lfm3_slot_length(ctx, slot) -> int:
@@ -280,6 +310,27 @@ class Engine:
 
     def synchronize(self):
         lfm3_synchronize(self.ctx)
+
+    def verify(self, slot, tokens):
+        """A verify window of len(tokens) rows on `slot`: (logits [n, vocab], argmax [n])."""
+        n = int(tokens.shape[0])
+        lg = self._empty((n, self.cfg["vocab"]), self.torch.float32)
+        am = self._empty((n,), self.torch.int32)
+        lfm3_verify(self.ctx, slot, tokens, n, lg, am)
+        return lg, am
+
+    def commit(self, slot, n_accept):
+        lfm3_commit(self.ctx, slot, n_accept)
+
+    def save_state(self, slot, buf=None):
+        """Kept state of `slot` into buf (a new uint8 device tensor if None): (buf, length)."""
+        n = self.length(slot)
+        if buf is None:
+            buf = self.torch.empty(lfm3_state_bytes(self.ctx, n), dtype=self.torch.uint8, device=self.device)
+        return buf, lfm3_save_state(self.ctx, slot, buf)
+
+    def load_state(self, slot, buf, length):
+        lfm3_load_state(self.ctx, slot, buf, length)
 
     def length(self, slot):
         return lfm3_slot_length(self.ctx, slot)

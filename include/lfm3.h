@@ -135,6 +135,45 @@ lfm3_status lfm3_decode_batch(lfm3_ctx* ctx, int32_t n, const int32_t* slots_hos
                               const int32_t* tokens_dev, const uint16_t* hidden_dev,
                               float* logits_dev, int32_t* argmax_dev, float* hidden_out_dev);
 
+/*
+ * Drafted decoding with verify windows ("TensorFold PR #1508": each stream leases one verify window;
+ * the short conv runs over each stream's state with every window row's snapshot, and an accepted
+ * row's conv state is committed; checked drafted == plain; TensorFold issue #1491, "Validation":
+ * partial acceptance). lfm3_verify appends n_rows positions (1 <= n_rows <= min(16, max_chunk)) to
+ * `slot` in one prefill pass and returns every row's logits fp32 [n_rows, vocab] and greedy id
+ * int32 [n_rows] (either may be NULL, not both): row i scores the token after tokens_dev[i]. The
+ * slot then holds an uncommitted window, and until lfm3_commit (or a reset / state load) no other
+ * call takes it (LFM3_ERR_ARG). lfm3_commit keeps the first n_accept rows (0 <= n_accept <= n_rows):
+ * the slot's length becomes its length before the window + n_accept, its conv states those after
+ * row n_accept - 1, and pages past the kept positions go back to the pool. Keys and values of
+ * dropped rows stay in the cache but are never read: the next position's are written before any
+ * query sees them. Needs has_embedding.
+ */
+lfm3_status lfm3_verify(lfm3_ctx* ctx, int32_t slot, const int32_t* tokens_dev, int32_t n_rows, float* logits_dev,
+                        int32_t* argmax_dev);
+lfm3_status lfm3_commit(lfm3_ctx* ctx, int32_t slot, int32_t n_accept);
+
+/*
+ * Kept states ("TensorFold PR #1508": a state at `at` is the slot's conv states and its keys and
+ * values at positions [0, at), kept in memory allocated once inside the prompt-cache budget so a
+ * keep or a restore allocates nothing, and checked resumed == fresh; "LFM3-1.7B port", the
+ * checkpoint and rewind paragraph: the conv state must be restored too, else the logits move).
+ * A state of a slot holding L positions is: the conv states of every conv layer, the full layers'
+ * keys and values of positions [0, L), and the sliding layers' keys and values of the last
+ * window - 1 positions (all that the next position sees); its size is a function of L alone.
+ * The caller owns the buffer (device memory, 256-byte aligned) and keeps the length.
+ */
+/* Bytes of a state at `length` positions (0 <= length <= max_ctx). Host only. */
+lfm3_status lfm3_state_bytes(const lfm3_ctx* ctx, int32_t length, size_t* bytes);
+/* Enqueue a copy of `slot`'s state at its current length into dst_dev (>= lfm3_state_bytes of
+ * that length); *length_out (nullable) receives the length. The slot is unchanged. */
+lfm3_status lfm3_save_state(lfm3_ctx* ctx, int32_t slot, void* dst_dev, size_t dst_bytes, int32_t* length_out);
+/* Make `slot` hold the state in src_dev saved at `length` positions (from any slot of a context of
+ * the same geometry): the slot is emptied, pages for `length` positions are leased from the pool
+ * (LFM3_ERR_CAPACITY, with nothing changed, if they are not there), the state is copied in and the
+ * slot's length set. The next prefill or decode of the slot continues from it. */
+lfm3_status lfm3_load_state(lfm3_ctx* ctx, int32_t slot, const void* src_dev, size_t src_bytes, int32_t length);
+
 /* Empty a slot: length 0, conv state zero, its pages back to the pool (TensorFold issue #1491,
  * "Validation": snapshots and reset are among the exactness cases; a reset slot must decode as a
  * fresh one). */
