@@ -63,10 +63,15 @@ def default_layer_types(n_layers: int = 24) -> list[int]:
     return out
 
 
+FFN_AS_LINEARS, FFN_NVFP4, FFN_FP8B = 0, 1, 2
+
+
 def make_config(*, layer_types, bits=4, group=64, embed_bits=None, embed_group=None,
                 has_embedding=1, max_slots=1, max_ctx=4096, max_chunk=2048, n_pages=None,
-                page_tokens=16):
-    """A complete config dict. Every field the library takes is explicit here."""
+                page_tokens=16, ffn_format=FFN_AS_LINEARS):
+    """A complete config dict. Every field the library takes is explicit here. bits = 16 stores
+    the mixers' linears (and, with embed_bits = 16, the embedding / head) as bf16; ffn_format
+    stores w13 and w2 as NVFP4 or block-FP8 instead of the mixers' format."""
     if embed_bits is None:
         embed_bits = bits
     if embed_group is None:
@@ -79,7 +84,7 @@ def make_config(*, layer_types, bits=4, group=64, embed_bits=None, embed_group=N
         rope_theta_full=1.0e6, rope_theta_sliding=1.0e4, rope_pairs_full=32, rope_pairs_sliding=64,
         norm_eps=1e-5, bits=bits, group=group, embed_bits=embed_bits, embed_group=embed_group,
         has_embedding=has_embedding, max_slots=max_slots, max_ctx=max_ctx, page_tokens=page_tokens,
-        max_chunk=max_chunk, n_pages=n_pages,
+        max_chunk=max_chunk, n_pages=n_pages, ffn_format=ffn_format,
     )
 
 
@@ -93,6 +98,14 @@ def slice3_config(**kw):
 def full_config(bits=4, group=64, **kw):
     """The full 24-layer LFM3-1.7B geometry."""
     return make_config(layer_types=default_layer_types(24), bits=bits, group=group, **kw)
+
+
+def nvfp4_config(**kw):
+    """The layout of the NVFP4 export ("TensorFold PR #1508"): FFN w1 | w3 and w2 in NVFP4, every
+    mixer projection, the embedding and the tied head in bf16."""
+    kw.setdefault("embed_bits", 16)
+    kw.setdefault("embed_group", 0)
+    return full_config(bits=16, group=0, ffn_format=FFN_NVFP4, **kw)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -114,15 +127,29 @@ def linear_shapes(cfg, lt):
     return out
 
 
-def tensor_plan(cfg):
-    """Ordered list of (name, kind, shape, bits, group); kind in {"lin", "bf16"}.
+def linear_kind(cfg, name):
+    """Storage of linear `name`: "lin" (MLX affine), "bf16lin", "nvfp4" or "fp8b"."""
+    if name == "embedding":
+        return "bf16lin" if cfg["embed_bits"] == 16 else "lin"
+    ff = cfg.get("ffn_format", FFN_AS_LINEARS)
+    if ".ffn." in name and ff:
+        return {FFN_NVFP4: "nvfp4", FFN_FP8B: "fp8b"}[ff]
+    return "bf16lin" if cfg["bits"] == 16 else "lin"
 
-    For "lin" the shape is the logical [N, K]; the blob stores .q/.scales/.biases.
+
+def tensor_plan(cfg):
+    """Ordered list of (name, kind, shape, bits, group); kind in {"lin", "bf16lin", "nvfp4",
+    "fp8b", "bf16"}.
+
+    For linears the shape is the logical [N, K]. The blob stores "lin" as .q/.scales/.biases,
+    "bf16lin" as .weight (bf16), "nvfp4" as .fp4 (codes [N, K/2]), .block_scales (e4m3 bytes
+    [N, K/16]), .tensor_scale and .input_scale (fp32 [1]), "fp8b" as .fp8 (e4m3 bytes [N, K]) and
+    .block_scales (fp32 [ceil(N/128), ceil(K/128)]).
     """
     H, D = cfg["hidden"], cfg["head_dim"]
     plan = []
     if cfg["has_embedding"]:
-        plan.append(("embedding", "lin", (cfg["vocab"], H), cfg["embed_bits"], cfg["embed_group"]))
+        plan.append(("embedding", linear_kind(cfg, "embedding"), (cfg["vocab"], H), cfg["embed_bits"], cfg["embed_group"]))
     for i, lt in enumerate(cfg["layer_type"]):
         p = f"layers.{i}."
         for nm in ("operator_norm", "post_operator_norm", "ffn_norm", "post_ffn_norm"):
@@ -133,7 +160,7 @@ def tensor_plan(cfg):
             plan.append((p + "attn.q_norm", "bf16", (D,), 0, 0))
             plan.append((p + "attn.k_norm", "bf16", (D,), 0, 0))
         for nm, n, k in linear_shapes(cfg, lt):
-            plan.append((p + nm, "lin", (n, k), cfg["bits"], cfg["group"]))
+            plan.append((p + nm, linear_kind(cfg, p + nm), (n, k), cfg["bits"], cfg["group"]))
     plan.append(("embedding_norm", "bf16", (H,), 0, 0))
     return plan
 
@@ -209,12 +236,68 @@ def _rng(seed: int, idx: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, idx])))
 
 
+_E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def _e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3 bytes, round to nearest (torch's float8_e4m3fn conversion), clamped to 448."""
+    import torch
+    t = torch.from_numpy(np.clip(np.asarray(x, dtype=np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_decode(b: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def quantize_nvfp4(w: np.ndarray):
+    """w [N, K] float32 -> (packed e2m1 [N, K/2], e4m3 scale bytes [N, K/16], tensor scale, input
+    scale). Tensor scale = amax / (6 * 448); a group's scale = e4m3(group amax / (6 * tensor
+    scale)); a code is the nearest e2m1 value of w / (scale * tensor scale)."""
+    n, k = w.shape
+    ts = np.float32(max(float(np.abs(w).max()), 1e-30) / (6.0 * 448.0))
+    g = w.reshape(n, k // 16, 16)
+    sb = _e4m3_bits(np.abs(g).max(axis=2) / (np.float32(6.0) * ts))
+    eff = _e4m3_decode(sb).astype(np.float32) * ts
+    r = g / np.where(eff == 0, np.float32(1.0), eff)[:, :, None]
+    mag = np.abs(r)
+    idx = np.abs(mag[..., None] - _E2M1_MAGS).argmin(axis=-1)
+    codes = (idx + np.where(r < 0, 8, 0)).astype(np.uint8).reshape(n, k)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sb, ts, np.float32(1.0)
+
+
+def quantize_fp8_block(w: np.ndarray, block: int = 128):
+    """w [N, K] float32 -> (e4m3 bytes [N, K], fp32 scales [ceil(N/128), ceil(K/128)]): per block
+    scale = amax / 448, code = e4m3(w / scale)."""
+    n, k = w.shape
+    nb, kb = -(-n // block), -(-k // block)
+    sc = np.zeros((nb, kb), dtype=np.float32)
+    for i in range(nb):
+        for j in range(kb):
+            a = float(np.abs(w[i * block:(i + 1) * block, j * block:(j + 1) * block]).max())
+            sc[i, j] = a / 448.0 if a > 0 else 1.0
+    full = np.repeat(np.repeat(sc, block, axis=0)[:n], block, axis=1)[:, :k]
+    return _e4m3_bits(w / full), sc
+
+
 def _gen_tensor(args):
     idx, (name, kind, shape, bits, group), seed = args
     rng = _rng(seed, idx)
-    if kind == "lin":
+    if kind in ("lin", "bf16lin", "nvfp4", "fp8b"):
         n, k = shape
         w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+        if kind == "bf16lin":
+            return [(name + ".weight", DT_BF16, f32_to_bf16_bits(w))]
+        if kind == "nvfp4":
+            packed, sb, ts, ins = quantize_nvfp4(w)
+            return [(name + ".fp4", DT_CODES, packed), (name + ".block_scales", DT_CODES, sb),
+                    (name + ".tensor_scale", DT_F32, np.array([ts], dtype=np.float32)),
+                    (name + ".input_scale", DT_F32, np.array([ins], dtype=np.float32))]
+        if kind == "fp8b":
+            codes, sc = quantize_fp8_block(w)
+            return [(name + ".fp8", DT_CODES, codes), (name + ".block_scales", DT_F32, sc)]
         q, s, b = quantize_affine(w, bits, group)
         return [(name + ".q", DT_CODES, pack_codes(q, bits)), (name + ".scales", DT_BF16, s),
                 (name + ".biases", DT_BF16, b)]
@@ -258,7 +341,10 @@ def build_blob(cfg, seed: int = 0, threads: int | None = None) -> bytes:
 def geometry_key(cfg) -> str:
     keys = ["n_layers", "hidden", "ffn", "n_q_heads", "n_kv_heads", "head_dim", "vocab", "conv_taps",
             "layer_type", "bits", "group", "embed_bits", "embed_group", "has_embedding"]
-    return hashlib.sha1(json.dumps({k: cfg[k] for k in keys}, sort_keys=True).encode()).hexdigest()[:16]
+    d = {k: cfg[k] for k in keys}
+    if cfg.get("ffn_format", FFN_AS_LINEARS):
+        d["ffn_format"] = cfg["ffn_format"]
+    return hashlib.sha1(json.dumps(d, sort_keys=True).encode()).hexdigest()[:16]
 
 
 def cached_blob(cfg, seed: int = 0, cache_dir: str | None = None) -> bytes:

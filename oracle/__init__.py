@@ -16,5 +16,6 @@ Parity status of each part is listed in ``oracle/ref.py``'s module docstring.
 """
 from .ref import (  # noqa: F401
     Blob, Oracle, SlotState, dequant, unpack_codes, rmsnorm, rope_angles, rope_apply, silu, sigmoid,
-    attention_rows, attention_core, conv_step, greedy_argmax, bf16_round, f16_round, top2_margin,
+    attention_rows, attention_core, conv_step, e2m1_values, e4m3_values, dequant_nvfp4,
+    dequant_fp8_block, load_weight, greedy_argmax, bf16_round, f16_round, top2_margin,
 )

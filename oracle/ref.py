@@ -66,6 +66,12 @@ class Blob:
         dt, shape, off, nb = self.entries[name]
         return dt, shape, np.frombuffer(self.data[off:off + nb], dtype=np.uint8)
 
+    def f32(self, name) -> np.ndarray:
+        """An fp32 tensor as float64 values."""
+        dt, shape, b = self.raw(name)
+        assert dt == 2
+        return b.view(np.float32).astype(np.float64).reshape(shape)
+
     def bf16(self, name) -> np.ndarray:
         """A bf16 tensor as exact float64 values."""
         dt, shape, b = self.raw(name)
@@ -89,6 +95,66 @@ def dequant(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray, group: in
     s = np.repeat(scales, group, axis=1)
     b = np.repeat(biases, group, axis=1)
     return codes.astype(np.float64) * s + b
+
+
+def e2m1_values(codes: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes (0..15) -> float64: bit 3 sign, bits 2..1 exponent with bias 1, bit 0
+    mantissa; exponent 0 is subnormal (0 or 0.5). The element format of NVFP4 ("TensorFold PR
+    #1508": the FFN's e2m1 codes)."""
+    c = np.asarray(codes).astype(np.int64)
+    s, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(s == 1, -mag, mag)
+
+
+def e4m3_values(codes: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 (the finite variant) bytes -> float64: bit 7 sign, bits 6..3 exponent with bias 7,
+    bits 2..0 mantissa; exponent 0 is subnormal (m * 2^-9); 0x7F and 0xFF are NaN. NVFP4's block
+    scales ("TensorFold PR #1508": e4m3 block scales) and block-FP8 weights are in it."""
+    c = np.asarray(codes).astype(np.int64)
+    s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def dequant_nvfp4(packed: np.ndarray, block_scales: np.ndarray, tensor_scale: float) -> np.ndarray:
+    """NVFP4 weight [N, K] from packed e2m1 codes [N, K/2] (two a byte, element 2i in the low
+    nibble), e4m3 scales [N, K/16] (one per 16 consecutive k) and the fp32 tensor scale:
+    w = e2m1(code) * e4m3(scale) * tensor_scale, exactly in float64 ("TensorFold PR #1508": e2m1
+    codes in groups of 16 with e4m3 block scales and an fp32 tensor scale)."""
+    n = packed.shape[0]
+    codes = np.empty((n, packed.shape[1] * 2), dtype=np.int64)
+    codes[:, 0::2] = packed & 0x0F
+    codes[:, 1::2] = packed >> 4
+    sc = np.repeat(e4m3_values(block_scales), 16, axis=1)
+    return e2m1_values(codes) * sc * float(tensor_scale)
+
+
+def dequant_fp8_block(codes: np.ndarray, block_scales: np.ndarray, block: int = 128) -> np.ndarray:
+    """Block-FP8 weight [N, K]: e4m3 codes times one fp32 scale per block x block tile of the
+    weight (scales [ceil(N/block), ceil(K/block)]), exactly in float64."""
+    n, k = codes.shape
+    sc = np.repeat(np.repeat(block_scales, block, axis=0)[:n], block, axis=1)[:, :k]
+    return e4m3_values(codes) * sc
+
+
+def load_weight(blob: Blob, name: str, fmt: str, bits: int = 0, group: int = 0) -> np.ndarray:
+    """Float64 weight [N, K] of linear `name` in storage format `fmt`: "affine" (MLX codes with bf16
+    scale and bias), "bf16" (stored bf16 values), "nvfp4" or "fp8b" (block-FP8, 128 x 128)."""
+    if fmt == "affine":
+        return load_linear(blob, name, bits, group)
+    if fmt == "bf16":
+        return blob.bf16(name + ".weight")
+    if fmt == "nvfp4":
+        _, shape, q = blob.raw(name + ".fp4")
+        _, sshape, sb = blob.raw(name + ".block_scales")
+        ts = float(blob.f32(name + ".tensor_scale")[0])
+        return dequant_nvfp4(q.reshape(shape), sb.reshape(sshape), ts)
+    if fmt == "fp8b":
+        _, shape, q = blob.raw(name + ".fp8")
+        return dequant_fp8_block(q.reshape(shape), blob.f32(name + ".block_scales"))
+    raise ValueError(f"unknown weight format {fmt}")
 
 
 def load_linear(blob: Blob, name: str, bits: int, group: int, row_chunk: int = 8192) -> np.ndarray:
@@ -275,31 +341,45 @@ class Oracle:
         self._w = {}
 
     # weights -------------------------------------------------------------------------------
+    def fmt_of(self, name: str):
+        """(format, bits, group) of linear `name` under the config: the embedding follows
+        embed_bits / embed_group, the FFN (w13, w2) ffn_format, the mixers bits / group; 16 bits
+        means stored bf16 ("TensorFold PR #1508": the NVFP4 export keeps the mixers, embedding and
+        tied head in bf16 and only the FFN in fp4)."""
+        c = self.cfg
+        if name == "embedding":
+            return ("bf16", 16, 0) if c["embed_bits"] == 16 else ("affine", c["embed_bits"], c["embed_group"])
+        ff = c.get("ffn_format", 0)
+        if ".ffn." in name and ff:
+            return ({1: "nvfp4", 2: "fp8b"}[ff], 0, 0)
+        return ("bf16", 16, 0) if c["bits"] == 16 else ("affine", c["bits"], c["group"])
+
     def _lin(self, name, bits=None, group=None):
-        key = name
-        if key not in self._w:
-            c = self.cfg
-            self._w[key] = load_linear(self.blob, name, bits or c["bits"], group or c["group"])
-        return self._w[key]
+        if name not in self._w:
+            fmt, b, g = self.fmt_of(name)
+            self._w[name] = load_weight(self.blob, name, fmt, b, g)
+        return self._w[name]
 
     def embedding(self):
-        return self._lin("embedding", self.cfg["embed_bits"], self.cfg["embed_group"])
+        return self._lin("embedding")
 
     def drop_cache(self):
         self._w.clear()
 
     def preload(self, threads: int = 8):
-        """Dequantize every linear up front (setup only; the same load_linear per tensor)."""
+        """Dequantize every linear up front (setup only; the same loader per tensor)."""
         from concurrent.futures import ThreadPoolExecutor
-        c = self.cfg
-        names = [(n, None, None) for n in sorted({k.rsplit(".", 1)[0] for k in self.blob.entries
-                                                    if k.endswith(".q") and not k.startswith("embedding")})]
-        if c["has_embedding"]:
-            names.append(("embedding", c["embed_bits"], c["embed_group"]))
-        todo = [t for t in names if t[0] not in self._w]
+        suffixes = (".q", ".weight", ".fp4", ".fp8")
+        names = sorted({k.rsplit(".", 1)[0] for k in self.blob.entries if k.endswith(suffixes)})
+        if not self.cfg["has_embedding"]:
+            names = [n for n in names if n != "embedding"]
+        todo = [n for n in names if n not in self._w]
+
+        def one(n):
+            fmt, b, g = self.fmt_of(n)
+            return load_weight(self.blob, n, fmt, b, g)
         with ThreadPoolExecutor(threads) as ex:
-            for (n, _, _), w in zip(todo, ex.map(lambda t: load_linear(self.blob, t[0], t[1] or c["bits"],
-                                                                      t[2] or c["group"]), todo)):
+            for n, w in zip(todo, ex.map(one, todo)):
                 self._w[n] = w
 
     def new_slot(self) -> SlotState:

@@ -355,3 +355,62 @@ def test_bf16_round_matches_storage_rounding():
     x = rng.standard_normal(10000).astype(np.float32)
     via_bits = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x)).astype(np.float64)
     assert np.array_equal(ref.bf16_round(x.astype(np.float64)), via_bits)
+
+
+# ----------------------------------------------------------------------------------------------
+# NVFP4 and block-FP8 weights ("TensorFold PR #1508": the FFN as e2m1 codes in groups of 16 with
+# e4m3 block scales and an fp32 tensor scale; block-FP8 linears)
+# ----------------------------------------------------------------------------------------------
+
+
+def test_e4m3_matches_torch_float8_for_every_byte():
+    """The oracle's E4M3 decoder against torch's float8_e4m3fn, an independent implementation."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = ref.e4m3_values(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert ref.e4m3_values(np.array([0x7E]))[0] == 448.0          # the largest finite value
+    assert ref.e4m3_values(np.array([0x01]))[0] == 2.0 ** -9      # the smallest subnormal
+
+
+def test_e2m1_through_e4m3():
+    """E2M1 (exponent bias 1) embeds in E4M3 (bias 7): a normal code (s, e, m) is the E4M3 byte with
+    exponent e + 6 and mantissa m << 2; the subnormal 0.5 is exponent 6, mantissa 0. torch's E4M3
+    decoder then gives every E2M1 value; they are the 8 magnitudes 0 .. 6 and their negatives."""
+    import torch
+    codes = np.arange(16)
+    s, e, m = codes >> 3, (codes >> 1) & 3, codes & 1
+    byte = np.where(e > 0, (s << 7) | ((e + 6) << 3) | (m << 2),
+                    np.where(m == 1, (s << 7) | (6 << 3), s << 7)).astype(np.uint8)
+    want = torch.from_numpy(byte).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ref.e2m1_values(codes), want)
+    assert sorted(set(np.abs(want))) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_nvfp4_dequant_hand_packed():
+    """Two rows of 32 codes: element 2i in a byte's low nibble, one e4m3 scale per 16 k, the
+    tensor scale on everything."""
+    packed = np.zeros((2, 16), dtype=np.uint8)
+    packed[0, 0] = 0x2A          # k0: code 0xA = -1.0, k1: code 0x2 = +1.0
+    packed[0, 7] = 0xF1          # k14: 0x1 = 0.5, k15: 0xF = -6.0
+    packed[0, 8] = 0x07          # k16: 0x7 = 6.0 (next group), k17: 0
+    packed[1, 15] = 0x5B         # k30: 0xB = -1.5, k31: 0x5 = 3.0
+    scales = np.array([[0x38, 0x40], [0x30, 0x48]], dtype=np.uint8)   # 1.0, 2.0 / 0.5, 4.0
+    w = ref.dequant_nvfp4(packed, scales, 0.25)
+    want = np.zeros((2, 32))
+    want[0, [0, 1, 14, 15]] = np.array([-1.0, 1.0, 0.5, -6.0]) * 1.0 * 0.25
+    want[0, 16] = 6.0 * 2.0 * 0.25
+    want[1, [30, 31]] = np.array([-1.5, 3.0]) * 4.0 * 0.25
+    assert np.array_equal(w, want)
+
+
+def test_fp8_block_dequant_boundaries():
+    """One scale per 128 x 128 block: the scales change exactly at row 128 and at column 128."""
+    codes = np.full((130, 260), 0x38, dtype=np.uint8)        # every code 1.0
+    sc = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])
+    w = ref.dequant_fp8_block(codes, sc)
+    assert w[127, 127] == 1.0 and w[127, 128] == 2.0 and w[128, 127] == 4.0 and w[129, 259] == 6.0
+    assert w[0, 256] == 3.0
