@@ -123,12 +123,55 @@ LFM3_DEV uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// A quantized linear [N, K] as stored in the blob (device pointers into it).
-struct QLinear {
-  const uint8_t* q;       // [N, K * bits / 8]
-  const bf16_t* scales;   // [N, K / group]
-  const bf16_t* biases;   // [N, K / group]
-  int32_t n, k, bits, group;
+// Storage formats of a linear's weight.
+enum WeightFmt {
+  FMT_AFFINE = 0,   // MLX affine: `bits`-bit codes, bf16 scale and bias per `group` along K
+  FMT_BF16 = 1,     // stored bf16 values
+  FMT_NVFP4 = 2,    // e2m1 codes (two a byte, element 2i in the low nibble), an e4m3 scale per 16 k, an fp32 tensor scale
+  FMT_FP8B = 3      // e4m3 codes, an fp32 scale per 128 x 128 block
 };
+
+// A linear [N, K] as stored in the blob (device pointers into it).
+struct QLinear {
+  const uint8_t* q;       // affine: [N, K * bits / 8]; bf16: [N, K] bf16; nvfp4: [N, K / 2]; fp8b: [N, K]
+  const bf16_t* scales;   // affine: [N, K / group]
+  const bf16_t* biases;   // affine: [N, K / group]
+  int32_t n, k, bits, group;
+  int32_t fmt;            // WeightFmt
+  const uint8_t* bscale;  // nvfp4: e4m3 [N, K / 16]; fp8b: fp32 [ceil(N / 128), ceil(K / 128)]
+  float tscale;           // nvfp4: the tensor scale (1 otherwise)
+};
+
+// FP4 E2M1 code (4 bits) as an fp16 bit pattern worth 2^-14 of its value: the exponent and mantissa
+// bits moved to fp16 bits 11..9 (exponent 0 becomes an fp16 subnormal, as E2M1's is), the sign to 15.
+LFM3_HOST_DEV uint32_t e2m1_f16_scaled(uint32_t c) { return ((c & 7u) << 9) | ((c & 8u) << 12); }
+// FP8 E4M3 byte as an fp16 bit pattern worth 2^-8 of its value (exponent and mantissa to bits
+// 13..7, sign to 15; exponent 0 is a subnormal in both). NaN bytes (0x7F, 0xFF) are never stored.
+LFM3_HOST_DEV uint32_t e4m3_f16_scaled(uint32_t b) { return ((b & 0x7Fu) << 7) | ((b & 0x80u) << 8); }
+LFM3_DEV float e4m3_value(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)e4m3_f16_scaled(b)) * 256.f;
+}
+LFM3_DEV float e2m1_value(uint32_t c) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)e2m1_f16_scaled(c)) * 16384.f;
+}
+
+// Weight (n, k) of a non-affine linear in fp32: exact for bf16; for nvfp4 and fp8b the code times
+// its block scale is exact in fp32 and one fp32 multiply rounds the product with the tensor scale
+// (nvfp4) or the fp32 block scale (fp8b).
+LFM3_DEV float weight_value(const QLinear& w, int n, int k) {
+  if (w.fmt == FMT_BF16) {
+    const uint16_t b = ((const uint16_t*)w.q)[(size_t)n * w.k + k];
+    return __uint_as_float((uint32_t)b << 16);
+  }
+  if (w.fmt == FMT_NVFP4) {
+    const uint32_t byte = w.q[(size_t)n * (w.k / 2) + k / 2];
+    const uint32_t c = (k & 1) ? byte >> 4 : byte & 15u;
+    const float sc = e4m3_value(w.bscale[(size_t)n * (w.k / 16) + k / 16]);
+    return (e2m1_value(c) * sc) * w.tscale;
+  }
+  const int kb = (w.k + 127) / 128;
+  const float sc = ((const float*)w.bscale)[(size_t)(n / 128) * kb + k / 128];
+  return e4m3_value(w.q[(size_t)n * w.k + k]) * sc;
+}
 
 }  // namespace lfm3

@@ -328,6 +328,36 @@ hipError_t launch_repack_gemm16(hipStream_t s, const GemmW& w, uint32_t* w16) {
   return hipGetLastError();
 }
 
+// The fp16 operand copy of a linear stored as bf16, NVFP4 or block-FP8: one wave per (32-row,
+// 64-k) tile, lane l writes its four planes of f16(weight_value) (rows past N repeat row N - 1).
+__global__ void __launch_bounds__(64) k_make_w16(QLinear w, uint32_t* w16, int nk) {
+  const size_t tile = blockIdx.x;          // wtile * nk + kt
+  const int lane = threadIdx.x;
+  const int nt = (int)(tile / nk), kt = (int)(tile - (size_t)nt * nk);
+  const int row = min(nt * 32 + (lane & 31), w.n - 1);
+  const int k0 = kt * BK + 32 * (lane >> 5);
+  u32x4_v* out = (u32x4_v*)(w16 + tile * 1024);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    uint32_t p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + 8 * t + 2 * i;
+      p[i] = (uint32_t)f2h(weight_value(w, row, k)) | ((uint32_t)f2h(weight_value(w, row, k + 1)) << 16);
+    }
+    out[t * 64 + lane] = u32x4_v{p[0], p[1], p[2], p[3]};
+  }
+}
+
+hipError_t launch_make_w16(hipStream_t s, const QLinear& w, uint32_t* w16) {
+  if (w.fmt == FMT_AFFINE || !w16 || w.k % BK) return hipErrorInvalidValue;
+  const int nk = w.k / BK;
+  const size_t tiles = (size_t)((w.n + 31) / 32) * nk;
+  if (tiles == 0 || tiles > 0x7fffffff || tiles * 4096u > 0xffffffffull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_make_w16, dim3((unsigned)tiles), dim3(64), 0, s, w, w16, nk);
+  return hipGetLastError();
+}
+
 // One block of 64 threads per (32-row, 64-k) tile; thread l writes lane l's codes and (scale,
 // bias) pair of the re-tiled copy (the layout is described with GemmW).
 template <int BITS>
@@ -396,7 +426,7 @@ static hipError_t launch_bits(hipStream_t s, const GemmArgs& a) {
 hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
   if (a.m <= 0) return hipSuccess;
   // 16-byte rows of X, an even number of K tiles, 32-code runs inside one group, whole SwiGLU tiles
-  if (a.w.k % (2 * BK) || a.w.group % 32 || a.ldx % 8 || (uintptr_t)a.x % 16 || (uintptr_t)a.x_lo % 16 ||
+  if (a.w.k % (2 * BK) || (!a.w.w16 && a.w.group % 32) || a.ldx % 8 || (uintptr_t)a.x % 16 || (uintptr_t)a.x_lo % 16 ||
       a.w.ntile != (a.w.n + 31) / 32 || (a.epi == GEMM_SWIGLU && a.w.n % BN))
     return hipErrorInvalidValue;
   // a K split: two halves of an even number of K tiles, plain STORE
@@ -436,12 +466,14 @@ constexpr int kHeadTiles = 4;    // 32-row tiles of the head per block
 // WV waves per block (4, or 8 to halve each wave's K walk on the short-M, one-block-per-CU launches).
 template <int BITS, int EPI, int MT, int WV>
 __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
+  constexpr bool F16 = BITS == 16;             // operands from the fp16 copy (GemmW::w16)
+  constexpr int QB = F16 ? 4 : BITS;
   constexpr int NT = SgTiles<EPI>::v;
   constexpr int NTH = 64 * WV;
   static_assert(EPI != GEMV_LOGITS || WV == 4, "the head's argmax slots assume 256 threads");
   constexpr int D = MT == 1 ? 4 : 2;   // K tiles in flight per wave
   constexpr int TW = NT * 32, TR = MT * 32;
-  constexpr uint32_t kTileBytes = 256u * BITS;
+  constexpr uint32_t kTileBytes = F16 ? 4096u : 256u * BITS;
   extern __shared__ __attribute__((aligned(16))) float sg_smem[];   // [WV][TR][32] partials, [TR][TW] sums
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hf = lane >> 5, c32 = lane & 31;
@@ -468,12 +500,12 @@ __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
   } else {
     tile[0] = tb;
   }
-  const __amdgpu_buffer_rsrc_t rq = rsrc_of(w.codes, (uint32_t)w.ntile * nk * kTileBytes);
-  const __amdgpu_buffer_rsrc_t rsb = rsrc_of(w.sb, (uint32_t)w.ntile * nk * 256u);
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(F16 ? (const void*)w.w16 : (const void*)w.codes, (uint32_t)w.ntile * nk * kTileBytes);
+  const __amdgpu_buffer_rsrc_t rsb = rsrc_of(F16 ? (const void*)w.w16 : (const void*)w.sb, (uint32_t)w.ntile * nk * 256u);
   uint32_t qoff[NT], sboff[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    qoff[j] = (uint32_t)tile[j] * nk * kTileBytes + (uint32_t)lane * Planes<BITS>::PB;
+    qoff[j] = (uint32_t)tile[j] * nk * kTileBytes + (uint32_t)lane * (F16 ? 16u : (uint32_t)Planes<QB>::PB);
     sboff[j] = ((uint32_t)tile[j] * nk * 64u + lane) * 4u;
   }
   // the lane's A rows: virtual row 32i + c32 (x rows, then x_lo rows; rows past Meff read row 0)
@@ -485,8 +517,9 @@ __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
   }
 
   struct WSet {
-    Run<BITS> run[NT];
-    uint32_t sb[NT];
+    Run<QB> run[F16 ? 1 : NT];
+    uint32_t sb[F16 ? 1 : NT];
+    u32x4_v p[F16 ? NT : 1][F16 ? 4 : 1];   // fp16 copy: the operand registers themselves
     u32x4_v av[MT][4];
   };
   // K tiles [k0, k0 + nkb) of this block; this wave's: k0 + wave, k0 + wave + WV, ...
@@ -496,8 +529,13 @@ __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
     const int kt = k0 + wave + WV * min(s, ns - 1);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      load_run<BITS>(rq, qoff[j], (uint32_t)kt * kTileBytes, ws.run[j]);
-      ws.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, sboff[j], (uint32_t)kt * 256u, 0);
+      if constexpr (F16) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ws.p[j][t] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j] + 1024u * t, (uint32_t)kt * kTileBytes, 0);
+      } else {
+        load_run<QB>(rq, qoff[j], (uint32_t)kt * kTileBytes, ws.run[j]);
+        ws.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, sboff[j], (uint32_t)kt * 256u, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -515,7 +553,7 @@ __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
     f16x2_v s2[NT], b2[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const f16x2_v sbv = __builtin_bit_cast(f16x2_v, ws.sb[j]);
+      const f16x2_v sbv = __builtin_bit_cast(f16x2_v, ws.sb[F16 ? 0 : j]);
       s2[j] = __builtin_shufflevector(sbv, sbv, 0, 0);
       b2[j] = __builtin_shufflevector(sbv, sbv, 1, 1);
     }
@@ -523,7 +561,9 @@ __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
       constexpr int T = decltype(tc)::value;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const f16x8_v b = deq8<BITS, T>(ws.run[j], s2[j], b2[j]);
+        f16x8_v b;
+        if constexpr (F16) b = __builtin_bit_cast(f16x8_v, ws.p[j][T]);
+        else b = deq8<QB, T>(ws.run[F16 ? 0 : j], s2[j], b2[j]);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_v, ws.av[i][T]), b, acc[i][j], 0, 0, 0);
@@ -703,11 +743,15 @@ static hipError_t launch_sg_bits(hipStream_t s, const GemmW& w, const GemvArgs& 
 
 hipError_t launch_sgemm(hipStream_t s, const GemmW& w, const GemvArgs& g) {
   const int meff = g.x_lo ? 2 * g.batch : g.batch;
-  if (g.batch < 1 || meff > 64 || w.k % (4 * BK) || w.group % 32 || g.ldx % 8 || (uintptr_t)g.x % 16 ||
+  if (g.batch < 1 || meff > 64 || w.k % (4 * BK) || (!w.w16 && w.group % 32) || g.ldx % 8 || (uintptr_t)g.x % 16 ||
       (uintptr_t)g.x_lo % 16 || w.ntile != (w.n + 31) / 32 ||
       (g.epi == GEMV_SWIGLU && w.n % 64) || (g.epi == GEMV_CONV && ((w.n / 3) % 32 || w.n % 3 || g.conv_taps < 2 ||
                                                                   g.conv_taps > kMaxTaps)))
     return hipErrorInvalidValue;
+  if (w.w16) {
+    if ((size_t)w.ntile * (w.k / BK) * 4096u > 0xffffffffull) return hipErrorInvalidValue;
+    return launch_sg_bits<16>(s, w, g, meff);
+  }
   switch (w.bits) {
     case 4: return launch_sg_bits<4>(s, w, g, meff);
     case 6: return launch_sg_bits<6>(s, w, g, meff);

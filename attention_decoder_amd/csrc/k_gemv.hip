@@ -18,10 +18,19 @@
 
 namespace lfm3 {
 
+// Chunk geometry of a weight format: CH weights per lane chunk, NDW dwords of codes, NP fp16 pairs
+// after unpacking, CB code bits. BITS 4 / 6 / 8 are MLX affine codes; 16 stored bf16 weights; 41
+// NVFP4 (e2m1 codes, an e4m3 scale per 16 k, an fp32 tensor scale); 48 block-FP8 (e4m3 codes, an
+// fp32 scale per 128 x 128 block).
 template <int BITS> struct QT;
-template <> struct QT<4> { static constexpr int CH = 32, NDW = 4, NP = 16; };
-template <> struct QT<6> { static constexpr int CH = 16, NDW = 3, NP = 8; };
-template <> struct QT<8> { static constexpr int CH = 16, NDW = 4, NP = 8; };
+template <> struct QT<4> { static constexpr int CH = 32, NDW = 4, NP = 16, CB = 4; };
+template <> struct QT<6> { static constexpr int CH = 16, NDW = 3, NP = 8, CB = 6; };
+template <> struct QT<8> { static constexpr int CH = 16, NDW = 4, NP = 8, CB = 8; };
+template <> struct QT<16> { static constexpr int CH = 8, NDW = 4, NP = 4, CB = 16; };
+template <> struct QT<41> { static constexpr int CH = 32, NDW = 4, NP = 16, CB = 4; };
+template <> struct QT<48> { static constexpr int CH = 16, NDW = 4, NP = 8, CB = 8; };
+// The pair order of a format's unpacked codes (NVFP4 pairs like 4-bit codes, block-FP8 like 8-bit).
+template <int BITS> struct PairOrder { static constexpr int v = BITS == 41 ? 4 : BITS == 48 ? 8 : BITS; };
 constexpr float kMagicOff = 1024.f;       // fp16 0x6400 | q == 1024 + q for q < 1024
 constexpr uint32_t kMagic2 = 0x64006400u;
 
@@ -73,6 +82,31 @@ template <int BITS> LFM3_DEV void unpack(const uint32_t (&w)[QT<BITS>::NDW], uin
       p[2 * d] = (w[d] & 0x00FF00FFu) | magic;
       p[2 * d + 1] = ((w[d] >> 8) & 0x00FF00FFu) | magic;
     }
+  }
+}
+
+// NVFP4: e2m1 codes of one chunk (4 words, 32 codes) as fp16 pairs worth 2^-14 of their values,
+// in the 4-bit pair order: pair 4d + j holds nibbles j and j + 4 of word d. A half's nibble
+// s e e m becomes fp16 bits 15 (s) and 11..9 (e e m).
+LFM3_DEV void unpack_e2m1(const uint32_t (&w)[4], uint32_t (&p)[16]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t x = w[d];
+    p[4 * d] = ((x & 0x00070007u) << 9) | ((x & 0x00080008u) << 12);
+    p[4 * d + 1] = ((x & 0x00700070u) << 5) | ((x & 0x00800080u) << 8);
+    p[4 * d + 2] = ((x & 0x07000700u) << 1) | ((x & 0x08000800u) << 4);
+    p[4 * d + 3] = ((x & 0x70007000u) >> 3) | (x & 0x80008000u);
+  }
+}
+
+// Block-FP8: e4m3 codes of one chunk (4 words, 16 codes) as fp16 pairs worth 2^-8 of their
+// values, in the 8-bit pair order: pair 2d = bytes 0 and 2 of word d, pair 2d + 1 = bytes 1 and 3.
+LFM3_DEV void unpack_e4m3(const uint32_t (&w)[4], uint32_t (&p)[8]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t x = w[d], y = w[d] >> 8;
+    p[2 * d] = ((x & 0x007F007Fu) << 7) | ((x & 0x00800080u) << 8);
+    p[2 * d + 1] = ((y & 0x007F007Fu) << 7) | ((y & 0x00800080u) << 8);
   }
 }
 
@@ -137,11 +171,11 @@ LFM3_DEV float bfly8(const float (&in)[8]) {
 // unpacked codes pair up.
 template <int BITS> LFM3_DEV uint4 pair_order8(const uint32_t (&h)[4]) {
   // h: 8 fp16 in natural order, two per word
-  if constexpr (BITS == 4) {
+  if constexpr (PairOrder<BITS>::v == 4) {
     // (x0, x4), (x1, x5), (x2, x6), (x3, x7)
     return make_uint4(__builtin_amdgcn_perm(h[2], h[0], 0x05040100u), __builtin_amdgcn_perm(h[2], h[0], 0x07060302u),
                       __builtin_amdgcn_perm(h[3], h[1], 0x05040100u), __builtin_amdgcn_perm(h[3], h[1], 0x07060302u));
-  } else if constexpr (BITS == 8) {
+  } else if constexpr (PairOrder<BITS>::v == 8) {
     // (x0, x2), (x1, x3), (x4, x6), (x5, x7)
     return make_uint4(__builtin_amdgcn_perm(h[1], h[0], 0x05040100u), __builtin_amdgcn_perm(h[1], h[0], 0x07060302u),
                       __builtin_amdgcn_perm(h[3], h[2], 0x05040100u), __builtin_amdgcn_perm(h[3], h[2], 0x07060302u));
@@ -388,8 +422,9 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = a.w.n;
   const int n_groups = n_groups_of<EPI>(N);
-  const size_t row_bytes = (size_t)K * BITS / 8;
-  const int ngr = K / a.w.group;
+  const size_t row_bytes = (size_t)K * Q::CB / 8;
+  constexpr bool AFFINE = BITS == 4 || BITS == 6 || BITS == 8;
+  const int ngr = AFFINE ? K / a.w.group : 1;
   // group walk: a wave (KW = 1) or a block (KW > 1) takes groups g0, g0 + gstride, ...
   const int g0 = KW == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
   const int gstride = KW == 1 ? gridDim.x * 4 : gridDim.x;
@@ -404,17 +439,18 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   // the end of the wave).
   struct WRegs {
     uint32_t q[RG][Q::NDW];
-    bf16_t s[RG], b[RG];   // raw bits: converted when used
+    bf16_t s[RG], b[RG];   // raw bits: converted when used (NVFP4: s holds the chunk's two e4m3 scales)
+    float f[BITS == 48 ? RG : 1];   // block-FP8: the chunk's fp32 block scale
   };
   auto fetch = [&](WRegs& W, int step) {
     const int gi = step / NITW, it = kw + KW * (step - gi * NITW);
     const int c = min(lane + 64 * it, NC - 1);
     int rows[RG];
     rows_of<EPI>(min(g0 + gi * gstride, n_groups - 1), N, rows);
-    const int grp = (c * Q::CH) / a.w.group;
+    const int grp = AFFINE ? (c * Q::CH) / a.w.group : 0;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
-      const uint32_t* src = (const uint32_t*)(a.w.q + (size_t)rows[r] * row_bytes + (size_t)c * (Q::CH * BITS / 8));
+      const uint32_t* src = (const uint32_t*)(a.w.q + (size_t)rows[r] * row_bytes + (size_t)c * (Q::CH * Q::CB / 8));
       if constexpr (Q::NDW == 4) {
         const u32x4_v v = __builtin_nontemporal_load((const u32x4_v*)src);
         W.q[r][0] = v[0]; W.q[r][1] = v[1]; W.q[r][2] = v[2]; W.q[r][3] = v[3];
@@ -422,8 +458,14 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
 #pragma unroll
         for (int d = 0; d < Q::NDW; ++d) W.q[r][d] = __builtin_nontemporal_load(src + d);
       }
-      W.s[r] = a.w.scales[(size_t)rows[r] * ngr + grp];
-      W.b[r] = a.w.biases[(size_t)rows[r] * ngr + grp];
+      if constexpr (AFFINE) {
+        W.s[r] = a.w.scales[(size_t)rows[r] * ngr + grp];
+        W.b[r] = a.w.biases[(size_t)rows[r] * ngr + grp];
+      } else if constexpr (BITS == 41) {
+        W.s[r] = *(const uint16_t*)(a.w.bscale + (size_t)rows[r] * (K / 16) + 2 * c);
+      } else if constexpr (BITS == 48) {
+        W.f[r] = ((const float*)a.w.bscale)[(size_t)(rows[r] / 128) * ((K + 127) / 128) + (c * Q::CH) / 128];
+      }
     }
   };
 
@@ -521,6 +563,62 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
         X[b] = xs.x;
         XO[b] = xs.y;
       }
+      if constexpr (BITS == 16) {
+        // stored bf16 weights: products of exact fp32 values (8 + 11 significant bits), fp32 sums
+        float xf[BT][8];
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            xf[b][2 * q] = h2f((f16_t)(xv[b][q] & 0xffffu));
+            xf[b][2 * q + 1] = h2f((f16_t)(xv[b][q] >> 16));
+          }
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            float d = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              d = fmaf(__uint_as_float(W.q[r][q] << 16), xf[b][2 * q], d);
+              d = fmaf(__uint_as_float(W.q[r][q] & 0xffff0000u), xf[b][2 * q + 1], d);
+            }
+            acc[r][b] += d;
+          }
+      } else if constexpr (BITS == 41) {
+        // NVFP4: two groups of 16 codes a chunk (pairs 0-7, 8-15), each times its e4m3 scale; the
+        // values carry 2^-14 (codes) and 2^-8 (scales), removed with the tensor scale at the end
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          uint32_t wp[16];
+          unpack_e2m1(W.q[r], wp);
+          const float s0 = h2f((f16_t)e4m3_f16_scaled(W.s[r] & 0xffu)), s1 = h2f((f16_t)e4m3_f16_scaled(W.s[r] >> 8));
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+              d0 = dot2(wp[p], xv[b][p], d0);
+              d1 = dot2(wp[p + 8], xv[b][p + 8], d1);
+            }
+            acc[r][b] += fmaf(d0, s0, d1 * s1);
+          }
+        }
+      } else if constexpr (BITS == 48) {
+        // block-FP8: one fp32 scale for the chunk; the values carry 2^-8, removed at the end
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          uint32_t wp[8];
+          unpack_e4m3(W.q[r], wp);
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            float d = 0.f;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) d = dot2(wp[p], xv[b][p], d);
+            acc[r][b] = fmaf(d, W.f[r], acc[r][b]);
+          }
+        }
+      } else {
 #pragma unroll
       for (int r = 0; r < RG; ++r) {
         uint32_t wp[Q::NP];
@@ -546,6 +644,7 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
           }
           acc[r][b] += fmaf(sc, inner, bi * X[b]);
         }
+      }
       }
     }
     if (sw != NITW - 1) return;
@@ -582,6 +681,12 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
       if (split)
 #pragma unroll
         for (int b = 0; b < BT / 2; ++b) t[b] = t[b] + t[b + BT / 2];
+    }
+    if constexpr (BITS == 41 || BITS == 48) {
+      // the codes' and scales' powers of two (2^-14 and 2^-8, or 2^-8), and NVFP4's tensor scale
+      const float mult = BITS == 41 ? a.w.tscale * 4194304.f : 256.f;
+#pragma unroll
+      for (int b = 0; b < BT; ++b) t[b] *= mult;
     }
     const int r = lane >> 3;
     if constexpr (EPI == GEMV_STORE) {
@@ -690,6 +795,12 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
 
 template <int BITS, int BT, int PRO, int KW>
 static void launch_epi(hipStream_t s, const GemvArgs& a, int grid, size_t lds) {
+  if constexpr (BITS == 41 || BITS == 48) {
+    // the FFN formats: w13 with the SwiGLU epilogue, w2 plain (the caller refuses other epilogues)
+    if (a.epi == GEMV_SWIGLU) hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_SWIGLU, PRO, KW>), dim3(grid), dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, PRO, KW>), dim3(grid), dim3(256), lds, s, a);
+    return;
+  }
   switch (a.epi) {
     case GEMV_STORE: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
     case GEMV_SWIGLU: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_SWIGLU, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
@@ -726,8 +837,9 @@ static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
     }
   } else if (a.part) {
     if constexpr (BT <= 2) {
-      if (split || a.epi != GEMV_STORE) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, 2, 1>), dim3(grid), dim3(256), lds, s, a);
+      if (a.epi != GEMV_STORE) return hipErrorInvalidValue;
+      if (split) hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, 2, 4>), dim3(grid), dim3(256), lds, s, a);
+      else hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, 2, 1>), dim3(grid), dim3(256), lds, s, a);
     } else {
       return hipErrorInvalidValue;
     }
@@ -794,10 +906,21 @@ hipError_t launch_gemv(hipStream_t s, const GemvArgs& a) {
                  (a.w_post && (uintptr_t)a.w_post % 16))
               : ((uintptr_t)a.x % 16 || a.ldx % 8 || (uintptr_t)a.x_lo % 16))
     return hipErrorInvalidValue;
-  switch (a.w.bits) {
-    case 4: return launch_bits<4>(s, a);
-    case 6: return launch_bits<6>(s, a);
-    case 8: return launch_bits<8>(s, a);
+  switch (a.w.fmt) {
+    case FMT_AFFINE:
+      switch (a.w.bits) {
+        case 4: return launch_bits<4>(s, a);
+        case 6: return launch_bits<6>(s, a);
+        case 8: return launch_bits<8>(s, a);
+        default: return hipErrorInvalidValue;
+      }
+    case FMT_BF16: return launch_bits<16>(s, a);
+    case FMT_NVFP4:
+      if (a.w.k % 32 || (a.epi != GEMV_STORE && a.epi != GEMV_SWIGLU) || a.part) return hipErrorInvalidValue;
+      return launch_bits<41>(s, a);
+    case FMT_FP8B:
+      if (a.w.k % 16 || (a.epi != GEMV_STORE && a.epi != GEMV_SWIGLU) || a.part) return hipErrorInvalidValue;
+      return launch_bits<48>(s, a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -34,6 +34,10 @@ __global__ void __launch_bounds__(256) k_embed(QLinear e, const int32_t* __restr
     if (threadIdx.x == 0) atomicOr(flags, 1u);
     return;
   }
+  if (e.fmt != FMT_AFFINE) {
+    for (int k = threadIdx.x; k < e.k; k += blockDim.x) out[k] = weight_value(e, tok, k);
+    return;
+  }
   const size_t row_bytes = (size_t)e.k * e.bits / 8;
   const uint8_t* row = e.q + (size_t)tok * row_bytes;
   const int ng = e.k / e.group;
@@ -67,6 +71,14 @@ hipError_t launch_bf16_to_f32(hipStream_t s, const bf16_t* in, int rows, int col
 __global__ void __launch_bounds__(256) k_dequant_rows(QLinear w, int row0, float* f32, f16_t* hv) {
   const int r = blockIdx.x;
   const int n = row0 + r;
+  if (w.fmt != FMT_AFFINE) {
+    for (int k = threadIdx.x; k < w.k; k += blockDim.x) {
+      const float v = weight_value(w, n, k);
+      if (f32) f32[(size_t)r * w.k + k] = v;
+      if (hv) hv[(size_t)r * w.k + k] = f2h(v);
+    }
+    return;
+  }
   const size_t row_bytes = (size_t)w.k * w.bits / 8;
   const uint8_t* row = w.q + (size_t)n * row_bytes;
   const int ng = w.k / w.group;

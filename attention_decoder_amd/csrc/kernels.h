@@ -174,6 +174,7 @@ struct GemmW {
   const uint32_t* sb;
   const uint32_t* w16;
   int32_t n, k, bits, group, ntile;
+  int32_t fmt;   // the stored format (WeightFmt); bf16, NVFP4 and block-FP8 have only w16
 };
 size_t gemm_codes_bytes(int n, int k, int bits);
 size_t gemm_sb_bytes(int n, int k);
@@ -181,6 +182,9 @@ size_t gemm_w16_bytes(int n, int k);
 hipError_t launch_repack_gemm(hipStream_t s, const QLinear& w, uint8_t* codes, uint32_t* sb);
 // w16 from the re-tiled codes and (scale, bias) of w (which must already hold them).
 hipError_t launch_repack_gemm16(hipStream_t s, const GemmW& w, uint32_t* w16);
+// w16 straight from a linear stored as bf16, NVFP4 or block-FP8: f16 of each weight's fp32 value
+// (weight_value), in the same operand order. These linears have no re-tiled codes.
+hipError_t launch_make_w16(hipStream_t s, const QLinear& w, uint32_t* w16);
 
 // Decode linears of 3 .. 32 rows on MFMA from the re-tiled weights: the GEMV's STORE, SWIGLU,
 // CONV and LOGITS epilogues with its argument block (x, x_lo, batch, outputs, conv state, argmax

@@ -32,7 +32,19 @@ struct Entry {
   uint64_t offset, nbytes;
 };
 
-constexpr uint32_t DT_CODES = 0, DT_BF16 = 1;
+constexpr uint32_t DT_CODES = 0, DT_BF16 = 1, DT_F32 = 2;
+
+// Storage of one linear: format, code bits, group (affine) -- from the config by role.
+struct LinFmt {
+  int fmt, bits, group;
+};
+enum LinRole { ROLE_MIXER = 0, ROLE_FFN = 1, ROLE_EMBED = 2 };
+LinFmt fmt_of(const lfm3_config& c, int role) {
+  if (role == ROLE_EMBED) return c.embed_bits == 16 ? LinFmt{FMT_BF16, 16, 0} : LinFmt{FMT_AFFINE, c.embed_bits, c.embed_group};
+  if (role == ROLE_FFN && c.ffn_format == LFM3_FFN_NVFP4) return {FMT_NVFP4, 4, 16};
+  if (role == ROLE_FFN && c.ffn_format == LFM3_FFN_FP8_BLOCK) return {FMT_FP8B, 8, 128};
+  return c.bits == 16 ? LinFmt{FMT_BF16, 16, 0} : LinFmt{FMT_AFFINE, c.bits, c.group};
+}
 
 struct Expect {
   std::string name;
@@ -48,39 +60,52 @@ int n_of_type(const lfm3_config& c, int t) {
 
 int qkvg_rows(const lfm3_config& c) { return c.n_q_heads * c.head_dim + 2 * c.n_kv_heads * c.head_dim + c.n_q_heads; }
 
-void add_linear(std::vector<Expect>& v, const std::string& name, uint32_t n, uint32_t k, int bits, int group) {
-  v.push_back({name + ".q", DT_CODES, {n, (uint32_t)((uint64_t)k * bits / 8)}});
-  v.push_back({name + ".scales", DT_BF16, {n, k / (uint32_t)group}});
-  v.push_back({name + ".biases", DT_BF16, {n, k / (uint32_t)group}});
+void add_linear(std::vector<Expect>& v, const std::string& name, uint32_t n, uint32_t k, LinFmt f) {
+  if (f.fmt == FMT_BF16) {
+    v.push_back({name + ".weight", DT_BF16, {n, k}});
+  } else if (f.fmt == FMT_NVFP4) {
+    v.push_back({name + ".fp4", DT_CODES, {n, k / 2}});
+    v.push_back({name + ".block_scales", DT_CODES, {n, k / 16}});
+    v.push_back({name + ".tensor_scale", DT_F32, {1}});
+    v.push_back({name + ".input_scale", DT_F32, {1}});
+  } else if (f.fmt == FMT_FP8B) {
+    v.push_back({name + ".fp8", DT_CODES, {n, k}});
+    v.push_back({name + ".block_scales", DT_F32, {(n + 127) / 128, (k + 127) / 128}});
+  } else {
+    v.push_back({name + ".q", DT_CODES, {n, (uint32_t)((uint64_t)k * f.bits / 8)}});
+    v.push_back({name + ".scales", DT_BF16, {n, k / (uint32_t)f.group}});
+    v.push_back({name + ".biases", DT_BF16, {n, k / (uint32_t)f.group}});
+  }
 }
 
 std::vector<Expect> expected_tensors(const lfm3_config& c) {
   std::vector<Expect> v;
   const uint32_t H = c.hidden, F = c.ffn, D = c.head_dim;
-  if (c.has_embedding) add_linear(v, "embedding", c.vocab, H, c.embed_bits, c.embed_group);
+  const LinFmt fm = fmt_of(c, ROLE_MIXER), ff = fmt_of(c, ROLE_FFN);
+  if (c.has_embedding) add_linear(v, "embedding", c.vocab, H, fmt_of(c, ROLE_EMBED));
   for (int i = 0; i < c.n_layers; ++i) {
     const std::string p = "layers." + std::to_string(i) + ".";
     for (const char* nm : {"operator_norm", "post_operator_norm", "ffn_norm", "post_ffn_norm"})
       v.push_back({p + nm, DT_BF16, {H}});
     if (c.layer_type[i] == LFM3_LAYER_CONV) {
       v.push_back({p + "conv.kernel", DT_BF16, {H, (uint32_t)c.conv_taps}});
-      add_linear(v, p + "conv.in_proj", 3 * H, H, c.bits, c.group);
-      add_linear(v, p + "conv.out_proj", H, H, c.bits, c.group);
+      add_linear(v, p + "conv.in_proj", 3 * H, H, fm);
+      add_linear(v, p + "conv.out_proj", H, H, fm);
     } else {
       v.push_back({p + "attn.q_norm", DT_BF16, {D}});
       v.push_back({p + "attn.k_norm", DT_BF16, {D}});
-      add_linear(v, p + "attn.qkvg_proj", qkvg_rows(c), H, c.bits, c.group);
-      add_linear(v, p + "attn.o_proj", H, c.n_q_heads * D, c.bits, c.group);
+      add_linear(v, p + "attn.qkvg_proj", qkvg_rows(c), H, fm);
+      add_linear(v, p + "attn.o_proj", H, c.n_q_heads * D, fm);
     }
-    add_linear(v, p + "ffn.w13", 2 * F, H, c.bits, c.group);
-    add_linear(v, p + "ffn.w2", H, F, c.bits, c.group);
+    add_linear(v, p + "ffn.w13", 2 * F, H, ff);
+    add_linear(v, p + "ffn.w2", H, F, ff);
   }
   v.push_back({"embedding_norm", DT_BF16, {H}});
   return v;
 }
 
 uint64_t elem_bytes(const Expect& e) {
-  uint64_t n = e.dtype == DT_BF16 ? 2 : 1;
+  uint64_t n = e.dtype == DT_BF16 ? 2 : e.dtype == DT_F32 ? 4 : 1;
   for (uint32_t s : e.shape) n *= s;
   return n;
 }
@@ -130,14 +155,16 @@ bool check_config(const lfm3_config& c, std::string& err) {
     return bad("rope pairs %d/%d outside [0, 64]", c.rope_pairs_full, c.rope_pairs_sliding);
   if (!(c.rope_theta_full > 1.0) || !(c.rope_theta_sliding > 1.0)) return bad("rope theta must be > 1 (full %g, sliding %g)", c.rope_theta_full, c.rope_theta_sliding);
   if (!(c.norm_eps > 0.f)) return bad("norm_eps must be > 0");
-  auto bits_ok = [](int b) { return b == 4 || b == 6 || b == 8; };
-  if (!bits_ok(c.bits)) return bad("unsupported affine bits %d (4, 6 or 8)", c.bits);
-  if (c.group != 32 && c.group != 64) return bad("unsupported affine group %d (32 or 64)", c.group);
+  auto bits_ok = [](int b) { return b == 4 || b == 6 || b == 8 || b == 16; };
+  if (!bits_ok(c.bits)) return bad("unsupported affine bits %d (4, 6 or 8; 16 for stored bf16)", c.bits);
+  if (c.bits != 16 && c.group != 32 && c.group != 64) return bad("unsupported affine group %d (32 or 64)", c.group);
   if (c.has_embedding != 0 && c.has_embedding != 1) return bad("has_embedding must be 0 or 1");
   if (c.has_embedding) {
     if (!bits_ok(c.embed_bits)) return bad("unsupported embedding bits %d", c.embed_bits);
-    if (c.embed_group != 32 && c.embed_group != 64) return bad("unsupported embedding group %d", c.embed_group);
+    if (c.embed_bits != 16 && c.embed_group != 32 && c.embed_group != 64) return bad("unsupported embedding group %d", c.embed_group);
   }
+  if (c.ffn_format < LFM3_FFN_AS_LINEARS || c.ffn_format > LFM3_FFN_FP8_BLOCK)
+    return bad("unsupported ffn_format %d (0 as the other linears, 1 NVFP4, 2 block-FP8)", c.ffn_format);
   for (int i = 0; i < c.n_layers; ++i)
     if (c.layer_type[i] > LFM3_LAYER_SLIDING) return bad("layer %d has unknown type %d", i, c.layer_type[i]);
   if (c.max_slots < 1) return bad("max_slots %d", c.max_slots);
@@ -166,31 +193,38 @@ struct Layout {
 
 // (N, K) of every prefill GEMM weight, in layer order: the mixer's input and output linears, then
 // w13 and w2.
-std::vector<std::pair<int, int>> gemm_shapes(const lfm3_config& c) {
-  std::vector<std::pair<int, int>> v;
+// (N, K, role) of every prefill GEMM weight, in layer order: the mixer's input and output linears,
+// then w13 and w2.
+struct GemmShape {
+  int n, k, role;
+};
+std::vector<GemmShape> gemm_shapes(const lfm3_config& c) {
+  std::vector<GemmShape> v;
   for (int i = 0; i < c.n_layers; ++i) {
     if (c.layer_type[i] == LFM3_LAYER_CONV) {
-      v.push_back({3 * c.hidden, c.hidden});
-      v.push_back({c.hidden, c.hidden});
+      v.push_back({3 * c.hidden, c.hidden, ROLE_MIXER});
+      v.push_back({c.hidden, c.hidden, ROLE_MIXER});
     } else {
-      v.push_back({qkvg_rows(c), c.hidden});
-      v.push_back({c.hidden, c.n_q_heads * c.head_dim});
+      v.push_back({qkvg_rows(c), c.hidden, ROLE_MIXER});
+      v.push_back({c.hidden, c.n_q_heads * c.head_dim, ROLE_MIXER});
     }
-    v.push_back({2 * c.ffn, c.hidden});
-    v.push_back({c.hidden, c.ffn});
+    v.push_back({2 * c.ffn, c.hidden, ROLE_FFN});
+    v.push_back({c.hidden, c.ffn, ROLE_FFN});
   }
   return v;
 }
 
-// Whether the layers' linears also get the fp16 operand copy for the prefill GEMM: at 6 bits, whose
-// in-loop unpack is the costliest (the copy's 4x weight bytes cost more than the unpack saves at
-// 4 and 8 bits, measured on the 8k prefill).
-bool gemm_f16_copy(const lfm3_config& c) { return c.bits == 6; }
+// Whether a linear's MFMA paths read an fp16 operand copy: always for bf16, NVFP4 and block-FP8
+// (no re-tiled codes), and for affine codes at 6 bits, whose in-loop unpack is the costliest (the
+// copy's 4x weight bytes cost more than the unpack saves at 4 and 8 bits, measured on the 8k
+// prefill). The head never gets one for affine codes (its MFMA path dequantises in the K loop).
+bool gemm_f16_copy(const LinFmt& f) { return f.fmt != FMT_AFFINE || f.bits == 6; }
 
-// codes, (scale, bias) pairs and (layer linears) the fp16 operand copy, each 256-byte aligned
-size_t gemm_w_bytes(int n, int k, int bits, bool f16) {
+// re-tiled codes and (scale, bias) pairs (affine only) and the fp16 operand copy, each 256-byte aligned
+size_t gemm_w_bytes(int n, int k, const LinFmt& f, bool f16) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-  return up(gemm_codes_bytes(n, k, bits)) + up(gemm_sb_bytes(n, k)) + (f16 ? up(gemm_w16_bytes(n, k)) : 0);
+  const size_t codes = f.fmt == FMT_AFFINE ? up(gemm_codes_bytes(n, k, f.bits)) + up(gemm_sb_bytes(n, k)) : 0;
+  return codes + (f16 ? up(gemm_w16_bytes(n, k)) : 0);
 }
 
 Layout make_layout(const lfm3_config& c) {
@@ -241,8 +275,14 @@ Layout make_layout(const lfm3_config& c) {
   L.vpre = take((size_t)c.max_slots * L.conv_slot * 2);
   L.vz = take((size_t)c.max_slots * n_conv * kMaxVerify * H * 2);
   L.gemm_w_bytes = 0;
-  for (const auto& nk : gemm_shapes(c)) L.gemm_w_bytes += gemm_w_bytes(nk.first, nk.second, c.bits, gemm_f16_copy(c));
-  if (c.has_embedding) L.gemm_w_bytes += gemm_w_bytes(c.vocab, c.hidden, c.embed_bits, false);   // the tied head
+  for (const auto& g : gemm_shapes(c)) {
+    const LinFmt f = fmt_of(c, g.role);
+    L.gemm_w_bytes += gemm_w_bytes(g.n, g.k, f, gemm_f16_copy(f));
+  }
+  if (c.has_embedding) {   // the tied head: codes for affine, the fp16 copy otherwise
+    const LinFmt f = fmt_of(c, ROLE_EMBED);
+    L.gemm_w_bytes += gemm_w_bytes(c.vocab, c.hidden, f, f.fmt != FMT_AFFINE);
+  }
   L.gemm_w = take(L.gemm_w_bytes);
   L.total = off;
   return L;
@@ -387,13 +427,16 @@ hipError_t timed(lfm3_ctx* ctx, int kind, double bytes, double flops, F fn) {
   return fn();
 }
 
-double lin_bytes(const QLinear& w) {
-  return (double)w.n * ((double)w.k * w.bits / 8.0 + 4.0 * w.k / w.group);
+// Algorithmic bytes of a weight as stored: codes (or bf16 values) and their scales.
+double stored_bytes(int fmt, double n, double k, int bits, int group) {
+  if (fmt == FMT_BF16) return 2.0 * n * k;
+  if (fmt == FMT_NVFP4) return n * k / 2.0 + n * k / 16.0 + 8.0;
+  if (fmt == FMT_FP8B) return n * k + 4.0 * std::ceil(n / 128.0) * std::ceil(k / 128.0);
+  return n * (k * bits / 8.0 + 4.0 * k / group);
 }
-// the same algorithmic bytes for the re-tiled copy (the quantized weight itself)
-double lin_bytes(const GemmW& w) {
-  return (double)w.n * ((double)w.k * w.bits / 8.0 + 4.0 * w.k / w.group);
-}
+double lin_bytes(const QLinear& w) { return stored_bytes(w.fmt, w.n, w.k, w.bits, w.group); }
+// the same algorithmic bytes for the weight behind a re-tiled or fp16 copy
+double lin_bytes(const GemmW& w) { return stored_bytes(w.fmt, w.n, w.k, w.bits, w.group); }
 
 #define LFM3_TRY(expr)                                                                      \
   do {                                                                                      \
@@ -816,15 +859,34 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
   ctx->ws = (uint8_t*)workspace_dev;
   const lfm3_config& c = *cfg;
   auto bf = [&](const std::string& n) { return (const bf16_t*)(ctx->blob + ent.at(n).offset); };
-  auto lin = [&](const std::string& n, int N, int K, int bits, int group) {
-    QLinear q;
-    q.q = ctx->blob + ent.at(n + ".q").offset;
-    q.scales = bf(n + ".scales");
-    q.biases = bf(n + ".biases");
-    q.n = N; q.k = K; q.bits = bits; q.group = group;
+  bool scales_ok = true;
+  auto lin = [&](const std::string& n, int N, int K, const LinFmt& f) {
+    QLinear q{};
+    q.n = N; q.k = K; q.bits = f.bits; q.group = f.group; q.fmt = f.fmt; q.tscale = 1.f;
+    if (f.fmt == FMT_AFFINE) {
+      q.q = ctx->blob + ent.at(n + ".q").offset;
+      q.scales = bf(n + ".scales");
+      q.biases = bf(n + ".biases");
+    } else if (f.fmt == FMT_BF16) {
+      q.q = ctx->blob + ent.at(n + ".weight").offset;
+    } else if (f.fmt == FMT_NVFP4) {
+      q.q = ctx->blob + ent.at(n + ".fp4").offset;
+      q.bscale = ctx->blob + ent.at(n + ".block_scales").offset;
+      // the tensor scale is applied; the static input scale is admitted but not applied (the
+      // weights are used weight-only: activations keep their own precision)
+      float ts = 0.f;
+      if (hipMemcpy(&ts, ctx->blob + ent.at(n + ".tensor_scale").offset, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+          !(ts > 0.f) || !std::isfinite(ts))
+        scales_ok = false;
+      q.tscale = ts;
+    } else {
+      q.q = ctx->blob + ent.at(n + ".fp8").offset;
+      q.bscale = ctx->blob + ent.at(n + ".block_scales").offset;
+    }
     ctx->lin_by_name[n] = q;
     return q;
   };
+  const LinFmt fm = fmt_of(c, ROLE_MIXER), ff = fmt_of(c, ROLE_FFN);
   int sub[3] = {0, 0, 0};
   for (int i = 0; i < c.n_layers; ++i) {
     const std::string p = "layers." + std::to_string(i) + ".";
@@ -837,37 +899,50 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
     lw.post_ffn = bf(p + "post_ffn_norm");
     if (lw.type == LFM3_LAYER_CONV) {
       lw.conv_kernel = bf(p + "conv.kernel");
-      lw.mix_in = lin(p + "conv.in_proj", 3 * c.hidden, c.hidden, c.bits, c.group);
-      lw.mix_out = lin(p + "conv.out_proj", c.hidden, c.hidden, c.bits, c.group);
+      lw.mix_in = lin(p + "conv.in_proj", 3 * c.hidden, c.hidden, fm);
+      lw.mix_out = lin(p + "conv.out_proj", c.hidden, c.hidden, fm);
     } else {
       lw.q_norm = bf(p + "attn.q_norm");
       lw.k_norm = bf(p + "attn.k_norm");
-      lw.mix_in = lin(p + "attn.qkvg_proj", qkvg_rows(c), c.hidden, c.bits, c.group);
-      lw.mix_out = lin(p + "attn.o_proj", c.hidden, c.n_q_heads * c.head_dim, c.bits, c.group);
+      lw.mix_in = lin(p + "attn.qkvg_proj", qkvg_rows(c), c.hidden, fm);
+      lw.mix_out = lin(p + "attn.o_proj", c.hidden, c.n_q_heads * c.head_dim, fm);
     }
-    lw.w13 = lin(p + "ffn.w13", 2 * c.ffn, c.hidden, c.bits, c.group);
-    lw.w2 = lin(p + "ffn.w2", c.hidden, c.ffn, c.bits, c.group);
+    lw.w13 = lin(p + "ffn.w13", 2 * c.ffn, c.hidden, ff);
+    lw.w2 = lin(p + "ffn.w2", c.hidden, c.ffn, ff);
     ctx->layers.push_back(lw);
   }
-  if (c.has_embedding) ctx->emb = lin("embedding", c.vocab, c.hidden, c.embed_bits, c.embed_group);
+  if (c.has_embedding) ctx->emb = lin("embedding", c.vocab, c.hidden, fmt_of(c, ROLE_EMBED));
+  if (!scales_ok) {
+    delete ctx;
+    g_err = "an NVFP4 tensor scale is not a finite positive number (or cannot be read)";
+    return LFM3_ERR_BLOB;
+  }
   ctx->emb_norm = bf("embedding_norm");
 
   // re-tiled copies of the prefill GEMM weights, in the order gemm_shapes lists them
   {
     size_t goff = L.gemm_w;
     hipError_t e = hipSuccess;
-    // with16: also the fp16 operand copy the prefill GEMM reads (the layers' linears; the head
-    // runs only on the decode paths, which read the codes)
+    // with16: also the fp16 operand copy the MFMA paths read (affine: from the re-tiled codes with
+    // the GEMM's own dequantisation; other formats: straight from the stored weight, which then has
+    // no re-tiled codes)
     auto retile = [&](const QLinear& q, const std::string& name, bool with16) {
       GemmW g{};
       auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-      uint8_t* codes = ctx->at<uint8_t>(goff);
-      uint32_t* sbp = (uint32_t*)(codes + up(gemm_codes_bytes(q.n, q.k, q.bits)));
-      uint32_t* w16 = with16 ? (uint32_t*)((uint8_t*)sbp + up(gemm_sb_bytes(q.n, q.k))) : nullptr;
-      goff += gemm_w_bytes(q.n, q.k, q.bits, with16);
+      const bool affine = q.fmt == FMT_AFFINE;
+      uint8_t* base = ctx->at<uint8_t>(goff);
+      uint8_t* codes = affine ? base : nullptr;
+      uint32_t* sbp = affine ? (uint32_t*)(codes + up(gemm_codes_bytes(q.n, q.k, q.bits))) : nullptr;
+      uint32_t* w16 = with16 ? (affine ? (uint32_t*)((uint8_t*)sbp + up(gemm_sb_bytes(q.n, q.k))) : (uint32_t*)base) : nullptr;
+      goff += gemm_w_bytes(q.n, q.k, LinFmt{q.fmt, q.bits, q.group}, with16);
       g.codes = codes; g.sb = sbp; g.n = q.n; g.k = q.k; g.bits = q.bits; g.group = q.group; g.ntile = (q.n + 31) / 32;
-      if (e == hipSuccess) e = launch_repack_gemm(ctx->stream, q, codes, sbp);
-      if (with16 && e == hipSuccess) e = launch_repack_gemm16(ctx->stream, g, w16);
+      g.fmt = q.fmt;
+      if (affine) {
+        if (e == hipSuccess) e = launch_repack_gemm(ctx->stream, q, codes, sbp);
+        if (with16 && e == hipSuccess) e = launch_repack_gemm16(ctx->stream, g, w16);
+      } else if (e == hipSuccess) {
+        e = launch_make_w16(ctx->stream, q, w16);
+      }
       g.w16 = w16;
       ctx->gemm_by_name[name] = g;
       return g;
@@ -876,14 +951,13 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
       LayerW& lw = ctx->layers[i];
       const std::string p = "layers." + std::to_string(i) + ".";
       const bool conv = lw.type == LFM3_LAYER_CONV;
-      const bool f16 = gemm_f16_copy(c);
-      lw.g_in = retile(lw.mix_in, p + (conv ? "conv.in_proj" : "attn.qkvg_proj"), f16);
-      lw.g_out = retile(lw.mix_out, p + (conv ? "conv.out_proj" : "attn.o_proj"), f16);
-      lw.g13 = retile(lw.w13, p + "ffn.w13", f16);
-      lw.g2 = retile(lw.w2, p + "ffn.w2", f16);
+      lw.g_in = retile(lw.mix_in, p + (conv ? "conv.in_proj" : "attn.qkvg_proj"), gemm_f16_copy(fm));
+      lw.g_out = retile(lw.mix_out, p + (conv ? "conv.out_proj" : "attn.o_proj"), gemm_f16_copy(fm));
+      lw.g13 = retile(lw.w13, p + "ffn.w13", gemm_f16_copy(ff));
+      lw.g2 = retile(lw.w2, p + "ffn.w2", gemm_f16_copy(ff));
     }
     if (c.has_embedding) {
-      ctx->g_emb = retile(ctx->emb, "embedding", false);
+      ctx->g_emb = retile(ctx->emb, "embedding", ctx->emb.fmt != FMT_AFFINE);
       ctx->gemm_by_name.erase("embedding");   // the GEMM hook paths stay off the head
     }
     if (e != hipSuccess || goff != L.gemm_w + L.gemm_w_bytes) {
@@ -1206,7 +1280,10 @@ lfm3_status lfm3_linear(lfm3_ctx* ctx, const char* name, int32_t path, const uin
     if (gt == ctx->gemm_by_name.end()) return ctx->fail(LFM3_ERR_ARG, std::string(name) + " has no GEMM copy (the head is decode-only)");
     GemmArgs g{};
     g.w = gt->second; g.x = x_dev; g.ldx = w.k; g.m = rows;
-    if (path == 6) g.w.w16 = nullptr;   // dequantise the codes in the K loop instead of the fp16 copy
+    if (path == 6) {   // dequantise the codes in the K loop instead of the fp16 copy
+      if (!g.w.codes) return ctx->fail(LFM3_ERR_ARG, std::string(name) + " has no re-tiled codes (stored as bf16, NVFP4 or block-FP8)");
+      g.w.w16 = nullptr;
+    }
     if (path == 3) { g.epi = GEMM_SWIGLU; g.y = (f16_t*)y_dev; g.ldy = w.n / 2; }
     else { g.epi = GEMM_STORE; g.yf = y_dev; g.ldy = w.n; }
     LFM3_TRY(launch_gemm(ctx->stream, g));

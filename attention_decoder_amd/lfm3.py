@@ -32,7 +32,7 @@ class Config(ctypes.Structure):
         "rope_pairs_full", "rope_pairs_sliding", "bits", "group", "embed_bits", "embed_group", "has_embedding",
         "max_slots", "max_ctx", "page_tokens", "max_chunk", "n_pages")] + [
         ("norm_eps", ctypes.c_float), ("rope_theta_full", ctypes.c_double), ("rope_theta_sliding", ctypes.c_double),
-        ("layer_type", ctypes.c_uint8 * MAX_LAYERS)]
+        ("layer_type", ctypes.c_uint8 * MAX_LAYERS), ("ffn_format", ctypes.c_int32)]
 
 
 def config_from_dict(d: dict) -> Config:
@@ -41,6 +41,8 @@ def config_from_dict(d: dict) -> Config:
         if name == "layer_type":
             lt = (ctypes.c_uint8 * MAX_LAYERS)(*([int(v) for v in d["layer_type"]] + [0] * (MAX_LAYERS - len(d["layer_type"]))))
             c.layer_type = lt
+        elif name == "ffn_format":
+            c.ffn_format = int(d.get("ffn_format", 0))
         else:
             setattr(c, name, d[name])
     return c

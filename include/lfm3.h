@@ -62,15 +62,22 @@ enum { LFM3_MAX_LAYERS = 64, LFM3_MAX_BATCH = 64 };
  *   RoPE:      rope_theta_full / rope_pairs_full (1e6, 32 of 64 pairs rotate: partial, zero tail);
  *              rope_theta_sliding / rope_pairs_sliding (1e4, all 64 pairs)
  *   norms:     norm_eps (1e-5)
- *   weights:   bits in {4, 6, 8}, group in {32, 64} for every linear; embed_bits / embed_group for
- *              the tied embedding and head; has_embedding = 0 runs without embedding and head
- *              (rows enter as hidden states, the output is the final normed hidden state)
+ *   weights:   bits in {4, 6, 8}, group in {32, 64} for every linear (MLX affine), or bits 16 for
+ *              linears stored as bf16 (group ignored); embed_bits / embed_group the same for the
+ *              tied embedding and head; has_embedding = 0 runs without embedding and head (rows
+ *              enter as hidden states, the output is the final normed hidden state);
+ *              ffn_format: LFM3_FFN_AS_LINEARS (w13 and w2 as bits / group say),
+ *              LFM3_FFN_NVFP4 (the FFN as e2m1 codes in groups of 16 with e4m3 block scales and an
+ *              fp32 tensor scale, weight-only: the static input scale is admitted, not applied --
+ *              "TensorFold PR #1508", the layout of the NVFP4 export, whose other linears are
+ *              bf16) or LFM3_FFN_FP8_BLOCK (e4m3 codes with one fp32 scale per 128 x 128 block)
  *   runtime:   max_slots streams, max_ctx positions per slot, page_tokens positions per KV page
  *              (16), max_chunk rows per prefill pass, n_pages pages in the full-attention pool
  * This build runs head_dim 128, n_q_heads = 4 * n_kv_heads, conv_taps <= 8, page_tokens 16,
  * hidden (<= 4096) and ffn multiples of 512, max_ctx <= 65536; anything else is refused with
  * LFM3_ERR_CONFIG.
  */
+enum { LFM3_FFN_AS_LINEARS = 0, LFM3_FFN_NVFP4 = 1, LFM3_FFN_FP8_BLOCK = 2 };
 typedef struct lfm3_config {
   int32_t n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, vocab, conv_taps, window;
   int32_t rope_pairs_full, rope_pairs_sliding;
@@ -79,6 +86,7 @@ typedef struct lfm3_config {
   float norm_eps;
   double rope_theta_full, rope_theta_sliding;
   uint8_t layer_type[LFM3_MAX_LAYERS];
+  int32_t ffn_format;
 } lfm3_config;
 
 typedef struct lfm3_ctx lfm3_ctx;

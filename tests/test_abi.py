@@ -19,9 +19,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_config_struct_layout_matches_header():
-    # 21 int32 + float = 88 bytes, two doubles, 64 layer bytes
-    assert ctypes.sizeof(lfm3.Config) == 88 + 16 + 64
+    # 21 int32 + float = 88 bytes, two doubles, 64 layer bytes, then ffn_format
+    assert ctypes.sizeof(lfm3.Config) == 88 + 16 + 64 + 4 + 4   # + tail padding to the doubles' alignment
     assert lfm3.Config.rope_theta_full.offset == 88
+    assert lfm3.Config.ffn_format.offset == 88 + 16 + 64
 
 
 def test_query_sizes_full_geometry():
@@ -99,3 +100,29 @@ def test_binding_has_no_fallback(tmp_path, monkeypatch):
     monkeypatch.setattr(lfm3, "_lib", None)
     with pytest.raises(OSError):
         lfm3.load_library(str(tmp_path / "missing.so"))
+
+
+@pytest.mark.parametrize("ffn_format", [1, 2])
+def test_nvfp4_and_fp8_layouts_admitted(ffn_format):
+    """The NVFP4 export's layout (FFN in fp4 with e4m3 block scales and fp32 tensor / input scales,
+    everything else bf16) and the block-FP8 FFN: the host admission accepts the seeded blobs of
+    the three-layer slice and names a missing scale."""
+    cfg = synth.make_config(layer_types=[0, 2, 1], bits=16, group=0, embed_bits=16, embed_group=0,
+                            ffn_format=ffn_format, max_slots=1, max_ctx=128, max_chunk=64)
+    cfg["vocab"] = 256
+    blob = synth.cached_blob(cfg, seed=0)
+    c = lfm3.config_from_dict(cfg)
+    assert lfm3.lfm3_query_sizes(c)[0] == len(blob)
+    st, msg = lfm3.lfm3_validate_blob(c, blob)
+    assert st == 0, msg
+    name = "layers.0.ffn.w2.block_scales"
+    st, msg = lfm3.lfm3_validate_blob(c, _corrupt_entry(blob, name, 0, "<20s", b"layers.0.ffn.w2.nope"))
+    assert st == 3 and "block_scales" in msg
+
+
+def test_ffn_format_refused_by_name():
+    cfg = synth.full_config()
+    cfg["ffn_format"] = 3
+    with pytest.raises(lfm3.LFM3Error) as ei:
+        lfm3.lfm3_query_sizes(lfm3.config_from_dict(cfg))
+    assert ei.value.status == 2 and "ffn_format 3" in ei.value.message
