@@ -743,13 +743,15 @@ static hipError_t launch_sg_bits(hipStream_t s, const GemmW& w, const GemvArgs& 
 
 hipError_t launch_sgemm(hipStream_t s, const GemmW& w, const GemvArgs& g) {
   const int meff = g.x_lo ? 2 * g.batch : g.batch;
-  if (g.batch < 1 || meff > 64 || w.k % (4 * BK) || (!w.w16 && w.group % 32) || g.ldx % 8 || (uintptr_t)g.x % 16 ||
+  if (g.batch < 1 || meff > 64 || w.k % (4 * BK) || (w.codes && w.group % 32) || g.ldx % 8 || (uintptr_t)g.x % 16 ||
       (uintptr_t)g.x_lo % 16 || w.ntile != (w.n + 31) / 32 ||
       (g.epi == GEMV_SWIGLU && w.n % 64) || (g.epi == GEMV_CONV && ((w.n / 3) % 32 || w.n % 3 || g.conv_taps < 2 ||
                                                                   g.conv_taps > kMaxTaps)))
     return hipErrorInvalidValue;
-  if (w.w16) {
-    if ((size_t)w.ntile * (w.k / BK) * 4096u > 0xffffffffull) return hipErrorInvalidValue;
+  // the fp16 copy only where there are no codes (bf16, NVFP4, block-FP8): decode reads the fewest
+  // bytes from the codes
+  if (!w.codes) {
+    if (!w.w16 || (size_t)w.ntile * (w.k / BK) * 4096u > 0xffffffffull) return hipErrorInvalidValue;
     return launch_sg_bits<16>(s, w, g, meff);
   }
   switch (w.bits) {

@@ -218,7 +218,10 @@ std::vector<GemmShape> gemm_shapes(const lfm3_config& c) {
 // (no re-tiled codes), and for affine codes at 6 bits, whose in-loop unpack is the costliest (the
 // copy's 4x weight bytes cost more than the unpack saves at 4 and 8 bits, measured on the 8k
 // prefill). The head never gets one for affine codes (its MFMA path dequantises in the K loop).
-bool gemm_f16_copy(const LinFmt& f) { return f.fmt != FMT_AFFINE || f.bits == 6; }
+bool gemm_f16_copy(const LinFmt& f, int n) {
+  (void)n;
+  return f.fmt != FMT_AFFINE || f.bits == 6;
+}
 
 // re-tiled codes and (scale, bias) pairs (affine only) and the fp16 operand copy, each 256-byte aligned
 size_t gemm_w_bytes(int n, int k, const LinFmt& f, bool f16) {
@@ -277,7 +280,7 @@ Layout make_layout(const lfm3_config& c) {
   L.gemm_w_bytes = 0;
   for (const auto& g : gemm_shapes(c)) {
     const LinFmt f = fmt_of(c, g.role);
-    L.gemm_w_bytes += gemm_w_bytes(g.n, g.k, f, gemm_f16_copy(f));
+    L.gemm_w_bytes += gemm_w_bytes(g.n, g.k, f, gemm_f16_copy(f, g.n));
   }
   if (c.has_embedding) {   // the tied head: codes for affine, the fp16 copy otherwise
     const LinFmt f = fmt_of(c, ROLE_EMBED);
@@ -506,7 +509,9 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
     const LayerW& lw = ctx->layers[i];
     // h += post_ffn_norm(m) of the previous layer (if any); x = operator_norm(h)
     NormArgs na{};
-    na.h_in = h; na.h_out = h; na.x_out = x; na.x_lo = xlo; na.rows = M; na.hidden = H; na.eps = c.norm_eps;
+    // the conv layers' operator-norm output is carried as an fp16 pair (x, x_lo) into in_proj
+    na.h_in = h; na.h_out = h; na.x_out = x; na.x_lo = lw.type == LFM3_LAYER_CONV ? xlo : nullptr;
+    na.rows = M; na.hidden = H; na.eps = c.norm_eps;
     na.w_pre = lw.op_norm;
     if (i > 0) { na.m = m; na.m2 = m2; na.w_post = ctx->layers[i - 1].post_ffn; na.capture = cap(i - 1); }
     LFM3_TRY(timed(ctx, LFM3_PROF_NORM, norm_bytes, 0, [&] { return launch_resid_norm(s, na); }));
@@ -522,7 +527,7 @@ lfm3_status run_layers(lfm3_ctx* ctx, const Rows& rows, int capture_row0, float*
       LFM3_TRY(timed(ctx, LFM3_PROF_CONV, (double)M * H * (12 + 2) + 2.0 * H * 2 * (c.conv_taps - 1), 0,
                      [&] { return launch_conv(s, ca); }));
     } else {
-      LFM3_TRY(linear(lw.g_in, x, H, big, nullptr, L.big_ld, GEMM_STORE, xlo));
+      LFM3_TRY(linear(lw.g_in, x, H, big, nullptr, L.big_ld, GEMM_STORE));
       const bool full = lw.type == LFM3_LAYER_FULL;
       QkRopeArgs qa{};
       qa.qkvg = big; qa.ld = L.big_ld; qa.q_norm = lw.q_norm; qa.k_norm = lw.k_norm;
@@ -605,8 +610,8 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     return timed(ctx, LFM3_PROF_GEMV, gemv_bytes(g.w, out_bytes), fl, [&] { return launch_gemv(s, g); });
   };
   // GEMV whose input is rmsnorm(cur [+ rmsnorm(m) * w_post]) * w_pre
-  // split: the normed input is carried as the fp16 pair x + x_lo (the operator-norm output, which
-  // feeds in_proj and qkvg); a fused split prologue handles one row
+  // split: the normed input is carried as the fp16 pair x + x_lo (the conv layers' operator-norm
+  // output, which feeds in_proj); a fused split prologue handles one row
   auto normed_gemv = [&](GemvArgs& g, const bf16_t* w_post, const bf16_t* w_pre, float* capture, float* x_copy,
                          double out_bytes, bool split = false, const GemmW* gw = nullptr) -> hipError_t {
     g.batch = M;
@@ -646,7 +651,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     } else {
       GemvArgs g{};
       g.w = lw.mix_in; g.epi = GEMV_STORE; g.yf = big; g.ldy = L.big_ld;
-      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4, true, &lw.g_in));
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4, false, &lw.g_in));
       const bool full = lw.type == LFM3_LAYER_FULL;
       AttnDecodeArgs aa{};
       aa.qkvg = big; aa.ld = L.big_ld; aa.gate_col = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
@@ -951,10 +956,10 @@ lfm3_status lfm3_create(const lfm3_config* cfg, const void* blob_dev, size_t blo
       LayerW& lw = ctx->layers[i];
       const std::string p = "layers." + std::to_string(i) + ".";
       const bool conv = lw.type == LFM3_LAYER_CONV;
-      lw.g_in = retile(lw.mix_in, p + (conv ? "conv.in_proj" : "attn.qkvg_proj"), gemm_f16_copy(fm));
-      lw.g_out = retile(lw.mix_out, p + (conv ? "conv.out_proj" : "attn.o_proj"), gemm_f16_copy(fm));
-      lw.g13 = retile(lw.w13, p + "ffn.w13", gemm_f16_copy(ff));
-      lw.g2 = retile(lw.w2, p + "ffn.w2", gemm_f16_copy(ff));
+      lw.g_in = retile(lw.mix_in, p + (conv ? "conv.in_proj" : "attn.qkvg_proj"), gemm_f16_copy(fm, lw.mix_in.n));
+      lw.g_out = retile(lw.mix_out, p + (conv ? "conv.out_proj" : "attn.o_proj"), gemm_f16_copy(fm, lw.mix_out.n));
+      lw.g13 = retile(lw.w13, p + "ffn.w13", gemm_f16_copy(ff, lw.w13.n));
+      lw.g2 = retile(lw.w2, p + "ffn.w2", gemm_f16_copy(ff, lw.w2.n));
     }
     if (c.has_embedding) {
       ctx->g_emb = retile(ctx->emb, "embedding", ctx->emb.fmt != FMT_AFFINE);

@@ -403,8 +403,8 @@ class Oracle:
         return bf16_round(x) if self.storage == "bf16" else f16_round(x)
 
     def _r2(self, x):
-        """Storage diagnostic for the operator-norm output feeding in_proj and qkvg: one rounding,
-        or in "fp16_pair" mode the high part plus its rounded remainder."""
+        """Storage diagnostic for the conv layers' operator-norm output, which feeds in_proj: one
+        rounding, or in "fp16_pair" mode the high part plus its rounded remainder."""
         if self.storage != "fp16_pair":
             return self._r(x)
         hi = f16_round(x)
@@ -470,7 +470,8 @@ class Oracle:
         pos = np.arange(st.length, st.length + m)
         layers = []
         for i, lt in enumerate(c["layer_type"]):
-            u = self._r2(rmsnorm(h, self.blob.bf16(f"layers.{i}.operator_norm"), eps))
+            u = rmsnorm(h, self.blob.bf16(f"layers.{i}.operator_norm"), eps)
+            u = self._r2(u) if lt == LT_CONV else self._r(u)
             if lt == LT_CONV:
                 mo = self._conv_mixer(i, st, u)
             else:
