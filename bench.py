@@ -6,8 +6,9 @@ g64 weights -- a step is one whole job: a 2048-token prompt prefilled in one 204
 carries the 2048-token prefill rate, the 8-stream decode, the 8192-token prefill (warm, and the
 first pass of a fresh context) and the other weight schemes (extras), the roofline figure of the
 dominant kernel (the dequant-GEMV: algorithmic bytes per launch over its event-timed launch
-duration, with the HBM bytes of the committed counter record) and the float64 oracle timed on the
-host cores (cpu_baseline). --profile-only, --profile-8stream and --profile-prefill run one short
+duration, with the HBM bytes of the committed counter record), the prefill's MfmaUtil from the
+committed counter record, the NVFP4 layout's decode and prefill, and the float64 oracle timed on
+the host cores (cpu_baseline). --profile-only, --profile-8stream and --profile-prefill run one short
 job each for profiler runs.
 
 Inputs are seeded and synthetic (random-init weights quantized from N(0, 0.02), token ids uniform
@@ -202,6 +203,23 @@ def main():
     eng.close()
 
 
+def committed_record(name):
+    """A committed profiles/ record, or None when the kernel sources it was measured on have
+    changed since (its source_sha256 over its source_files)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for p in rec["source_files"]:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec if h.hexdigest() == rec.get("source_sha256") else None
+
+
 def gemv_traffic():
     """HBM bytes per decode GEMV launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE record
     (each counter scaled by a 256 MiB device copy of known size), or None when the kernel sources
@@ -317,6 +335,9 @@ def run_extras(eng, synth, torch, dev, schemes=True):
     total_flops = g["flops"] + a["flops"] + 2.0 * 128000 * 2048     # + the last row's tied head
     out["prefill_8k_flops_algorithmic"] = total_flops
     out["prefill_8k_frac_of_f16_peak"] = round(total_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+    mf = committed_record("prefill_8k_q4g64_mfma.json")
+    out["prefill_8k_mfma_util_pct_profile"] = (
+        {"gemm": mf["gemm_time_weighted_pct"], "attn_prefill": mf["attn_prefill_time_weighted_pct"]} if mf else None)
     log(f"8k prefill {out['prefill_8k_tok_s']} tok/s ({ms:.2f} ms); {out['prefill_8k_breakdown_ms']}")
     out["prefill_8k_cold_ttft_ms"] = round(cold_prefill_8k(synth, torch, dev), 3)
     log(f"8k prefill, first pass of a fresh context: {out['prefill_8k_cold_ttft_ms']} ms")
@@ -333,6 +354,39 @@ def run_extras(eng, synth, torch, dev, schemes=True):
                 log(f"q6 8k prefill {out['q6_prefill_8k_tok_s']} tok/s ({ms6:.2f} ms)")
             e2.close()
         out.update(cfg5_extras(synth, torch, dev))
+        out.update(nvfp4_extras(synth, torch, dev))
+    return out
+
+
+def nvfp4_extras(synth, torch, dev):
+    """The NVFP4 export's layout (FFN NVFP4, mixers / embedding / head bf16): B = 1 decode on the
+    headline job's shape (2048-token prompt, 128 greedy steps), the 8-stream decode and the 8k
+    prefill."""
+    from attention_decoder_amd.lfm3 import Engine
+    out = {}
+    cfg = synth.nvfp4_config(max_slots=8, max_ctx=8704, max_chunk=2048)
+    eng = Engine(cfg, synth.cached_blob(cfg, seed=0))
+    prompt = torch.from_numpy(synth.prompt_tokens(2, 2048)).to(dev)
+    ids = torch.empty((129,), dtype=torch.int32, device=dev)
+    best = 0.0
+    for _ in range(2):
+        eng.reset(0)
+        o = eng.prefill(0, tokens=prompt, logits=False, argmax=True)
+        ids[0:1].copy_(o["argmax"])
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(eng.stream)
+        for t in range(128):
+            eng.decode([0], tokens=ids[t:t + 1], logits=False, argmax=True, out={"argmax": ids[t + 1:t + 2]})
+        b.record(eng.stream)
+        torch.cuda.synchronize()
+        best = max(best, 128 / (a.elapsed_time(b) / 1e3))
+    out["nvfp4_decode_b1_tok_s"] = round(best, 1)
+    out["nvfp4_decode_8stream_tok_s"], _, _ = decode_8stream(eng, synth, torch, dev)
+    out["nvfp4_prefill_8k_tok_s"], _, _ = prefill_8k(eng, synth, torch, dev)
+    log(f"NVFP4 layout: decode {out['nvfp4_decode_b1_tok_s']} tok/s at B = 1, {out['nvfp4_decode_8stream_tok_s']} at 8 "
+        f"streams, 8k prefill {out['nvfp4_prefill_8k_tok_s']} tok/s")
+    eng.close()
     return out
 
 
