@@ -115,13 +115,16 @@ LFM3_DEV float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // Rows handled together by one wave: 8 for STORE / LOGITS, 4 gate + the 4 matching up rows for
-// SWIGLU, B, C and x rows of 2 channels (6, reduced as 8 with two zero rows) for the conv epilogue.
+// SWIGLU, B, C and x rows of 2 channels (6, reduced as 8 with two zero rows) for the conv epilogue,
+// 2 for STORE2 (outputs too narrow to give every CU a block at 8 rows a wave: out_proj, o_proj and
+// qkvg at 2048-3104 rows run 4x the waves, each with a quarter of the dot products).
 constexpr int kRG = 8;
-template <int EPI> struct RowsPerGroup { static constexpr int v = EPI == GEMV_CONV ? 6 : 8; };
+template <int EPI> struct RowsPerGroup { static constexpr int v = EPI == GEMV_CONV ? 6 : EPI == GEMV_STORE2 ? 2 : 8; };
 
 template <int EPI> LFM3_HOST_DEV int n_groups_of(int N) {
   if (EPI == GEMV_SWIGLU) return N / 8;
   if (EPI == GEMV_CONV) return N / 6;
+  if (EPI == GEMV_STORE2) return (N + 1) / 2;
   return (N + 7) / 8;
 }
 
@@ -134,6 +137,9 @@ template <int EPI> LFM3_DEV void rows_of(int g, int N, int (&rows)[RowsPerGroup<
     const int third = N / 3;
 #pragma unroll
     for (int j = 0; j < 3; ++j) { rows[2 * j] = j * third + 2 * g; rows[2 * j + 1] = j * third + 2 * g + 1; }
+  } else if constexpr (EPI == GEMV_STORE2) {
+    rows[0] = 2 * g;
+    rows[1] = min(2 * g + 1, N - 1);
   } else {
 #pragma unroll
     for (int r = 0; r < 8; ++r) rows[r] = min(8 * g + r, N - 1);
@@ -164,6 +170,15 @@ LFM3_DEV float bfly8(const float (&in)[8]) {
   t += dpp_mov<0x4e>(t);
   t += dpp_mov<0x141>(t);                 // row_half_mirror: lane i <-> 7 - i
   return t;
+}
+
+// The same for 2 values: lanes 32r .. 32r+31 end with the total of value r (halves swapped by
+// permlane32, 16-lane rows by permlane16, then the DPP row sum).
+LFM3_DEV float bfly2(float a0, float a1) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+  const float v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return row16_sum(__uint_as_float(q[0]) + __uint_as_float(q[1]));
 }
 
 // Stage the fp16 input rows in LDS in chunk pair order with per-chunk sums of the staged values.
@@ -406,6 +421,7 @@ template <int BITS, int BT, int EPI, int PRO, int KW>
 __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
   using Q = QT<BITS>;
   constexpr int RG = RowsPerGroup<EPI>::v;
+  static_assert(EPI != GEMV_STORE2 || KW == 1, "2-row groups are for rows of one wave");
   extern __shared__ uint32_t smem[];
   __shared__ float red[8 * BT];
   __shared__ uint64_t wkeys[EPI == GEMV_LOGITS ? 4 * BT : 1];
@@ -649,14 +665,18 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
     }
     if (sw != NITW - 1) return;
     const int g = g0 + gi * gstride;
-    // t[b]: lanes 8r .. 8r+7 hold the total of row r of the group
+    // t[b]: lanes 8r .. 8r+7 (2-row groups: 32r .. 32r+31) hold the total of row r of the group
     float t[BT];
 #pragma unroll
     for (int b = 0; b < BT; ++b) {
-      float v8[8];
+      if constexpr (RG == 2) {
+        t[b] = bfly2(acc[0][b], acc[1][b]);
+      } else {
+        float v8[8];
 #pragma unroll
-      for (int r = 0; r < kRG; ++r) v8[r] = acc[r][b];
-      t[b] = bfly8(v8);
+        for (int r = 0; r < kRG; ++r) v8[r] = acc[r][b];
+        t[b] = bfly8(v8);
+      }
     }
 #pragma unroll
     for (int r = 0; r < kRG; ++r)
@@ -694,6 +714,12 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
 #pragma unroll
         for (int b = 0; b < BT; ++b)
           if (b < a.batch) a.yf[(size_t)b * a.ldy + 8 * g + r] = t[b];
+    } else if constexpr (EPI == GEMV_STORE2) {
+      const int n = 2 * g + (lane >> 5);
+      if ((lane & 31) == 0 && n < N)
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+          if (b < a.batch) a.yf[(size_t)b * a.ldy + n] = t[b];
     } else if constexpr (EPI == GEMV_SWIGLU) {
       // silu(a) * b is rounded to fp32, then to fp16, in every batch-size instance, so a row's
       // result does not depend on the batch it is decoded in
@@ -794,14 +820,20 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
 #endif
 
 template <int BITS, int BT, int PRO, int KW>
-static void launch_epi(hipStream_t s, const GemvArgs& a, int grid, size_t lds) {
+static void launch_epi(hipStream_t s, const GemvArgs& a, int epi, int grid, size_t lds) {
+  if constexpr (KW == 1) {
+    if (epi == GEMV_STORE2) {
+      hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE2, PRO, KW>), dim3(grid), dim3(256), lds, s, a);
+      return;
+    }
+  }
   if constexpr (BITS == 41 || BITS == 48) {
     // the FFN formats: w13 with the SwiGLU epilogue, w2 plain (the caller refuses other epilogues)
-    if (a.epi == GEMV_SWIGLU) hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_SWIGLU, PRO, KW>), dim3(grid), dim3(256), lds, s, a);
+    if (epi == GEMV_SWIGLU) hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_SWIGLU, PRO, KW>), dim3(grid), dim3(256), lds, s, a);
     else hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, PRO, KW>), dim3(grid), dim3(256), lds, s, a);
     return;
   }
-  switch (a.epi) {
+  switch (epi) {
     case GEMV_STORE: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
     case GEMV_SWIGLU: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_SWIGLU, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
     case GEMV_CONV: hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_CONV, PRO, KW>), dim3(grid), dim3(256), lds, s, a); break;
@@ -815,8 +847,9 @@ static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
   const int K = a.w.k;
   const size_t lds = (size_t)BT * K * 2 + (size_t)BT * (K / Q::CH) * sizeof(float2);
   const int N = a.w.n;
-  const int n_groups = a.epi == GEMV_SWIGLU ? n_groups_of<GEMV_SWIGLU>(N)
-                       : a.epi == GEMV_CONV ? n_groups_of<GEMV_CONV>(N) : n_groups_of<GEMV_STORE>(N);
+  int epi = a.epi;
+  int n_groups = epi == GEMV_SWIGLU ? n_groups_of<GEMV_SWIGLU>(N)
+                 : epi == GEMV_CONV ? n_groups_of<GEMV_CONV>(N) : n_groups_of<GEMV_STORE>(N);
   // Long rows (4 or more k iterations of 64 chunks) are shared by the 4 waves of a block, so that
   // narrow matrices still spread over the whole chip.
   const int nit = (K / Q::CH + 63) / 64;
@@ -824,14 +857,19 @@ static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
   // a block per 4 row groups (one per wave), or per group when its 4 waves share the group's K
   // range, at most one block per CU; the head (147 MB at 4 bits, bandwidth-bound) takes two blocks
   // per CU for more loads in flight. Waves with more groups than one walk them in steps.
-  const int cap = a.max_blocks > 0 ? a.max_blocks : (a.epi == GEMV_LOGITS ? 2 * LFM3_GEMV_MAX_BLOCKS : LFM3_GEMV_MAX_BLOCKS);
+  const int cap = a.max_blocks > 0 ? a.max_blocks : (epi == GEMV_LOGITS ? 2 * LFM3_GEMV_MAX_BLOCKS : LFM3_GEMV_MAX_BLOCKS);
+  // plain outputs whose 8-row groups would leave CUs without a block take 2-row groups
+  if (epi == GEMV_STORE && !split && (n_groups + 3) / 4 < cap) {
+    epi = GEMV_STORE2;
+    n_groups = n_groups_of<GEMV_STORE2>(N);
+  }
   int grid = split ? n_groups : (n_groups + 3) / 4;
   if (grid > cap) grid = cap;
   if (a.epi == GEMV_LOGITS && grid > kArgmaxParts) return hipErrorInvalidValue;
   if (a.h_src) {
     if constexpr (BT <= 2) {
-      if (split) launch_epi<BITS, BT, 1, 4>(s, a, grid, lds);
-      else launch_epi<BITS, BT, 1, 1>(s, a, grid, lds);
+      if (split) launch_epi<BITS, BT, 1, 4>(s, a, epi, grid, lds);
+      else launch_epi<BITS, BT, 1, 1>(s, a, epi, grid, lds);
     } else {
       return hipErrorInvalidValue;
     }
@@ -839,13 +877,14 @@ static hipError_t launch_bt(hipStream_t s, const GemvArgs& a) {
     if constexpr (BT <= 2) {
       if (a.epi != GEMV_STORE) return hipErrorInvalidValue;
       if (split) hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, 2, 4>), dim3(grid), dim3(256), lds, s, a);
+      else if (epi == GEMV_STORE2) hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE2, 2, 1>), dim3(grid), dim3(256), lds, s, a);
       else hipLaunchKernelGGL((k_gemv<BITS, BT, GEMV_STORE, 2, 1>), dim3(grid), dim3(256), lds, s, a);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
-    if (split) launch_epi<BITS, BT, 0, 4>(s, a, grid, lds);
-    else launch_epi<BITS, BT, 0, 1>(s, a, grid, lds);
+    if (split) launch_epi<BITS, BT, 0, 4>(s, a, epi, grid, lds);
+    else launch_epi<BITS, BT, 0, 1>(s, a, epi, grid, lds);
   }
   return hipGetLastError();
 }
@@ -890,6 +929,7 @@ static hipError_t launch_bits(hipStream_t s, const GemvArgs& a) {
 
 hipError_t launch_gemv(hipStream_t s, const GemvArgs& a) {
   if (a.batch <= 0) return hipSuccess;
+  if (a.epi < GEMV_STORE || a.epi > GEMV_CONV) return hipErrorInvalidValue;   // STORE2 is picked here, not asked for
   // attention-merge input: one vector block per thread, whole heads, 1-2 rows of at most
   // kFusedMergeSplits splits, plain STORE
   if (a.part) {

@@ -97,7 +97,8 @@ hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int ro
 
 // ---- k_gemv.hip --------------------------------------------------------------------------------
 
-enum GemvEpi { GEMV_STORE = 0, GEMV_SWIGLU = 1, GEMV_LOGITS = 2, GEMV_CONV = 3 };
+enum GemvEpi { GEMV_STORE = 0, GEMV_SWIGLU = 1, GEMV_LOGITS = 2, GEMV_CONV = 3,
+               GEMV_STORE2 = 4 };   // STORE in 2-row groups: chosen by launch_gemv itself for narrow outputs
 // y[b, n] = sum_k x[b, k] * (q[n, k] * s + bias) for b < batch (<= 8), exact weights (the per-group
 // factored form). STORE: fp32 yf [batch, ldy]. SWIGLU: rows n and n + N/2 -> fp16 silu(a) * b in
 // y. LOGITS: fp32 logits (nullable) + per-block argmax partials (keys, kArgmaxParts per row). CONV (in_proj, N = 3H): the
