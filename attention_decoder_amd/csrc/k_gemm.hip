@@ -745,13 +745,17 @@ static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, in
 
 // Up to 32 operand rows: 8 waves per block (the partial tiles of 8 waves fit in LDS); the head keeps
 // 4 (its argmax slots are laid out for 256 threads).
-// 8 waves per block for the conv in_proj (one block per 32 channels: 64 blocks, each with a long
-// K walk), 4 for the rest (measured: 8 waves elsewhere lost), and 4 when the block's K range has
-// fewer than 8 tiles (every wave needs one). The wave count depends on the weight shape and
-// epilogue alone, never on the row count, so a row's sums do not depend on its batch.
+// 8 waves per block for the conv in_proj at 4 and 6 bits (one block per 32 channels: 64 blocks,
+// each with a long K walk), 4 for the rest (measured: 8 waves elsewhere lost), and 4 when the
+// block's K range has fewer than 8 tiles (every wave needs one). At 8 bits and from the fp16 copy
+// the conv in_proj keeps 4 waves: three tiles' operands in four register sets exceed the 256
+// registers a lane of a 512-thread block has, and the spilled 8-wave form returned wrong sums from
+// the fp16 copy (the NVFP4 export's bf16 in_proj at 8 rows), while every form without spills
+// matches the oracle. The wave count depends on the weight shape and epilogue alone, never on the
+// row count, so a row's sums do not depend on its batch.
 template <int BITS, int EPI>
 static hipError_t launch_sg_epi(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int meff, int ksplit = 1) {
-  constexpr int W1 = EPI == GEMV_CONV ? 8 : 4;
+  constexpr int W1 = (EPI == GEMV_CONV && BITS != 8 && BITS != 16) ? 8 : 4;
   const int nkb = (w.k / BK) / ksplit;
   if (nkb < 4) return hipErrorInvalidValue;
   if (nkb < W1) return meff <= 32 ? launch_sg<BITS, EPI, 1, 4>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2, 4>(s, w, g, blocks, ksplit);

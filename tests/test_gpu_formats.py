@@ -138,6 +138,27 @@ def test_slice_layers_against_oracle(fmt_engine):
     assert d <= 2e-2
 
 
+def test_slice_batch8_decode_against_oracle(fmt_engine):
+    """Eight slots decoded in one step (the decode MFMA GEMM from the fp16 copies: the conv
+    in_proj with its input pair, the split output projections, SwiGLU and the head): each row's
+    logits against the oracle's decode of that slot alone."""
+    import torch
+    cfg, blob, eng, orc = fmt_engine
+    prompts = [synth.prompt_tokens(70 + i, 10 + 7 * i, vocab=1024) for i in range(8)]
+    for i in range(8):
+        eng.reset(i)
+        eng.prefill(i, tokens=dev_tokens(torch, prompts[i]), logits=False, argmax=False)
+    step = [int(t) for t in synth.prompt_tokens(80, 8, vocab=1024)]
+    o = eng.decode(list(range(8)), tokens=dev_tokens(torch, step), logits=True, argmax=True)
+    got = o["logits"].cpu().numpy().astype(np.float64)
+    for i in range(8):
+        st = orc.new_slot()
+        orc.forward(st, tokens=prompts[i], logits=None)
+        want = orc.forward(st, tokens=[step[i]], logits="last")["logits"][0]
+        d = np.abs(got[i] - want).max()
+        assert d <= 2e-2, (i, d)
+
+
 def test_nvfp4_full_geometry():
     """The NVFP4 export's layout at the full geometry: a 300-token prompt and 4 greedy steps at
     batch 1, then one batch-8 step, against the oracle."""
