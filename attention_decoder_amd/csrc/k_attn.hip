@@ -44,6 +44,11 @@ constexpr int PTILE = PKT * kHeadDim;        // elements of one K or V tile
 constexpr int kAttnPrefillLds = 8 * PTILE * 2;   // per key half: two K and two V buffers (bytes)
 
 LFM3_DEV int swz(int r, int c) { return r * kHeadDim + 8 * (c ^ (r & 15)); }   // element offset
+// The V tile's swizzle: chunk c of row r at c ^ 4 (r mod 4) ^ 2 ((r / 8) mod 2). A transpose read
+// of a wave covers rows R .. R+3 and R+8 .. R+11 (R a multiple of 8) and 4 chunks of them; with this
+// swizzle each half-wave's 32 lanes read 32 different 8-byte bank pairs (with the K swizzle rows R
+// and R+1 shared their chunks: 4-way conflicts, 6 cycles a read, measured with SQ_LDS_BANK_CONFLICT).
+LFM3_DEV int swzv(int r, int c) { return r * kHeadDim + 8 * (c ^ (4 * (r & 3)) ^ (2 * ((r >> 3) & 1))); }
 
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
@@ -110,9 +115,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_prefill(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = tid + 256 * i;
-      const int e = swz(u >> 4, u & 15);
-      *(u32x4_v*)(Ks + buf * PTILE + e) = kr[i];
-      *(u32x4_v*)(Vs + buf * PTILE + e) = vr[i];
+      *(u32x4_v*)(Ks + buf * PTILE + swz(u >> 4, u & 15)) = kr[i];
+      *(u32x4_v*)(Vs + buf * PTILE + swzv(u >> 4, u & 15)) = vr[i];
     }
   };
 
@@ -198,8 +202,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_prefill(AttnArgs a) {
         for (int d = 0; d < 4; ++d) {
           const int c = 4 * d + 2 * (tg & 1) + (tq >> 1);
           const int half = 4 * (tq & 1);
-          const s16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + swz(kr, c) + half));
-          const s16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + swz(kr + 4, c) + half));
+          const s16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + swzv(kr, c) + half));
+          const s16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + swzv(kr + 4, c) + half));
           const f16x8_v vt = __builtin_bit_cast(f16x8_v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt, pv[sub][t2], o[d], 0, 0, 0);
         }
