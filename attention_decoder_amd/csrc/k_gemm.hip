@@ -461,20 +461,20 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode linears at 3 .. 32 rows ("skinny" MFMA GEMM). One block per 32-row weight tile (SwiGLU:
-// the gate tile and its up tile; the conv in_proj: the B, C and x tiles of 32 channels); the four
-// waves take every fourth K tile (with the loads of the next 2-4 of them in flight), each
-// accumulating MT x NT MFMA tiles over all input rows
+// Decode linears at 3 .. 64 operand rows ("skinny" MFMA GEMM). One block per 32-row weight tile
+// (SwiGLU: the gate tile and its up tile); the four waves take every fourth K tile (with the loads
+// of the next 2-4 of them in flight), each accumulating MT x NT MFMA tiles over all input rows
 // (x rows, then the x_lo rows when the input is carried as a pair), with the weights dequantised
 // straight into operand registers from the re-tiled copy and the input rows read from L2 in
 // contiguous row segments and staged through a per-wave LDS slice (loading each lane's own operand
 // rows straight from L2 touched 64 row segments per load: 7.19k -> 7.41k tok/s at 8 streams). The
 // four partial tiles meet in LDS and are added in wave order; the epilogue (the GEMV's) runs one
-// thread per (row, column): the pair's two rows are added (x row first), then STORE, SwiGLU, the
-// gated short conv with the slot's kept state, or the head's logits with each row's argmax key.
+// thread per (row, column): the pair's two rows are added (x row first), then STORE, SwiGLU, or
+// the head's logits with each row's argmax key. The conv layers' in_proj runs here as a plain
+// STORE over all 192 tiles; the gated conv follows in its own launch (k_conv, decode mode).
 // ---------------------------------------------------------------------------------------------
 
-template <int EPI> struct SgTiles { static constexpr int v = EPI == GEMV_SWIGLU ? 2 : EPI == GEMV_CONV ? 3 : 1; };
+template <int EPI> struct SgTiles { static constexpr int v = EPI == GEMV_SWIGLU ? 2 : 1; };
 // Whether the waves' partial tiles exceed 96 KB of LDS together (then they are reduced per column tile).
 template <int EPI, int MT, int WV> struct SgTwoPhase {
   static constexpr bool v = (size_t)WV * MT * 32 * SgTiles<EPI>::v * 32 * sizeof(float) > 96 * 1024;
@@ -482,7 +482,6 @@ template <int EPI, int MT, int WV> struct SgTwoPhase {
 constexpr int kHeadTiles = 4;    // 32-row tiles of the head per block
 
 // STORE with g.yf_part set: blockIdx.y = K quarter (the block's waves share that quarter's tiles).
-// WV waves per block (4, or 8 to halve each wave's K walk on the short-M, one-block-per-CU launches).
 template <int BITS, int EPI, int MT, int WV>
 __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
   constexpr bool F16 = BITS == 16;             // operands from the fp16 copy (GemmW::w16)
@@ -513,9 +512,6 @@ __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
   if constexpr (EPI == GEMV_SWIGLU) {
     tile[0] = tb;
     tile[1] = (N / 2) / 32 + tb;
-  } else if constexpr (EPI == GEMV_CONV) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) tile[j] = j * ((N / 3) / 32) + tb;
   } else {
     tile[0] = tb;
   }
@@ -685,28 +681,10 @@ __global__ void __launch_bounds__(64 * WV) k_sgemm(GemmW w, GemvArgs g) {
       const int n = 32 * tile[0] + c;
       float* out = blockIdx.y == 0 ? g.yf : g.yf_part[blockIdx.y - 1];
       if (n < N) out[(size_t)r * g.ldy + n] = val(r, c);
-    } else if constexpr (EPI == GEMV_SWIGLU) {
+    } else {
+      static_assert(EPI == GEMV_SWIGLU, "STORE, SwiGLU or the head");
       const float gt = val(r, c), up = val(r, 32 + c);
       g.y[(size_t)r * g.ldy + 32 * tb + c] = f2h_sep(gt / (1.f + __expf(-gt)) * up);
-    } else {
-      // gated short conv of channel ch ("LFM3-1.7B port" table row 1): z = f16(B * x),
-      // y = sum_j ker[ch, j] * [state | z]_j, out = f16(C * y), state <- the last taps-1 z
-      const int H = N / 3, T = g.conv_taps, S = T - 1;
-      const int ch = 32 * tb + c;
-      f16_t* st = g.conv_state + (size_t)g.conv_slot[r] * g.conv_slot_stride;
-      const float z = h2f(f2h_sep(val(r, c) * val(r, 64 + c)));
-      float win[kMaxTaps];
-#pragma unroll
-      for (int q = 0; q < kMaxTaps - 1; ++q) win[q] = q < S ? h2f(st[(size_t)q * H + ch]) : 0.f;
-      float y = bf2f(g.conv_kernel[(size_t)ch * T + S]) * z;
-#pragma unroll
-      for (int q = 0; q < kMaxTaps - 1; ++q)
-        if (q < S) y = fmaf(bf2f(g.conv_kernel[(size_t)ch * T + q]), win[q], y);
-#pragma unroll
-      for (int q = 0; q < kMaxTaps - 2; ++q)
-        if (q + 1 < S) st[(size_t)q * H + ch] = f2h(win[q + 1]);
-      st[(size_t)(S - 1) * H + ch] = f2h(z);
-      g.y[(size_t)r * g.ldy + ch] = f2h_sep(val(r, 32 + c) * y);
     }
   }
   __syncthreads();   // the LDS tiles are reused by the next tile
@@ -743,23 +721,14 @@ static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, in
   return hipGetLastError();
 }
 
-// Up to 32 operand rows: 8 waves per block (the partial tiles of 8 waves fit in LDS); the head keeps
-// 4 (its argmax slots are laid out for 256 threads).
-// 8 waves per block for the conv in_proj at 4 and 6 bits (one block per 32 channels: 64 blocks,
-// each with a long K walk), 4 for the rest (measured: 8 waves elsewhere lost), and 4 when the
-// block's K range has fewer than 8 tiles (every wave needs one). At 8 bits and from the fp16 copy
-// the conv in_proj keeps 4 waves: three tiles' operands in four register sets exceed the 256
-// registers a lane of a 512-thread block has, and the spilled 8-wave form returned wrong sums from
-// the fp16 copy (the NVFP4 export's bf16 in_proj at 8 rows), while every form without spills
-// matches the oracle. The wave count depends on the weight shape and epilogue alone, never on the
-// row count, so a row's sums do not depend on its batch.
+// Four waves per block, each needing at least one K tile of the block's range (eight waves lost
+// on every linear measured). The wave count depends on the weight shape alone, never on the row
+// count, so a row's sums do not depend on its batch.
 template <int BITS, int EPI>
 static hipError_t launch_sg_epi(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int meff, int ksplit = 1) {
-  constexpr int W1 = (EPI == GEMV_CONV && BITS != 8 && BITS != 16) ? 8 : 4;
   const int nkb = (w.k / BK) / ksplit;
   if (nkb < 4) return hipErrorInvalidValue;
-  if (nkb < W1) return meff <= 32 ? launch_sg<BITS, EPI, 1, 4>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2, 4>(s, w, g, blocks, ksplit);
-  return meff <= 32 ? launch_sg<BITS, EPI, 1, W1>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2, W1>(s, w, g, blocks, ksplit);
+  return meff <= 32 ? launch_sg<BITS, EPI, 1, 4>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2, 4>(s, w, g, blocks, ksplit);
 }
 
 template <int BITS>
@@ -772,7 +741,6 @@ static hipError_t launch_sg_bits(hipStream_t s, const GemmW& w, const GemvArgs& 
       return launch_sg_epi<BITS, GEMV_STORE>(s, w, g, w.ntile, meff, ks ? 4 : 1);
     }
     case GEMV_SWIGLU: return launch_sg_epi<BITS, GEMV_SWIGLU>(s, w, g, w.n / 64, meff);
-    case GEMV_CONV: return launch_sg_epi<BITS, GEMV_CONV>(s, w, g, (w.n / 3) / 32, meff);
     case GEMV_LOGITS:
       if ((w.ntile + kHeadTiles - 1) / kHeadTiles > kArgmaxParts) return hipErrorInvalidValue;
       return launch_sg_epi<BITS, GEMV_LOGITS>(s, w, g, (w.ntile + kHeadTiles - 1) / kHeadTiles, meff);
@@ -784,8 +752,7 @@ hipError_t launch_sgemm(hipStream_t s, const GemmW& w, const GemvArgs& g) {
   const int meff = g.x_lo ? 2 * g.batch : g.batch;
   if (g.batch < 1 || meff > 64 || w.k % (4 * BK) || (w.codes && w.group % 32) || g.ldx % 8 || (uintptr_t)g.x % 16 ||
       (uintptr_t)g.x_lo % 16 || w.ntile != (w.n + 31) / 32 ||
-      (g.epi == GEMV_SWIGLU && w.n % 64) || (g.epi == GEMV_CONV && ((w.n / 3) % 32 || w.n % 3 || g.conv_taps < 2 ||
-                                                                  g.conv_taps > kMaxTaps)))
+      (g.epi == GEMV_SWIGLU && w.n % 64) || g.epi == GEMV_CONV)
     return hipErrorInvalidValue;
   // the fp16 copy only where there are no codes (bf16, NVFP4, block-FP8): decode reads the fewest
   // bytes from the codes

@@ -300,27 +300,53 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= a.hidden) return;
   const int H = a.hidden, T = a.taps, S = T - 1;
-  float ker[kMaxTaps];
+  // taps past T read tap T - 1 and are zeroed after the load: clamped addresses keep every load
+  // unconditional, so they all go out at once (a guarded load per tap waited for each in turn)
+  auto load_taps = [&](bf16_t (&kraw)[kMaxTaps]) {
 #pragma unroll
-  for (int j = 0; j < kMaxTaps; ++j) ker[j] = j < T ? bf2f(a.kernel[(size_t)c * T + j]) : 0.f;
+    for (int j = 0; j < kMaxTaps; ++j) kraw[j] = a.kernel[(size_t)c * T + min(j, T - 1)];
+  };
   auto zrow = [&](int r) -> float {
     const float* p = a.bcx + (size_t)r * a.ld;
     return h2f(f2h_sep(p[c] * p[2 * H + c]));
   };
-  auto crow = [&](int r) -> float { return a.bcx[(size_t)r * a.ld + H + c]; };
-  float win[kMaxTaps];
+  float ker[kMaxTaps];
+  bf16_t kraw[kMaxTaps];
   if (a.rows.mode == 1) {
+    // the row's own loads (state columns, B, C, x) go out first, then the taps; the tap loops run
+    // to the compile-time bound so the window stays in registers. The sums are those of in_proj's
+    // fused conv epilogue: z first, then the state columns oldest first.
     const int r = blockIdx.y;
     f16_t* st = a.state + (size_t)a.rows.slot[r] * a.slot_stride;
-    for (int j = 0; j < S; ++j) win[j] = h2f(st[(size_t)j * H + c]);
-    const float z = zrow(r);
-    float y = ker[S] * z;
-    for (int j = 0; j < S; ++j) y = fmaf(ker[j], win[j], y);
-    a.out[(size_t)r * H + c] = f2h_sep(crow(r) * y);
-    for (int j = 0; j + 1 < S; ++j) st[(size_t)j * H + c] = f2h(win[j + 1]);
+    f16_t sraw[kMaxTaps - 1];
+#pragma unroll
+    for (int j = 0; j < kMaxTaps - 1; ++j) sraw[j] = st[(size_t)min(j, S - 1) * H + c];
+    const float* p = a.bcx + (size_t)r * a.ld;
+    const float bv = p[c], cv = p[H + c], xv = p[2 * H + c];
+    load_taps(kraw);
+    float win[kMaxTaps - 1];
+#pragma unroll
+    for (int j = 0; j < kMaxTaps - 1; ++j) win[j] = j < S ? h2f(sraw[j]) : 0.f;
+    const float z = h2f(f2h_sep(bv * xv));
+#pragma unroll
+    for (int j = 0; j < kMaxTaps; ++j) ker[j] = j < T ? bf2f(kraw[j]) : 0.f;
+    float kS = ker[kMaxTaps - 1];
+#pragma unroll
+    for (int q = kMaxTaps - 2; q >= 0; --q) kS = q == S ? ker[q] : kS;   // ker[S]
+    float y = kS * z;
+#pragma unroll
+    for (int j = 0; j < kMaxTaps - 1; ++j)
+      if (j < S) y = fmaf(ker[j], win[j], y);
+    a.out[(size_t)r * H + c] = f2h_sep(cv * y);
+#pragma unroll
+    for (int j = 0; j < kMaxTaps - 2; ++j)
+      if (j + 1 < S) st[(size_t)j * H + c] = f2h(win[j + 1]);
     st[(size_t)(S - 1) * H + c] = f2h(z);
     return;
   }
+  load_taps(kraw);
+#pragma unroll
+  for (int j = 0; j < kMaxTaps; ++j) ker[j] = j < T ? bf2f(kraw[j]) : 0.f;
   // prefill: a run of kConvRun rows of one channel per thread; every input of the run (z of the
   // run and of the taps-1 rows before it, from bcx or, before row 0, the kept state; C of the run)
   // is loaded up front (clamped addresses, branch-free), then the run is computed

@@ -639,7 +639,20 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     // sliding layers at 1-2 rows: the o_proj GEMV merges the attention's split partials itself
     // (a window of at most kFusedMergeSplits tiles), which saves the merge launch
     GemvArgs merge_in{};
-    if (lw.type == LFM3_LAYER_CONV) {
+    if (lw.type == LFM3_LAYER_CONV && mfma && 2 * M <= 64) {
+      // 3-32 rows: in_proj as a plain MFMA linear over every CU (one block per 32-row tile of
+      // B | C | x), then the gated conv with each row's kept state in its own small launch
+      GemvArgs g{};
+      g.w = lw.mix_in; g.epi = GEMV_STORE; g.yf = big; g.ldy = L.big_ld;
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4, true, &lw.g_in));
+      ConvArgs ca{};
+      ca.bcx = big; ca.ld = L.big_ld; ca.kernel = lw.conv_kernel;
+      ca.state = ctx->at<f16_t>(L.conv_state) + (size_t)lw.sub * (c.conv_taps - 1) * H;
+      ca.slot_stride = (int64_t)L.conv_slot;
+      ca.out = mix; ca.rows = rows; ca.hidden = H; ca.taps = c.conv_taps;
+      LFM3_TRY(timed(ctx, LFM3_PROF_CONV, (double)M * H * (12 + 2 + 4 * (c.conv_taps - 1)), 0,
+                     [&] { return launch_conv(s, ca); }));
+    } else if (lw.type == LFM3_LAYER_CONV) {
       GemvArgs g{};
       g.w = lw.mix_in; g.epi = GEMV_CONV; g.y = mix; g.ldy = H;
       g.conv_kernel = lw.conv_kernel;
@@ -647,7 +660,9 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
       g.conv_slot_stride = (int64_t)L.conv_slot;
       g.conv_taps = c.conv_taps;
       for (int b = 0; b < M; ++b) g.conv_slot[b] = rows.slot[b];
-      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * H * (2 + 4 * (c.conv_taps - 1)), true, &lw.g_in));
+      // 1-2 rows (fused norm prologue) and 33-64 rows (the pair's 66-128 operand rows exceed the
+      // MFMA GEMM): the exact GEMV with the conv epilogue
+      LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * H * (2 + 4 * (c.conv_taps - 1)), true));
     } else {
       GemvArgs g{};
       g.w = lw.mix_in; g.epi = GEMV_STORE; g.yf = big; g.ldy = L.big_ld;
