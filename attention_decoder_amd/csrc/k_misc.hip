@@ -24,34 +24,36 @@ LFM3_DEV float deq_value(uint32_t q, float s, float b) { return fmaf((float)q, s
 // linears, 8-bit in the VL 4-bit export)
 // ---------------------------------------------------------------------------------------------
 
+// Block (row, 256-column slice), one column per thread: the whole row's loads go out at once (one
+// block looping over the row waited for each slice's loads in turn: 6 us a decode step at batch 1).
 __global__ void __launch_bounds__(256) k_embed(QLinear e, const int32_t* __restrict__ tokens, float* __restrict__ h,
                                                 uint32_t* flags) {
   const int r = blockIdx.x;
+  const int k = blockIdx.y * blockDim.x + threadIdx.x;
   const int tok = tokens[r];
+  if (k >= e.k) return;
   float* out = h + (size_t)r * e.k;
   if (tok < 0 || tok >= e.n) {
-    for (int k = threadIdx.x; k < e.k; k += blockDim.x) out[k] = 0.f;
-    if (threadIdx.x == 0) atomicOr(flags, 1u);
+    out[k] = 0.f;
+    if (k == 0) atomicOr(flags, 1u);
     return;
   }
   if (e.fmt != FMT_AFFINE) {
-    for (int k = threadIdx.x; k < e.k; k += blockDim.x) out[k] = weight_value(e, tok, k);
+    out[k] = weight_value(e, tok, k);
     return;
   }
   const size_t row_bytes = (size_t)e.k * e.bits / 8;
   const uint8_t* row = e.q + (size_t)tok * row_bytes;
   const int ng = e.k / e.group;
-  for (int k = threadIdx.x; k < e.k; k += blockDim.x) {
-    const int g = k / e.group;
-    const float s = bf2f(e.scales[(size_t)tok * ng + g]);
-    const float b = bf2f(e.biases[(size_t)tok * ng + g]);
-    out[k] = deq_value(code_at(row, k, e.bits), s, b);
-  }
+  const int g = k / e.group;
+  const float s = bf2f(e.scales[(size_t)tok * ng + g]);
+  const float b = bf2f(e.biases[(size_t)tok * ng + g]);
+  out[k] = deq_value(code_at(row, k, e.bits), s, b);
 }
 
 hipError_t launch_embed(hipStream_t s, const QLinear& emb, const int32_t* tokens, int rows, float* h, uint32_t* flags) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, emb, tokens, h, flags);
+  hipLaunchKernelGGL(k_embed, dim3(rows, (emb.k + 255) / 256), dim3(256), 0, s, emb, tokens, h, flags);
   return hipGetLastError();
 }
 
