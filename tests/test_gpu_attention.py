@@ -9,7 +9,8 @@ What is run (the shapes the benchmark and the pages use):
 - decode on a sliding layer across the window seams 255 / 256 / 257 and far past the ring's wrap;
 - prefill passes on both layer kinds: 256 rows with no history, 64 rows after 3,000 keys and 100
   after 500 (the served shapes of "TensorFold PR #1508", prefill-attention gate), and a 2048-row
-  chunk after 6,144 keys (the 8k prefill's last chunk), the sliding one across the ring's wrap.
+  chunk after 6,144 keys (the 8k prefill's last chunk), the sliding one across the ring's wrap;
+  on a full layer, the 2048-row chunk after 30,720 keys (the last pass of a 32768-token prompt).
 
 Full layers read their keys through a shuffled page table (slots' pages interleaved at random in the
 pool). Every cache row that holds no visible key -- unused pages, the tail of a slot's last page,
@@ -320,6 +321,19 @@ def test_prefill_pass(actx, sliding, hist_len, rows):
     q = case.exact_q()
     hist = _history(rng, case, q, [(3, hist_len, list(range(rows)))])
     _check(torch, eng, cfg, case, hist, f"prefill {'sliding' if sliding else 'full'} {rows} rows after {hist_len}")
+
+
+def test_prefill_pass_32k_last_chunk(actx):
+    """The last 2048-row pass of a 32768-token prompt on a full layer (2048 rows after 30,720
+    keys), the prompt length of the 4-bit g32 / 8-bit head workload. The oracle's dense scores for
+    it take about 9 GB of host memory and a minute."""
+    torch, cfg, eng = actx
+    hist_len, rows = 30720, 2048
+    rng = np.random.default_rng(1000 * hist_len + rows)
+    case = Case(rng, 0, 0, [3], [hist_len], rows)
+    q = case.exact_q()
+    hist = _history(rng, case, q, [(3, hist_len, list(range(rows)))])
+    _check(torch, eng, cfg, case, hist, f"prefill full {rows} rows after {hist_len}")
 
 
 def test_hook_refuses_bad_arguments(actx):
