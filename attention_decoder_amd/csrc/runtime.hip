@@ -607,6 +607,22 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     const double fl = 2.0 * M * (double)g.w.n * g.w.k;
     if (mfma && gw && (g.x_lo ? 2 * M : M) <= 64)
       return timed(ctx, LFM3_PROF_GEMV, gemv_bytes(g.w, out_bytes), fl, [&] { return launch_sgemm(s, *gw, g); });
+    if (mfma && gw && g.x_lo && g.epi == GEMV_STORE && !g.yf_part[0]) {
+      // an input carried as a pair past 32 rows (more than the MFMA kernel's 64 operand rows): one
+      // launch per 32 rows; a row's sums do not depend on the rows that share its launch
+      for (int r0 = 0; r0 < M; r0 += 32) {
+        GemvArgs gp = g;
+        gp.batch = std::min(32, M - r0);
+        gp.x = g.x + (size_t)r0 * g.ldx;
+        gp.x_lo = g.x_lo + (size_t)r0 * g.ldx;
+        gp.yf = g.yf + (size_t)r0 * g.ldy;
+        const double part = (double)gp.batch / M;
+        const hipError_t e = timed(ctx, LFM3_PROF_GEMV, gemv_bytes(g.w, out_bytes) * part, fl * part,
+                                   [&] { return launch_sgemm(s, *gw, gp); });
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
     return timed(ctx, LFM3_PROF_GEMV, gemv_bytes(g.w, out_bytes), fl, [&] { return launch_gemv(s, g); });
   };
   // GEMV whose input is rmsnorm(cur [+ rmsnorm(m) * w_post]) * w_pre
@@ -639,9 +655,10 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
     // sliding layers at 1-2 rows: the o_proj GEMV merges the attention's split partials itself
     // (a window of at most kFusedMergeSplits tiles), which saves the merge launch
     GemvArgs merge_in{};
-    if (lw.type == LFM3_LAYER_CONV && mfma && 2 * M <= 64) {
-      // 3-32 rows: in_proj as a plain MFMA linear over every CU (one block per 32-row tile of
-      // B | C | x), then the gated conv with each row's kept state in its own small launch
+    if (lw.type == LFM3_LAYER_CONV && mfma) {
+      // 3+ rows: in_proj as a plain MFMA linear over every CU (one block per 32-row tile of
+      // B | C | x; past 32 rows one launch per 32 rows), then the gated conv with each row's kept
+      // state in its own small launch
       GemvArgs g{};
       g.w = lw.mix_in; g.epi = GEMV_STORE; g.yf = big; g.ldy = L.big_ld;
       LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * lw.mix_in.n * 4, true, &lw.g_in));
@@ -660,8 +677,7 @@ lfm3_status run_decode(lfm3_ctx* ctx, const Rows& rows, float* hidden_out, float
       g.conv_slot_stride = (int64_t)L.conv_slot;
       g.conv_taps = c.conv_taps;
       for (int b = 0; b < M; ++b) g.conv_slot[b] = rows.slot[b];
-      // 1-2 rows (fused norm prologue) and 33-64 rows (the pair's 66-128 operand rows exceed the
-      // MFMA GEMM): the exact GEMV with the conv epilogue
+      // 1-2 rows: the exact GEMV with the fused norm prologue and the conv epilogue
       LFM3_TRY(normed_gemv(g, w_post, lw.op_norm, cap(i - 1), nullptr, (double)M * H * (2 + 4 * (c.conv_taps - 1)), true));
     } else {
       GemvArgs g{};
