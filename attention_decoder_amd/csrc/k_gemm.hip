@@ -721,13 +721,21 @@ static hipError_t launch_sg(hipStream_t s, const GemmW& w, const GemvArgs& g, in
   return hipGetLastError();
 }
 
-// Four waves per block, each needing at least one K tile of the block's range (eight waves lost
-// on every linear measured). The wave count depends on the weight shape alone, never on the row
-// count, so a row's sums do not depend on its batch.
+// Four waves per block (eight for the longer 4-bit plain linears), each needing at least one K
+// tile of the block's range. The wave count depends on the weight format and shape alone, never on
+// the row count, so a row's sums do not depend on its batch.
 template <int BITS, int EPI>
 static hipError_t launch_sg_epi(hipStream_t s, const GemmW& w, const GemvArgs& g, int blocks, int meff, int ksplit = 1) {
   const int nkb = (w.k / BK) / ksplit;
   if (nkb < 4) return hipErrorInvalidValue;
+  if constexpr (EPI == GEMV_STORE && BITS == 4) {
+    // 4-bit plain linears with at least 16 K tiles a block (w2's K quarters, qkvg, in_proj): 8 waves,
+    // each walking half as many K tiles (8 streams 7,657 -> 7,782 tok/s; at 8 bits and from the fp16
+    // copy the same lost 1.4% and 4.6%, and with the 8-tile K quarters of the 2048-wide
+    // projections as well it gained less)
+    if (nkb >= 16)
+      return meff <= 32 ? launch_sg<BITS, EPI, 1, 8>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2, 8>(s, w, g, blocks, ksplit);
+  }
   return meff <= 32 ? launch_sg<BITS, EPI, 1, 4>(s, w, g, blocks, ksplit) : launch_sg<BITS, EPI, 2, 4>(s, w, g, blocks, ksplit);
 }
 

@@ -71,6 +71,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise OSError(f"{path} is not built; run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+    # torch first: it brings its own HIP runtime, and the library must bind to that one. Loaded
+    # first, the library pulls in the system runtime and torch then loads a second one, whose
+    # device memory and streams the first cannot use (lfm3_create reports no HIP device).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     sig = {
