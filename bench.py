@@ -393,7 +393,7 @@ def nvfp4_extras(synth, torch, dev):
 def cfg5_extras(synth, torch, dev):
     """4-bit g32 linears with an 8-bit g64 embedding / head: a 32768-token prefill (one stream, 2048-row
     chunks), then 32 streams at contexts uniform in [1024, 32768] decoding 64 greedy tokens each at
-    batch 32."""
+    batch 32 (the first step untimed)."""
     from attention_decoder_amd.lfm3 import Engine
     out = {}
     cfg = synth.full_config(bits=4, group=32, embed_bits=8, embed_group=64, max_slots=32, max_ctx=32768 + 128,
@@ -421,15 +421,18 @@ def cfg5_extras(synth, torch, dev):
     ids = torch.empty((n_steps + 1, 32), dtype=torch.int32, device=dev)
     ids[0] = torch.from_numpy(synth.prompt_tokens(12, 32)).to(dev)
     slots = list(range(32))
+    # one untimed step first, as in the 8-stream decode: the batch-32 kernels' first launches (code
+    # loading) stay out of the timed steps
+    eng.decode(slots, tokens=ids[0], logits=False, argmax=True, out={"argmax": ids[1]})
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(eng.stream)
-    for t in range(n_steps):
+    for t in range(1, n_steps):
         eng.decode(slots, tokens=ids[t], logits=False, argmax=True, out={"argmax": ids[t + 1]})
     e1.record(eng.stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    out["cfg5_decode_32stream_tok_s"] = round(32 * n_steps / (ms / 1e3), 1)
+    out["cfg5_decode_32stream_tok_s"] = round(32 * (n_steps - 1) / (ms / 1e3), 1)
     out["cfg5_decode_32stream_mean_context"] = int(np.mean(lens))
     out["cfg5_decode_step_breakdown_ms"] = step_breakdown(eng, slots, ids[n_steps])
     log(f"g32 + 8-bit head: 32k prefill {out['cfg5_prefill_32k_tok_s']} tok/s, 32-stream decode "
