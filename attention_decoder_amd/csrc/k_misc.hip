@@ -475,11 +475,17 @@ __global__ void __launch_bounds__(256) k_argmax_finalize(uint64_t* keys, int32_t
   __shared__ uint64_t wk[4];
   const int r = blockIdx.x;
   uint64_t* part = keys + (size_t)r * kArgmaxParts;
+  // every partial of the thread is loaded before any is cleared (a load after a store to the same
+  // array would wait for it)
+  constexpr int kPer = kArgmaxParts / 256;
+  uint64_t v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) v[i] = part[threadIdx.x + 256 * i];
   uint64_t k = 0;
-  for (int p = threadIdx.x; p < kArgmaxParts; p += 256) {
-    const uint64_t v = part[p];
-    k = v > k ? v : k;
-    part[p] = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    k = v[i] > k ? v[i] : k;
+    part[threadIdx.x + 256 * i] = 0;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
