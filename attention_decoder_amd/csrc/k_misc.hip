@@ -105,6 +105,10 @@ hipError_t launch_dequant_rows(hipStream_t s, const QLinear& w, int row0, int ro
 // RMSNorm eps 1e-5). One block per row, 256 threads, hidden <= 4096.
 // ---------------------------------------------------------------------------------------------
 
+// NP: partial sums of m the row carries (1: m; 2: m + m2, the prefill K halves; 4: m + m2 + m3 + m4,
+// the decode K quarters). Every partial is loaded with the first loads: loaded behind a runtime
+// test, each one waited for the one before it.
+template <int NP>
 __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
   // the arithmetic is the decode GEMV's norm prologue (norm_vec.h), so fused and unfused steps
   // agree bitwise
@@ -114,32 +118,28 @@ __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
   const size_t base = (size_t)r * H;
   const int nv = H / 8;
   float hv[kVecBlocks][8], mv[kVecBlocks][8], wpo[kVecBlocks][8], wpr[kVecBlocks][8];
+  float pv[NP > 1 ? NP - 1 : 1][kVecBlocks][8];
   const float* mp = a.m ? a.m : a.h_in;
+  const float* pp[3] = {a.m2, a.m3, a.m4};
   const bf16_t* wpo_p = a.w_post ? a.w_post : a.w_pre;
 #pragma unroll
   for (int j = 0; j < kVecBlocks; ++j) {
     const int v = min((int)threadIdx.x + 256 * j, nv - 1);
     load_f32x8(a.h_in + base + 8 * v, hv[j]);
     load_f32x8(mp + base + 8 * v, mv[j]);
+#pragma unroll
+    for (int q = 0; q + 1 < NP; ++q) load_f32x8(pp[q] + base + 8 * v, pv[q][j]);
     bf16x8_to_f32(load_u16x8(wpo_p + 8 * v), wpo[j]);
     bf16x8_to_f32(load_u16x8(a.w_pre + 8 * v), wpr[j]);
   }
-  if (a.m && a.m2) {
+  if constexpr (NP > 1) {
 #pragma unroll
-    for (int j = 0; j < kVecBlocks; ++j) {
-      const int v = min((int)threadIdx.x + 256 * j, nv - 1);
-      float m2v[8];
-      load_f32x8(a.m2 + base + 8 * v, m2v);
+    for (int j = 0; j < kVecBlocks; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mv[j][e] = mv[j][e] + m2v[e];
-      if (a.m3) {
-        float m3v[8], m4v[8];
-        load_f32x8(a.m3 + base + 8 * v, m3v);
-        load_f32x8(a.m4 + base + 8 * v, m4v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mv[j][e] = (mv[j][e] + m3v[e]) + m4v[e];
+      for (int e = 0; e < 8; ++e) {
+        mv[j][e] = mv[j][e] + pv[0][j][e];
+        if constexpr (NP == 4) mv[j][e] = (mv[j][e] + pv[1][j][e]) + pv[2][j][e];
       }
-    }
   }
   bool ok[kVecBlocks];
 #pragma unroll
@@ -186,7 +186,11 @@ __global__ void __launch_bounds__(256) k_resid_norm(NormArgs a) {
 
 hipError_t launch_resid_norm(hipStream_t s, const NormArgs& a) {
   if (a.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_resid_norm, dim3(a.rows), dim3(256), 0, s, a);
+  // the partials present (a partial without m is never passed; m3 and m4 come together)
+  if (!a.m || !a.m2) hipLaunchKernelGGL(k_resid_norm<1>, dim3(a.rows), dim3(256), 0, s, a);
+  else if (!a.m3) hipLaunchKernelGGL(k_resid_norm<2>, dim3(a.rows), dim3(256), 0, s, a);
+  else if (a.m4) hipLaunchKernelGGL(k_resid_norm<4>, dim3(a.rows), dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
