@@ -481,6 +481,7 @@ __global__ void __launch_bounds__(256) k_argmax_finalize(uint64_t* keys, int32_t
   uint64_t* part = keys + (size_t)r * kArgmaxParts;
   // every partial of the thread is loaded before any is cleared (a load after a store to the same
   // array would wait for it)
+  static_assert(kArgmaxParts % 256 == 0, "whole partials per thread");
   constexpr int kPer = kArgmaxParts / 256;
   uint64_t v[kPer];
 #pragma unroll
